@@ -1,0 +1,245 @@
+"""CPU oracle of the W8A8 MoE expert layer (test infrastructure only).
+
+This package wraps ``moe_oracle.c`` -- the plain, slow, obviously correct CPU
+definition of the layer -- for the tests, the smoke check and the benchmark's
+CPU-baseline leg. Nothing on the product path imports it, and it imports
+nothing from the product package. All arrays are host numpy arrays; weights
+are in the plain row-major layouts described in ``moe_oracle.c``.
+
+The functions here only marshal arguments; every step is computed in C.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into oracle/libmoe_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-Wall", "-Wno-unknown-pragmas", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    sig = {
+        "oracle_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+        "oracle_quant_rows": (None, [_I64, _I64, _P, _P, _P]),
+        "oracle_calibrate": (ctypes.c_int, [_I32, _I32, _I32, _F32, _P, _I64, _P, _P, _P,
+                                            _P, _P, _P, _P, _P, _P, _P]),
+        "oracle_route": (None, [_I64, _I32, _I32, _P, _P, _P]),
+        "oracle_capacity": (_I64, [_F32, _I64, _I32, _I32]),
+        "oracle_permute": (_I64, [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P]),
+        "oracle_act_quant": (None, [_I64, _I32, _P, _P, _P, _P]),
+        "oracle_expert_rows": (None, [_I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, _P, _P, _P, _P]),
+        "oracle_combine": (None, [_I64, _P, _I32, _I32, _P, _P, _P, _P, _P]),
+        "oracle_forward": (_I64, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32,
+                                  _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "oracle_num_threads": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def f64_to_bf16(v: float) -> int:
+    """Round a float to bfloat16 bits (ties to even, one rounding)."""
+    return int(_load().oracle_f64_to_bf16(float(v)))
+
+
+def quant_rows(v: np.ndarray):
+    """Symmetric per-row INT8 quantiser (fp32 rule). v: float32 [rows][n]."""
+    v = _c(v, np.float32)
+    rows, n = v.shape
+    q = np.empty((rows, n), np.int8)
+    s = np.empty(rows, np.float32)
+    _load().oracle_quant_rows(rows, n, _ptr(v), _ptr(q), _ptr(s))
+    return q, s
+
+
+def calibrate(calib_x_bf16, w_gate, w_up, w_down, alpha: float, want_smoothed: bool = False):
+    """SmoothQuant calibration + per-output-channel INT8 weight quantisation.
+
+    calib_x_bf16: uint16 [Nc][H]; w_gate, w_up: float32 [E][F][H];
+    w_down: float32 [E][H][F]. Returns a dict with s, inv_s [H], q_gu int8
+    [E][2F][H], sw_gu [E][2F], q_d int8 [E][H][F], sw_d [E][H] (and ws_gu,
+    the smoothed fp32 gate/up weights, when asked)."""
+    cx = _c(calib_x_bf16, np.uint16)
+    wg, wu, wd = _c(w_gate, np.float32), _c(w_up, np.float32), _c(w_down, np.float32)
+    E, F, H = wg.shape
+    assert wu.shape == (E, F, H) and wd.shape == (E, H, F) and cx.shape[1] == H
+    out = dict(s=np.empty(H, np.float32), inv_s=np.empty(H, np.float32),
+               q_gu=np.empty((E, 2 * F, H), np.int8), sw_gu=np.empty((E, 2 * F), np.float32),
+               q_d=np.empty((E, H, F), np.int8), sw_d=np.empty((E, H), np.float32))
+    if want_smoothed:
+        out["ws_gu"] = np.empty((E, 2 * F, H), np.float32)
+    rc = _load().oracle_calibrate(H, F, E, float(alpha), _ptr(cx), cx.shape[0],
+                                  _ptr(wg), _ptr(wu), _ptr(wd), _ptr(out["s"]), _ptr(out["inv_s"]),
+                                  _ptr(out["q_gu"]), _ptr(out["sw_gu"]), _ptr(out["q_d"]),
+                                  _ptr(out["sw_d"]), _ptr(out.get("ws_gu")))
+    if rc != 0:
+        raise ValueError("oracle_calibrate failed: %d" % rc)
+    return out
+
+
+def route(logits, k: int):
+    """Top-k routing; logits float32 [T][E] -> ids int32 [T][k], w float32 [T][k]."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _load().oracle_route(T, E, k, _ptr(lg), _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def capacity(cf: float, T: int, k: int, E: int) -> int:
+    return int(_load().oracle_capacity(float(cf), T, k, E))
+
+
+def permute(ids, E: int, cap: int):
+    """Stable grouping by expert with capacity; ids int32 [T][k]."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    A = T * k
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sorted_ = np.full(max(A, 1), -1, np.int32)
+    row_of = np.empty(max(A, 1), np.int32)
+    kept = _load().oracle_permute(T, E, k, _ptr(ids), cap, _ptr(counts), _ptr(offsets),
+                                  _ptr(sorted_), _ptr(row_of))
+    return dict(counts=counts, offsets=offsets, sorted=sorted_[:kept].copy(),
+                row_of=row_of[:A].reshape(T, k), kept=int(kept))
+
+
+def act_quant(x_bf16, inv_s):
+    """Per-token smoothed INT8 quantisation; x uint16 [T][H] -> qx int8, sx f32 [T]."""
+    x = _c(x_bf16, np.uint16)
+    inv_s = _c(inv_s, np.float32)
+    T, H = x.shape
+    qx = np.empty((T, H), np.int8)
+    sx = np.empty(T, np.float32)
+    _load().oracle_act_quant(T, H, _ptr(x), _ptr(inv_s), _ptr(qx), _ptr(sx))
+    return qx, sx
+
+
+def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h: bool = True):
+    """Expert FFN for the permuted rows listed in `rows` (sorted positions)."""
+    rows = _c(rows, np.int32)
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    sorted_ = _c(sorted_, np.int32)
+    qx, sx = _c(qx, np.int8), _c(sx, np.float32)
+    q_gu, sw_gu = _c(cal["q_gu"], np.int8), _c(cal["sw_gu"], np.float32)
+    q_d, sw_d = _c(cal["q_d"], np.int8), _c(cal["sw_d"], np.float32)
+    E, F2, H = q_gu.shape
+    F = F2 // 2
+    n = rows.shape[0]
+    acc1 = np.empty((n, 2 * F), np.int32) if want_acc1 else None
+    h = np.empty((n, F), np.float32) if want_h else None
+    qh = np.empty((n, F), np.int8)
+    sh = np.empty(n, np.float32)
+    y = np.empty((n, H), np.float64)
+    _load().oracle_expert_rows(n, _ptr(rows), H, F, k, _ptr(ids), _ptr(sorted_), _ptr(qx), _ptr(sx),
+                               _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d),
+                               _ptr(acc1), _ptr(h), _ptr(qh), _ptr(sh), _ptr(y))
+    return dict(acc1=acc1, h=h, qh=qh, sh=sh, y=y)
+
+
+def combine(tokens, w, row_of, y, y_row_index=None):
+    """Gate-weighted sum for the listed tokens; returns bf16 bits [n][H]."""
+    w = _c(w, np.float32)
+    T, k = w.shape
+    row_of = _c(row_of, np.int32)
+    y = _c(y, np.float64)
+    H = y.shape[1]
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else tok.shape[0]
+    yri = None if y_row_index is None else _c(y_row_index, np.int64)
+    out = np.empty((n, H), np.uint16)
+    _load().oracle_combine(n, _ptr(tok), H, k, _ptr(w), _ptr(row_of), _ptr(yri), _ptr(y), _ptr(out))
+    return out
+
+
+def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor: float = 0.0,
+            want_acc1: bool = True, want_h: bool = True):
+    """The whole layer on the CPU. Returns a dict of every stage's output."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    q_gu, sw_gu = _c(cal["q_gu"], np.int8), _c(cal["sw_gu"], np.float32)
+    q_d, sw_d = _c(cal["q_d"], np.int8), _c(cal["sw_d"], np.float32)
+    inv_s = _c(cal["inv_s"], np.float32)
+    E, F2, _ = q_gu.shape
+    F = F2 // 2
+    A = T * k
+    lg = None if logits is None else _c(logits, np.float32)
+    ids_in = None if ids is None else _c(ids, np.int32)
+    w_in = None if w is None else _c(w, np.float32)
+    if lg is None:
+        assert ids_in is not None and w_in is not None
+    o = dict(ids=np.empty((T, k), np.int32), w=np.empty((T, k), np.float32),
+             counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
+             sorted=np.full(max(A, 1), -1, np.int32), row_of=np.empty((T, k), np.int32),
+             qx=np.empty((T, H), np.int8), sx=np.empty(T, np.float32),
+             acc1=np.empty((A, 2 * F), np.int32) if want_acc1 else None,
+             h=np.empty((A, F), np.float32) if want_h else None,
+             qh=np.empty((max(A, 1), F), np.int8), sh=np.empty(max(A, 1), np.float32),
+             y=np.empty((max(A, 1), H), np.float64), out=np.empty((T, H), np.uint16))
+    kept = _load().oracle_forward(
+        T, H, F, E, k, _ptr(x), _ptr(lg), _ptr(ids_in), _ptr(w_in), float(capacity_factor),
+        _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), _ptr(inv_s),
+        _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]),
+        _ptr(o["row_of"]), _ptr(o["qx"]), _ptr(o["sx"]), _ptr(o["acc1"]), _ptr(o["h"]),
+        _ptr(o["qh"]), _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]))
+    kept = int(kept)
+    o["kept"] = kept
+    o["sorted"] = o["sorted"][:kept]
+    o["qh"], o["sh"], o["y"] = o["qh"][:kept], o["sh"][:kept], o["y"][:kept]
+    if o["acc1"] is not None:
+        o["acc1"] = o["acc1"][:kept]
+    if o["h"] is not None:
+        o["h"] = o["h"][:kept]
+    return o
