@@ -1,0 +1,195 @@
+/*
+ * moe_w8a8.h -- C ABI of the W8A8-quantised Mixture-of-Experts expert layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one call to moe_w8a8_forward) computes, for T tokens x[T][H]:
+ *   1. route    top-k experts per token from router logits, ties to the lower
+ *               expert index, softmax weights renormalised over the chosen k
+ *               ("超大规模模型推理的Day0适配实践" §四: the fused MoE operator's
+ *               top-k must equal the reference, tie-break included);
+ *   2. permute  group the T*k (token, slot) assignments expert by expert,
+ *               (token, slot) order inside a group, an optional expert
+ *               capacity dropping the overflow (same page, §二.2);
+ *   3. quantise each token to INT8 per token after dividing by the
+ *               SmoothQuant scales ("MiniMax-M3 W8A8 inference on K100AI",
+ *               mhpq.cn/news/1068415, §3.2 and §6.4);
+ *   4. GEMM1    per expert, INT8 x INT8 -> INT32 gate and up projections,
+ *               dequantised per token and per output channel, h = silu(g)*u,
+ *               requantised to INT8 per (token, expert) row (K100AI page
+ *               §1.2 and §4.3: INT8 GEMM with integer accumulation; stay in
+ *               the INT8 domain between consecutive matmuls);
+ *   5. GEMM2    per expert, INT8 down projection, dequantised to fp32;
+ *   6. combine  out[t] = sum over kept slots of w[t][j] * y[row], rounded to
+ *               bfloat16 (Day0 page §四: un-sort and weighted sum).
+ * moe_w8a8_calibrate prepares the quantised weights (K100AI page §3.2:
+ * SmoothQuant with migration strength alpha, per-output-channel weights).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
+ *    by the caller; nothing is allocated or freed inside the library and no
+ *    library state survives a call. Layouts are row-major unless stated.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; the library never synchronises. Calls on
+ *    different streams with disjoint buffers may run concurrently.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call enqueues nothing and returns a negative code. Faults inside
+ *    kernels surface at the caller's next synchronisation.
+ *  - bfloat16 values are passed as uint16_t bit patterns.
+ */
+#ifndef MOE_W8A8_H
+#define MOE_W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_W8A8_OK 0
+#define MOE_W8A8_ERR_INVALID (-1)     /* NULL required pointer, bad size, k > E, ... */
+#define MOE_W8A8_ERR_UNSUPPORTED (-2) /* shape outside the supported set (below)     */
+#define MOE_W8A8_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than required     */
+#define MOE_W8A8_ERR_HIP (-4)         /* a HIP launch or copy reported an error      */
+
+/* Layer dimensions. Supported set: hidden H a multiple of 256 in [256, 65536];
+ * ffn F a multiple of 128 in [128, 65536]; 1 <= num_experts E <= 1024;
+ * 1 <= top_k k <= min(E, 32). */
+typedef struct {
+  int32_t hidden;      /* H */
+  int32_t ffn;         /* F, the expert FFN width (SwiGLU gate/up/down) */
+  int32_t num_experts; /* E, experts held on this device */
+  int32_t top_k;       /* k, assignments per token */
+} moe_w8a8_dims;
+
+/* Quantised layer weights (device memory, written by moe_w8a8_calibrate).
+ *
+ * Fragment-tiled INT8 layout. A weight matrix W[N][K] (N output channels,
+ * K input channels; N % 16 == 0, K % 64 == 0) is stored as 1024-byte tiles of
+ * 16 output channels x 64 input channels, tile (n/16, k/64) at byte offset
+ *     ((n/16) * (K/64) + k/64) * 1024,
+ * and inside a tile the element (n, k) at byte
+ *     (((k % 64) / 16) * 16 + n % 16) * 16 + k % 16.
+ * One tile is exactly one wavefront's 16-byte-per-lane load in the lane order
+ * of the gfx950 INT8 matrix instructions, so weight panels stream from HBM as
+ * contiguous 1 KB blocks.
+ *   w_gate_up : E matrices of [2F][H], consecutive; rows 0..F-1 are the gate
+ *               projection, rows F..2F-1 the up projection (smoothed).
+ *   w_down    : E matrices of [H][F], consecutive (not smoothed).
+ *   s_gate_up : fp32 [E][2F]  dequantisation scale per output channel.
+ *   s_down    : fp32 [E][H]   dequantisation scale per output channel.
+ *   smooth    : fp32 [H]      SmoothQuant scale s_j.
+ *   inv_smooth: fp32 [H]      1/s_j rounded to fp32 (what forward multiplies by).
+ * Code of W'[n][k] is q with W' ~= q * scale[n]; codes lie in [-127, 127]. */
+typedef struct {
+  int8_t *w_gate_up;
+  int8_t *w_down;
+  float *s_gate_up;
+  float *s_down;
+  float *smooth;
+  float *inv_smooth;
+} moe_w8a8_weights;
+
+/* Optional per-stage outputs of moe_w8a8_forward for checking; every pointer
+ * may be NULL. A = T*k. Rows of the permuted tensors are positions in the
+ * expert-grouped order; entries past the number of kept rows (the last
+ * expert_offsets value) are unspecified.
+ *   topk_ids int32 [T][k], topk_w fp32 [T][k]  (routing result or the given ids)
+ *   expert_counts int32 [E] kept rows per expert; expert_offsets int32 [E+1]
+ *   sorted_assign int32 [A] assignment t*k+j of each permuted row
+ *   row_of int32 [A] permuted row of assignment t*k+j, -1 if dropped
+ *   qx int8 [T][H], sx fp32 [T]   per-token codes and scales
+ *   acc1 int32 [A][2F]            GEMM1 accumulators (gate then up)
+ *   h fp32 [A][F]                 SwiGLU output before requantisation
+ *   qh int8 [A][F], sh fp32 [A]   requantised hidden rows and their scales
+ *   y fp32 [A][H]                 dequantised down-projection rows */
+typedef struct {
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *expert_counts;
+  int32_t *expert_offsets;
+  int32_t *sorted_assign;
+  int32_t *row_of;
+  int8_t *qx;
+  float *sx;
+  int32_t *acc1;
+  float *h;
+  int8_t *qh;
+  float *sh;
+  float *y;
+  /* Kernel family of the two grouped GEMMs: 0 = chosen from the shape
+   * (streaming kernels while experts average at most 32 rows, tiled kernels
+   * beyond), 1 = streaming, 2 = tiled. Any other value: MOE_W8A8_ERR_INVALID.
+   * Every choice computes the same result. */
+  int32_t gemm_path;
+} moe_w8a8_debug;
+
+/* Bytes of device workspace that moe_w8a8_forward needs for T tokens, and
+ * that moe_w8a8_calibrate needs (T = 0 gives at least the calibrate size).
+ * A pure function of the arguments; returns 0 for invalid or unsupported
+ * dimensions or T < 0. */
+size_t moe_w8a8_workspace_size(const moe_w8a8_dims *dims, int64_t T);
+
+/* Calibrate and quantise the layer weights ("MiniMax-M3 W8A8 inference on
+ * K100AI" §3.2: SmoothQuant, per-channel weights; published SmoothQuant scale).
+ *   alpha      migration strength in [0, 1] (the page's default is 0.6).
+ *   calib_x    bf16 [n_calib][H] calibration tokens, n_calib >= 0.
+ *   w_gate, w_up fp32 [E][F][H]; w_down fp32 [E][H][F] (unquantised, row-major).
+ *   out        device buffers to fill (layouts above); the struct itself is
+ *              host memory.
+ * Computes, per input channel j: ax_j = max |calib_x[:, j]|,
+ * aw_j = max over all experts and both projections of |W_gate|, |W_up| in
+ * column j, s_j = ax_j^alpha / aw_j^(1-alpha) evaluated in fp64 and rounded to
+ * fp32 (s_j = 1 when ax_j or aw_j is 0), inv_s_j = 1/s_j in fp32; then the
+ * gate/up rows W[n][j] * s_j (fp32) and the down rows are quantised per row:
+ * a = max |row|, code = rint(v * fl32(127/a)) clamped to [-127, 127],
+ * scale = a/127 (an all-zero row gets scale 0 and codes 0).
+ * Workspace: at least moe_w8a8_workspace_size(dims, 0) bytes.
+ * Errors: MOE_W8A8_ERR_INVALID (NULL pointer, alpha outside [0,1],
+ * n_calib < 0), MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE,
+ * MOE_W8A8_ERR_HIP. */
+int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
+                       const uint16_t *calib_x, int64_t n_calib,
+                       const float *w_gate, const float *w_up, const float *w_down,
+                       const moe_w8a8_weights *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward pass of the layer for T tokens (steps 1-6 above).
+ *   x           bf16 [T][H] input tokens.
+ *   router_logits fp32 [T][E], or NULL for pre-routed mode, in which case
+ *   topk_ids    int32 [T][k] and topk_w fp32 [T][k] give the assignments and
+ *               their weights (ids outside [0, E) are treated as dropped; the
+ *               weights are used as given). Exactly one of router_logits and
+ *               (topk_ids, topk_w) must be non-NULL.
+ *   capacity_factor  > 0: each expert keeps at most
+ *               C = ceil(capacity_factor * T * k / E) assignments (evaluated
+ *               in fp64), the first C in (token, slot) order; dropped slots
+ *               contribute nothing and the remaining weights are not
+ *               renormalised. <= 0: no limit.
+ *   out         bf16 [T][H] layer output (written for every token; a token
+ *               whose every slot was dropped gets zeros).
+ *   workspace   at least moe_w8a8_workspace_size(dims, T) bytes; contents on
+ *               entry are ignored.
+ *   debug       NULL, or a host struct of optional device outputs (above).
+ * T == 0 is a successful no-op whatever the other pointers are (empty
+ * tensors may carry NULL addresses). Errors: MOE_W8A8_ERR_INVALID (NULL required
+ * pointer, T < 0, T*k >= 2^31, both or neither routing inputs),
+ * MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
+int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
+                     const uint16_t *x, int64_t T,
+                     const float *router_logits,
+                     const int32_t *topk_ids, const float *topk_w,
+                     float capacity_factor,
+                     uint16_t *out,
+                     void *workspace, size_t workspace_bytes,
+                     const moe_w8a8_debug *debug, void *stream);
+
+/* Static description of a return code (never NULL). */
+const char *moe_w8a8_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W8A8_H */

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+its arguments on the host (no GPU is touched by these cases)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_expert_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a non-NULL pointer that validation never dereferences
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.LIB_PATH):
+        from w8a8_int8_expert_amd import build
+        build.build()
+    return m.load_library()
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(moe_w8a8_\w+)\s*\(", src,
+                                re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(m.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert m.moe_w8a8_strerror(code)
+    assert m.moe_w8a8_strerror(-3) == "workspace missing or too small"
+
+
+def test_workspace_size_pure(lib):
+    d = m.dims(4096, 1536, 64, 8)
+    a = m.moe_w8a8_workspace_size(d, 32)
+    assert a == m.moe_w8a8_workspace_size(d, 32) > 0
+    assert m.moe_w8a8_workspace_size(d, 16384) > a
+    assert m.moe_w8a8_workspace_size(d, 0) >= 2 * 4 * 4096
+    assert m.moe_w8a8_workspace_size(d, -1) == 0
+    assert m.moe_w8a8_workspace_size(m.dims(4096, 1536, 64, 65), 1) == 0     # k > E
+    assert m.moe_w8a8_workspace_size(m.dims(4000, 1536, 64, 8), 1) == 0     # H % 256
+    assert m.moe_w8a8_workspace_size(m.dims(4096, 1536, 2048, 8), 1) == 0   # E > 1024
+
+
+def _weights():
+    return m.moe_w8a8_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def _fwd(d, T=4, logits=FAKE, ids=None, w=None, ws=FAKE, ws_bytes=1 << 40, dbg=None, cf=0.0,
+         weights=None, x=FAKE, out=FAKE):
+    return m.moe_w8a8_forward(d, weights or _weights(), x, T, logits, ids, w, cf, out, ws,
+                              ws_bytes, dbg, stream=0)
+
+
+def test_forward_validation(lib):
+    d = m.dims(256, 512, 8, 2)
+    L = lib
+    # NULL dims
+    assert L.moe_w8a8_forward(None, ctypes.byref(_weights()), FAKE, 4, FAKE, None, None, 0.0,
+                              FAKE, FAKE, 1 << 40, None, None) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(m.dims(256, 512, 8, 9)) == m.MOE_W8A8_ERR_INVALID          # k > E
+    assert _fwd(m.dims(0, 512, 8, 2)) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(d, T=-1) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(d, logits=FAKE, ids=FAKE, w=FAKE) == m.MOE_W8A8_ERR_INVALID  # both
+    assert _fwd(d, logits=None) == m.MOE_W8A8_ERR_INVALID                    # neither
+    assert _fwd(d, logits=None, ids=FAKE, w=None) == m.MOE_W8A8_ERR_INVALID  # half pre-routed
+    assert _fwd(d, x=None) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(d, out=None) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(d, cf=float("nan")) == m.MOE_W8A8_ERR_INVALID
+    bad = _weights()
+    bad.w_down = None
+    assert _fwd(d, weights=bad) == m.MOE_W8A8_ERR_INVALID
+    dbg = m.moe_w8a8_debug()
+    dbg.gemm_path = 3
+    assert _fwd(d, dbg=dbg) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(m.dims(320, 512, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED      # H % 256
+    assert _fwd(m.dims(256, 500, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED      # F % 128
+    assert _fwd(m.dims(256, 512, 64, 33)) == m.MOE_W8A8_ERR_UNSUPPORTED    # k > 32
+    need = m.moe_w8a8_workspace_size(d, 4)
+    assert _fwd(d, ws_bytes=need - 1) == m.MOE_W8A8_ERR_WORKSPACE
+    assert _fwd(d, ws=None) == m.MOE_W8A8_ERR_WORKSPACE
+    assert _fwd(d, T=1 << 30, ws_bytes=1) == m.MOE_W8A8_ERR_INVALID         # T*k >= 2^31
+    # T == 0 is a successful no-op (nothing is enqueued)
+    assert _fwd(d, T=0, ws=None, ws_bytes=0, x=None, out=None) == m.MOE_W8A8_OK
+
+
+def test_calibrate_validation(lib):
+    d = m.dims(256, 512, 8, 2)
+    w = _weights()
+    def cal(d=d, alpha=0.6, n=64, cx=FAKE, ws=FAKE, ws_bytes=1 << 30, out=w):
+        return m.moe_w8a8_calibrate(d, alpha, cx, n, FAKE, FAKE, FAKE, out, ws, ws_bytes, 0)
+    assert cal(alpha=1.5) == m.MOE_W8A8_ERR_INVALID
+    assert cal(alpha=float("nan")) == m.MOE_W8A8_ERR_INVALID
+    assert cal(n=-1) == m.MOE_W8A8_ERR_INVALID
+    assert cal(cx=None) == m.MOE_W8A8_ERR_INVALID
+    bad = _weights()
+    bad.smooth = None
+    assert cal(out=bad) == m.MOE_W8A8_ERR_INVALID
+    assert cal(d=m.dims(256, 500, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED
+    assert cal(ws_bytes=16) == m.MOE_W8A8_ERR_WORKSPACE
+    assert cal(ws=None) == m.MOE_W8A8_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("w8a8_int8_expert_amd")
+    saved = mod._lib
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        mod._lib = saved

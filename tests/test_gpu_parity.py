@@ -1,0 +1,203 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every case prints what names it before touching the GPU. Small shapes are
+compared element by element over every stage; the full-size workloads compare
+every integer stage in full and the GEMM stages on sampled rows the oracle can
+compute one by one, plus the layer output of sampled tokens.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from moe_testlib import (check_act_quant, check_out, check_requant, check_routing_and_grouping,
+                         rows_of, run_gpu, unpack_tiled, upload_weights)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_int8_expert_amd as m
+    m.load_library()
+    return torch
+
+
+@functools.lru_cache(maxsize=2)
+def _layer_and_cal(wl: synth.Workload):
+    layer = synth.make_layer(wl)
+    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
+    return layer, cal
+
+
+def _gpu_layer(wl, cal):
+    import w8a8_int8_expert_amd as m
+    g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
+    upload_weights(g, cal)
+    return g
+
+
+def _full_parity(wl, inputs, cal, gemm_path):
+    g = run_gpu(_gpu_layer(wl, cal), inputs, wl.k, wl.capacity_factor, gemm_path)
+    o = oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits, ids=inputs.ids, w=inputs.w,
+                       capacity_factor=wl.capacity_factor)
+    check_routing_and_grouping(g, o)
+    check_act_quant(g, o["qx"], o["sx"])
+    kept = o["kept"]
+    if kept:
+        acc1 = g["gpu_tensors"]["acc1"].view(-1, 2 * wl.F)[:kept].cpu().numpy()
+        assert np.array_equal(acc1, o["acc1"]), "GEMM1 accumulators differ"
+        qh = g["gpu_tensors"]["qh"].view(-1, wl.F)[:kept].cpu().numpy()
+        sh = g["gpu_tensors"]["sh"][:kept].cpu().numpy()
+        check_requant(qh, sh, o["qh"], o["sh"])
+    return check_out(g["out"], o["out"])
+
+
+SMALL = {
+    "tiny": dict(),
+    "tiny_T1": dict(T=1),
+    "tiny_T3": dict(T=3),
+    "tiny_T65": dict(T=65),
+    "tiny_T200": dict(T=200),
+    "tiny_drop": dict(capacity_factor=0.5, T=40),
+    "tiny_dense": dict(E=1, k=1, T=24),
+    "tiny_E5k3": dict(E=5, k=3, T=50),
+    "tiny_ties": dict(logit_step=0.5, T=70),
+    "tiny_outliers": dict(outlier_frac=0.02, outlier_mult=50.0, lognormal_tokens=True, T=33),
+    "wide_E256": dict(E=256, k=8, H=256, F=128, T=130),
+    "pre_routed": dict(pre_routed=True, zipf_s=1.1, k=1, E=8, T=100),
+    "pre_routed_k2": dict(pre_routed=True, zipf_s=0.0, k=2, E=8, T=17),
+    "H512_F384": dict(H=512, F=384, T=48),
+}
+
+
+@pytest.mark.parametrize("gemm_path", [1, 2])
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_full_parity(torch_cuda, case, gemm_path):
+    wl = synth.workload("tiny", **SMALL[case])
+    _say("[parity] case=%s path=%d T=%d H=%d F=%d E=%d k=%d" % (case, gemm_path, wl.T, wl.H, wl.F,
+                                                                wl.E, wl.k))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    _full_parity(wl, inputs, cal, gemm_path)
+
+
+def test_all_tokens_one_expert_with_capacity(torch_cuda):
+    """Every token ties on every expert: ids 0..k-1, capacity drops the tail."""
+    wl = synth.workload("tiny", T=64, capacity_factor=1.0)
+    _say("[parity] case=all-ties capacity=1.0")
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    inputs.logits = np.zeros_like(inputs.logits)
+    inputs.logits[:, ::2] = -0.0
+    for path in (1, 2):
+        _full_parity(wl, inputs, cal, path)
+
+
+def test_decode_full_parity(torch_cuda):
+    wl = synth.workload("decode")
+    _say("[parity] case=decode full T=%d" % wl.T)
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    for path in (1, 2):
+        _say("[parity] decode path=%d" % path)
+        _full_parity(wl, inputs, cal, path)
+
+
+def _sampled_parity(wl, layer, cal, n_tok=24, seed=0):
+    inputs = synth.make_inputs(wl, layer)
+    g = run_gpu(_gpu_layer(wl, cal), inputs, wl.k, wl.capacity_factor, 0)
+    # integer stages in full
+    if inputs.logits is not None:
+        ids, w = oracle.route(inputs.logits, wl.k)
+    else:
+        ids, w = inputs.ids, inputs.w
+    cap = oracle.capacity(wl.capacity_factor, wl.T, wl.k, wl.E)
+    p = oracle.permute(ids, wl.E, cap)
+    qx, sx = oracle.act_quant(inputs.x, cal["inv_s"])
+    o = dict(ids=ids, w=w, **p)
+    check_routing_and_grouping(g, o)
+    check_act_quant(g, qx, sx)
+    # sampled tokens: all their kept rows through the oracle
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(wl.T, size=min(n_tok, wl.T), replace=False))
+    rows = np.unique(p["row_of"][toks].ravel())
+    rows = rows[rows >= 0].astype(np.int32)
+    r = oracle.expert_rows(rows, ids, p["sorted"], qx, sx, cal)
+    acc1 = rows_of(g, rows, "acc1", 2 * wl.F)
+    assert np.array_equal(acc1, r["acc1"]), "GEMM1 accumulators differ"
+    qh = rows_of(g, rows, "qh", wl.F)
+    sh = g["gpu_tensors"]["sh"].cpu().numpy()[rows]
+    check_requant(qh, sh, r["qh"], r["sh"])
+    yri = np.full(max(p["kept"], 1), -1, np.int64)
+    yri[rows] = np.arange(rows.size)
+    out_o = oracle.combine(toks, w, p["row_of"], r["y"], y_row_index=yri)
+    return check_out(g["out"][toks], out_o)
+
+
+@pytest.mark.parametrize("name", ["prefill", "stress", "ep_share"])
+def test_full_size_sampled_parity(torch_cuda, name):
+    wl = synth.workload(name)
+    _say("[parity] case=%s sampled T=%d H=%d E=%d k=%d F=%d" % (name, wl.T, wl.H, wl.E, wl.k,
+                                                                wl.F))
+    layer, cal = _layer_and_cal(wl if name != "prefill" else synth.workload("decode"))
+    _sampled_parity(wl, layer, cal)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "stress", "ep_share"])
+def test_calibrate_parity(torch_cuda, name):
+    """GPU calibration reproduces the oracle's scales and codes bit for bit."""
+    import torch
+    import w8a8_int8_expert_amd as m
+    from moe_testlib import bf16_tensor
+    wl = synth.workload(name)
+    _say("[calibrate] case=%s H=%d F=%d E=%d" % (name, wl.H, wl.F, wl.E))
+    layer, cal = _layer_and_cal(wl)
+    dev = torch.device("cuda")
+    g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
+    wg = torch.from_numpy(layer.w_gate).to(dev)
+    wu = torch.from_numpy(layer.w_up).to(dev)
+    wd = torch.from_numpy(layer.w_down).to(dev)
+    g.calibrate(bf16_tensor(layer.calib_x, dev), wg, wu, wd, wl.alpha)
+    torch.cuda.synchronize()
+    del wg, wu, wd
+    assert np.array_equal(g.smooth.cpu().numpy().view(np.uint32), cal["s"].view(np.uint32))
+    assert np.array_equal(g.inv_smooth.cpu().numpy().view(np.uint32), cal["inv_s"].view(np.uint32))
+    assert np.array_equal(g.s_gate_up.cpu().numpy().view(np.uint32), cal["sw_gu"].view(np.uint32))
+    assert np.array_equal(g.s_down.cpu().numpy().view(np.uint32), cal["sw_d"].view(np.uint32))
+    q_gu = unpack_tiled(g.w_gate_up.cpu().numpy(), wl.E, 2 * wl.F, wl.H)
+    assert np.array_equal(q_gu, cal["q_gu"])
+    q_d = unpack_tiled(g.w_down.cpu().numpy(), wl.E, wl.H, wl.F)
+    assert np.array_equal(q_d, cal["q_d"])
+
+
+def test_deterministic_and_t0(torch_cuda):
+    """Two runs give identical bits; T = 0 is a no-op."""
+    import torch
+    import w8a8_int8_expert_amd as m
+    wl = synth.workload("tiny", T=100)
+    _say("[parity] case=determinism")
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    gl = _gpu_layer(wl, cal)
+    for path in (1, 2):
+        a = run_gpu(gl, inputs, wl.k, 0.0, path)["out"]
+        b = run_gpu(gl, inputs, wl.k, 0.0, path)["out"]
+        assert np.array_equal(a, b)
+    x0 = torch.empty(0, wl.H, dtype=torch.bfloat16, device="cuda")
+    lg0 = torch.empty(0, wl.E, dtype=torch.float32, device="cuda")
+    out0 = gl.forward(x0, router_logits=lg0)
+    assert out0.shape == (0, wl.H)
+    rc = m.moe_w8a8_forward(gl.d, gl.weights, x0, 0, lg0, None, None, 0.0, out0, None, 0)
+    assert rc == m.MOE_W8A8_OK

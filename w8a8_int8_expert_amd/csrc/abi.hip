@@ -1,0 +1,198 @@
+// abi.hip -- host side of the C ABI declared in include/moe_w8a8.h:
+// argument validation (before anything touches HIP), workspace carving and
+// the launch sequence of one forward / calibrate call on the caller's stream.
+#include <math.h>
+
+#include "moe_internal.h"
+#include "moe_w8a8.h"
+
+namespace moe {
+
+namespace {
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Streaming kernels are used while experts get few rows on average; past
+// that the tiled kernels reuse each weight panel across 128-row tiles.
+constexpr int64_t kStreamMaxAvgRows = 32;
+
+bool dims_valid(const moe_w8a8_dims *d) {
+  return d && d->hidden > 0 && d->ffn > 0 && d->num_experts > 0 && d->top_k > 0 &&
+         d->top_k <= d->num_experts;
+}
+bool dims_supported(const moe_w8a8_dims *d) {
+  return d->hidden % 256 == 0 && d->hidden <= 65536 && d->ffn % 128 == 0 && d->ffn <= 65536 &&
+         d->num_experts <= kMaxExperts && d->top_k <= kMaxTopK;
+}
+}  // namespace
+
+FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
+  FwdLayout L{};
+  const int64_t A = T * k;
+  L.nblk = (T + kRouteTokens - 1) / kRouteTokens;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  L.ids = take(sizeof(int32_t) * A);
+  L.wts = take(sizeof(float) * A);
+  L.blk_hist = take(sizeof(int32_t) * (size_t)L.nblk * E);
+  L.counts = take(sizeof(int32_t) * E);
+  L.offsets = take(sizeof(int32_t) * (E + 1));
+  L.mtile_off = take(sizeof(int32_t) * (E + 1));
+  L.sorted = take(sizeof(int32_t) * A);
+  L.row_of = take(sizeof(int32_t) * A);
+  L.qx = take((size_t)T * H);
+  L.sx = take(sizeof(float) * T);
+  L.h = take(sizeof(float) * (size_t)A * F);
+  L.amax = take(sizeof(uint32_t) * (size_t)L.nblk * kRouteTokens * k);
+  L.qh = take((size_t)A * F);
+  L.sh = take(sizeof(float) * A);
+  L.y = take(sizeof(float) * (size_t)A * H);
+  L.total = o;
+  return L;
+}
+
+size_t calib_ws_bytes(int H) { return align_up(sizeof(uint32_t) * H) * 2; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_w8a8_workspace_size(const moe_w8a8_dims *d, int64_t T) {
+  if (!dims_valid(d) || !dims_supported(d) || T < 0) return 0;
+  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return 0;
+  const size_t f = fwd_layout(T, d->hidden, d->ffn, d->num_experts, d->top_k).total;
+  const size_t c = calib_ws_bytes(d->hidden);
+  return f > c ? f : c;
+}
+
+extern "C" const char *moe_w8a8_strerror(int code) {
+  switch (code) {
+    case MOE_W8A8_OK: return "success";
+    case MOE_W8A8_ERR_INVALID: return "invalid argument";
+    case MOE_W8A8_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_W8A8_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_W8A8_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+#define MOE_CHECK(expr)                                  \
+  do {                                                   \
+    if ((expr) != hipSuccess) return MOE_W8A8_ERR_HIP;   \
+  } while (0)
+
+extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uint16_t *calib_x,
+                                  int64_t n_calib, const float *w_gate, const float *w_up,
+                                  const float *w_down, const moe_w8a8_weights *out,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!dims_valid(d) || !out || !w_gate || !w_up || !w_down || n_calib < 0 ||
+      (n_calib > 0 && !calib_x) || !(alpha >= 0.0f && alpha <= 1.0f))
+    return MOE_W8A8_ERR_INVALID;
+  if (!out->w_gate_up || !out->w_down || !out->s_gate_up || !out->s_down || !out->smooth ||
+      !out->inv_smooth)
+    return MOE_W8A8_ERR_INVALID;
+  if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
+  const int H = d->hidden, F = d->ffn, E = d->num_experts;
+  if (!workspace || workspace_bytes < calib_ws_bytes(H)) return MOE_W8A8_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t *ax = (uint32_t *)workspace;
+  uint32_t *aw = (uint32_t *)((char *)workspace + calib_ws_bytes(H) / 2);
+  MOE_CHECK(launch_calib_colmax(calib_x, n_calib, w_gate, w_up, H, F, E, ax, aw, st));
+  MOE_CHECK(launch_calib_smooth(ax, aw, alpha, H, out->smooth, out->inv_smooth, st));
+  MOE_CHECK(launch_calib_quant(w_gate, w_up, w_down, out->smooth, H, F, E, out->w_gate_up,
+                               out->s_gate_up, out->w_down, out->s_down, st));
+  return MOE_W8A8_OK;
+}
+
+extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *wt,
+                                const uint16_t *x, int64_t T, const float *router_logits,
+                                const int32_t *topk_ids, const float *topk_w,
+                                float capacity_factor, uint16_t *out, void *workspace,
+                                size_t workspace_bytes, const moe_w8a8_debug *dbg,
+                                void *stream) {
+  if (!dims_valid(d) || !wt || T < 0) return MOE_W8A8_ERR_INVALID;
+  if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
+  const bool routed = router_logits != nullptr;
+  const bool pre = topk_ids != nullptr || topk_w != nullptr;
+  if (routed == pre || (pre && (!topk_ids || !topk_w))) return MOE_W8A8_ERR_INVALID;
+  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (!x || !out || !wt->w_gate_up || !wt->w_down || !wt->s_gate_up || !wt->s_down ||
+      !wt->inv_smooth)
+    return MOE_W8A8_ERR_INVALID;
+  if (isnan(capacity_factor)) return MOE_W8A8_ERR_INVALID;
+  if (dbg && (dbg->gemm_path < 0 || dbg->gemm_path > 2)) return MOE_W8A8_ERR_INVALID;
+  if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
+  const int H = d->hidden, F = d->ffn, E = d->num_experts, k = d->top_k;
+  const FwdLayout L = fwd_layout(T, H, F, E, k);
+  if (!workspace || workspace_bytes < L.total) return MOE_W8A8_ERR_WORKSPACE;
+
+  const int64_t A = T * k;
+  int64_t capacity = 0;
+  if (capacity_factor > 0.0f) {
+    const double c = ceil((double)capacity_factor * (double)T * (double)k / (double)E);
+    capacity = c >= (double)A ? A : (int64_t)c;
+    if (capacity < 1) capacity = 1;
+  }
+  int path = dbg ? dbg->gemm_path : 0;
+  if (path == 0) path = A <= kStreamMaxAvgRows * E ? 1 : 2;
+
+  char *ws = (char *)workspace;
+  int32_t *ids = (int32_t *)(ws + L.ids);
+  float *wts = (float *)(ws + L.wts);
+  int32_t *blk_hist = (int32_t *)(ws + L.blk_hist);
+  int32_t *counts = (int32_t *)(ws + L.counts);
+  int32_t *offsets = (int32_t *)(ws + L.offsets);
+  int32_t *mtile_off = (int32_t *)(ws + L.mtile_off);
+  int32_t *sorted = (int32_t *)(ws + L.sorted);
+  int32_t *row_of = (int32_t *)(ws + L.row_of);
+  int8_t *qx = (int8_t *)(ws + L.qx);
+  float *sx = (float *)(ws + L.sx);
+  float *h = (float *)(ws + L.h);
+  uint32_t *amax = (uint32_t *)(ws + L.amax);
+  int8_t *qh = (int8_t *)(ws + L.qh);
+  float *sh = (float *)(ws + L.sh);
+  float *y = (float *)(ws + L.y);
+  int32_t *acc1_dbg = dbg ? dbg->acc1 : nullptr;
+  hipStream_t st = (hipStream_t)stream;
+
+  MOE_CHECK(launch_route_hist(router_logits, topk_ids, topk_w, T, E, k, ids, wts, blk_hist, amax,
+                              st));
+  MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, mtile_off, st));
+  MOE_CHECK(launch_scatter(ids, blk_hist, offsets, T, E, k, capacity, sorted, row_of, st));
+  MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st));
+  if (path == 1) {
+    MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, offsets, wt->w_gate_up, wt->s_gate_up,
+                                  H, F, E, h, amax, acc1_dbg, st));
+  } else {
+    MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, offsets, mtile_off, A, wt->w_gate_up,
+                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st));
+  }
+  MOE_CHECK(launch_requant(h, amax, offsets, E, A, F, qh, sh, st));
+  if (path == 1) {
+    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, offsets, wt->w_down, wt->s_down, H, F, E, y, st));
+  } else {
+    MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, offsets, mtile_off, A, wt->w_down, wt->s_down, H,
+                                 F, E, y, st));
+  }
+  MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st));
+
+  if (dbg) {
+    auto cp = [&](void *dst, const void *src, size_t bytes) -> hipError_t {
+      if (!dst || bytes == 0) return hipSuccess;
+      return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st);
+    };
+    MOE_CHECK(cp(dbg->topk_ids, ids, sizeof(int32_t) * A));
+    MOE_CHECK(cp(dbg->topk_w, wts, sizeof(float) * A));
+    MOE_CHECK(cp(dbg->expert_counts, counts, sizeof(int32_t) * E));
+    MOE_CHECK(cp(dbg->expert_offsets, offsets, sizeof(int32_t) * (E + 1)));
+    MOE_CHECK(cp(dbg->sorted_assign, sorted, sizeof(int32_t) * A));
+    MOE_CHECK(cp(dbg->row_of, row_of, sizeof(int32_t) * A));
+    MOE_CHECK(cp(dbg->qx, qx, (size_t)T * H));
+    MOE_CHECK(cp(dbg->sx, sx, sizeof(float) * T));
+    MOE_CHECK(cp(dbg->h, h, sizeof(float) * (size_t)A * F));
+    MOE_CHECK(cp(dbg->qh, qh, (size_t)A * F));
+    MOE_CHECK(cp(dbg->sh, sh, sizeof(float) * A));
+    MOE_CHECK(cp(dbg->y, y, sizeof(float) * (size_t)A * H));
+  }
+  return MOE_W8A8_OK;
+}

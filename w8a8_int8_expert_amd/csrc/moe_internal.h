@@ -1,0 +1,121 @@
+// moe_internal.h -- internal declarations shared by the HIP sources of
+// libmoe_w8a8 (kernel launchers, device helpers, workspace carving).
+// Not part of the public ABI (include/moe_w8a8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Tokens routed (and histogrammed) per block of the routing kernel.
+constexpr int kRouteTokens = 64;
+// Rows per M tile of the tiled grouped GEMMs.
+constexpr int kTiledBM = 128;
+// Output channels per block of the tiled GEMMs (gate+up rows for GEMM1).
+constexpr int kTiledBN = 256;
+// Maximum experts (LDS histograms are sized for it).
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+// ------------------------------------------------------------ device helpers
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+// fp32 -> bf16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+// Symmetric INT8 code of v for reciprocal scale rr = fl32(127/amax):
+// rint(fl32(v*rr)) clamped to [-127, 127].
+__device__ __forceinline__ int q8(float v, float rr) {
+  float c = __builtin_rintf(v * rr);
+  c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
+  return (int)c;
+}
+// Byte offset of the 1 KB fragment tile (n_tile, k_tile) of a fragment-tiled
+// [N][K] INT8 matrix.
+__device__ __forceinline__ size_t frag_tile(int n_tile, int k_tile, int K) {
+  return ((size_t)n_tile * (size_t)(K >> 6) + (size_t)k_tile) << 10;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+#endif
+
+// ---------------------------------------------------------------- workspace
+// Regions of the forward workspace (byte offsets from its base).
+struct FwdLayout {
+  size_t ids, wts, blk_hist, counts, offsets, mtile_off, sorted, row_of, qx, sx, h, amax, qh,
+      sh, y, total;
+  int64_t nblk;  // routing blocks
+};
+FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k);
+// Calibrate workspace: ax[H], aw[H] as uint32 float bits.
+size_t calib_ws_bytes(int H);
+
+// ----------------------------------------------------------------- launchers
+// Each returns hipGetLastError() after enqueueing on `st`.
+hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
+                             int64_t T, int E, int k, int32_t *ids, float *wts,
+                             int32_t *blk_hist, uint32_t *amax, hipStream_t st);
+hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
+                       int32_t *offsets, int32_t *mtile_off, hipStream_t st);
+hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
+                          int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
+                          int32_t *row_of, hipStream_t st);
+hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
+                            float *sx, hipStream_t st);
+hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *offsets, int E,
+                          int64_t A, int F, int8_t *qh, float *sh, hipStream_t st);
+hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
+                               const int32_t *counts, const int32_t *offsets, const int8_t *w_gu,
+                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
+                               int32_t *acc1_dbg, hipStream_t st);
+hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
+                               const int32_t *offsets, const int8_t *w_d, const float *s_d, int H,
+                               int F, int E, float *y, hipStream_t st);
+hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
+                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
+                              int32_t *acc1_dbg, hipStream_t st);
+hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
+                              const int32_t *offsets, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
+                              hipStream_t st);
+hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
+                          int H, int k, uint16_t *out, hipStream_t st);
+// calibrate
+hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const float *w_gate,
+                               const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,
+                               hipStream_t st);
+hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alpha, int H,
+                               float *s, float *inv_s, hipStream_t st);
+hipError_t launch_calib_quant(const float *w_gate, const float *w_up, const float *w_down,
+                              const float *s, int H, int F, int E, int8_t *w_gu, float *s_gu,
+                              int8_t *w_d, float *s_d, hipStream_t st);
+
+}  // namespace moe
