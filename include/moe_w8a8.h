@@ -123,6 +123,12 @@ typedef struct {
    * beyond), 1 = streaming, 2 = tiled. Any other value: MOE_W8A8_ERR_INVALID.
    * Every choice computes the same result. */
   int32_t gemm_path;
+  /* NULL, or an array of 16 hipEvent_t (as void*): entry 2s is recorded on
+   * the stream right before stage s is enqueued and entry 2s+1 right after,
+   * for s = 0 route, 1 scan, 2 scatter, 3 activation quant, 4 GEMM1,
+   * 5 requant, 6 GEMM2, 7 combine. NULL entries are skipped. Lets a caller
+   * time one kernel of the layer on the layer's own stream. */
+  void **stage_events;
 } moe_w8a8_debug;
 
 /* Bytes of device workspace that moe_w8a8_forward needs for T tokens, and

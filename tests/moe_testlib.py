@@ -80,8 +80,8 @@ def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, want=("all",
         qh=torch.empty(A * F, dtype=torch.int8, device=dev),
         sh=torch.empty(A, dtype=torch.float32, device=dev),
         y=torch.empty(A * H, dtype=torch.float32, device=dev))
-    dbg = m.moe_w8a8_debug(*(dbgt[f].data_ptr() for f, _ in m.moe_w8a8_debug._fields_[:-1]),
-                           gemm_path)
+    dbg = m.moe_w8a8_debug(*(dbgt[f].data_ptr() for f, _ in m.moe_w8a8_debug._fields_[:-2]),
+                           gemm_path, None)
     out = layer_gpu.forward(x, router_logits=logits, topk_ids=ids, topk_w=w,
                             capacity_factor=capacity_factor, debug=dbg)
     torch.cuda.synchronize()

@@ -39,7 +39,10 @@ class moe_w8a8_weights(ctypes.Structure):
 class moe_w8a8_debug(ctypes.Structure):
     _fields_ = [("topk_ids", _P), ("topk_w", _P), ("expert_counts", _P), ("expert_offsets", _P),
                 ("sorted_assign", _P), ("row_of", _P), ("qx", _P), ("sx", _P), ("acc1", _P),
-                ("h", _P), ("qh", _P), ("sh", _P), ("y", _P), ("gemm_path", ctypes.c_int32)]
+                ("h", _P), ("qh", _P), ("sh", _P), ("y", _P), ("gemm_path", ctypes.c_int32),
+                ("stage_events", ctypes.POINTER(_P))]
+
+STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine")
 
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_forward",
