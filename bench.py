@@ -154,6 +154,15 @@ def time_workload(gl: GpuLayer, wl, inputs, steps, warmup, hip, timed_stages):
     return dict(seconds=t1 - t0, stage_ms=stage_ms, counts=counts_h, out=out)
 
 
+def launched_stages(wl):
+    """Stages that have a launch of their own (and so a timing pair): up to
+    2048 assignments route, grouping and activation quantisation are one
+    launch, timed as "route"."""
+    fused = wl.T * wl.k <= 2048
+    pre = ["route"] if fused else ["route", "scan", "scatter", "act_quant"]
+    return pre + ["gemm1", "requant", "gemm2", "combine"]
+
+
 def layer_bytes(wl, counts, T):
     touched = int((counts > 0).sum())
     b = touched * (3 * wl.H * wl.F + 4 * (2 * wl.F + wl.H)) + 4 * wl.H + 4 * T * wl.H
@@ -231,8 +240,7 @@ def main():
     inputs = synth.make_inputs(wl, layer)
     gl.wl = wl
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
-    r = time_workload(gl, wl, inputs, args.steps, args.warmup, hip,
-                      ["gemm1", "gemm2", "act_quant", "requant", "combine", "route"])
+    r = time_workload(gl, wl, inputs, args.steps, args.warmup, hip, launched_stages(wl))
     T = wl.T
     sec = r["seconds"]
     ms_step = sec * 1e3 / args.steps
@@ -277,8 +285,7 @@ def main():
         log("timing prefill: 3 warmup + %d steps" % args.prefill_steps)
         pin = synth.make_inputs(pwl, layer)
         gl.wl = pwl
-        pr = time_workload(gl, pwl, pin, args.prefill_steps, 3, hip,
-                           ["gemm1", "gemm2", "requant", "combine", "act_quant"])
+        pr = time_workload(gl, pwl, pin, args.prefill_steps, 3, hip, launched_stages(pwl))
         pA = int(pr["counts"].sum())
         psec = pr["seconds"]
         g1ops = 4 * pA * pwl.H * pwl.F

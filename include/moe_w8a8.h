@@ -18,9 +18,11 @@
  *               requantised to INT8 per (token, expert) row (K100AI page
  *               §1.2 and §4.3: INT8 GEMM with integer accumulation; stay in
  *               the INT8 domain between consecutive matmuls);
- *   5. GEMM2    per expert, INT8 down projection, dequantised to fp32;
- *   6. combine  out[t] = sum over kept slots of w[t][j] * y[row], rounded to
- *               bfloat16 (Day0 page §四: un-sort and weighted sum).
+ *   5. GEMM2    per expert, INT8 down projection, dequantised per row and
+ *               per output channel to fp32;
+ *   6. combine  out[t] = sum over kept slots of w[t][j] * y[row], summed in
+ *               fp32 and rounded to bfloat16 (Day0 page §四: un-sort and
+ *               weighted sum).
  * moe_w8a8_calibrate prepares the quantised weights (K100AI page §3.2:
  * SmoothQuant with migration strength alpha, per-output-channel weights).
  *
@@ -123,11 +125,15 @@ typedef struct {
    * beyond), 1 = streaming, 2 = tiled. Any other value: MOE_W8A8_ERR_INVALID.
    * Every choice computes the same result. */
   int32_t gemm_path;
-  /* NULL, or an array of 16 hipEvent_t (as void*): entry 2s is recorded on
-   * the stream right before stage s is enqueued and entry 2s+1 right after,
-   * for s = 0 route, 1 scan, 2 scatter, 3 activation quant, 4 GEMM1,
-   * 5 requant, 6 GEMM2, 7 combine. NULL entries are skipped. Lets a caller
-   * time one kernel of the layer on the layer's own stream. */
+  /* NULL, or an array of 16 hipEvent_t (as void*) to time the layer's
+   * kernels on its own stream: entries 2s and 2s+1 are stamped with the
+   * start and the end of the execution of the launch that performs stage s
+   * (s = 0 route, 1 scan, 2 scatter, 3 activation quant, 4 GEMM1, 5 requant,
+   * 6 GEMM2, 7 combine), by that launch's own dispatch (hipExtLaunchKernel),
+   * so timing inserts nothing between the kernels. Stages fused into one
+   * launch are timed by the pair of the first of them: for T*k <= 2048,
+   * stages 0-3 are one launch and pairs 1-3 are left untouched. NULL entries
+   * are skipped. */
   void **stage_events;
 } moe_w8a8_debug;
 

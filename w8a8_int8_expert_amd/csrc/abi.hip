@@ -155,48 +155,49 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   int32_t *acc1_dbg = dbg ? dbg->acc1 : nullptr;
   hipStream_t st = (hipStream_t)stream;
 
-  void **ev = dbg ? dbg->stage_events : nullptr;
-  auto mark = [&](int slot) -> hipError_t {
-    if (!ev || !ev[slot]) return hipSuccess;
-    return hipEventRecord((hipEvent_t)ev[slot], st);
-  };
+  const bool small = A <= kSmallA;
 
-  MOE_CHECK(mark(0));
-  MOE_CHECK(launch_route_hist(router_logits, topk_ids, topk_w, T, E, k, ids, wts, blk_hist, amax,
-                              st));
-  MOE_CHECK(mark(1));
-  MOE_CHECK(mark(2));
-  MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, mtile_off, st));
-  MOE_CHECK(mark(3));
-  MOE_CHECK(mark(4));
-  MOE_CHECK(launch_scatter(ids, blk_hist, offsets, T, E, k, capacity, sorted, row_of, st));
-  MOE_CHECK(mark(5));
-  MOE_CHECK(mark(6));
-  MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st));
-  MOE_CHECK(mark(7));
-  MOE_CHECK(mark(8));
-  if (path == 1) {
-    MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, offsets, wt->w_gate_up, wt->s_gate_up,
-                                  H, F, E, h, amax, acc1_dbg, st));
+  // Stage events: pair s is stamped by the dispatch of the launch that
+  // performs stage s; a launch that fuses several stages takes the pair of
+  // the first of them.
+  void **ev = dbg ? dbg->stage_events : nullptr;
+  auto tm = [&](int s) -> Timing {
+    Timing t;
+    if (ev) {
+      t.start = (hipEvent_t)ev[2 * s];
+      t.stop = (hipEvent_t)ev[2 * s + 1];
+    }
+    return t;
+  };
+  enum { kRoute, kScan, kScatter, kActQ, kG1, kReq, kG2, kComb };
+
+  if (small) {
+    MOE_CHECK(launch_prologue_small(router_logits, topk_ids, topk_w, (int)T, E, k, capacity, ids,
+                                    wts, counts, offsets, mtile_off, sorted, row_of, x,
+                                    wt->inv_smooth, H, qx, sx, amax, st, tm(kRoute)));
   } else {
+    MOE_CHECK(launch_route_hist(router_logits, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
+                                amax, st, tm(kRoute)));
+    MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, mtile_off, st,
+                          tm(kScan)));
+    MOE_CHECK(launch_scatter(ids, blk_hist, offsets, T, E, k, capacity, sorted, row_of, st,
+                             tm(kScatter)));
+    MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ)));
+  }
+  if (path == 1)
+    MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, offsets, wt->w_gate_up,
+                                  wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
+  else
     MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, offsets, mtile_off, A, wt->w_gate_up,
-                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st));
-  }
-  MOE_CHECK(mark(9));
-  MOE_CHECK(mark(10));
-  MOE_CHECK(launch_requant(h, amax, offsets, E, A, F, qh, sh, st));
-  MOE_CHECK(mark(11));
-  MOE_CHECK(mark(12));
-  if (path == 1) {
-    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, offsets, wt->w_down, wt->s_down, H, F, E, y, st));
-  } else {
+                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
+  MOE_CHECK(launch_requant(h, amax, offsets, E, A, F, qh, sh, st, tm(kReq)));
+  if (path == 1)
+    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, offsets, wt->w_down, wt->s_down, H, F, E, y, st,
+                                  tm(kG2)));
+  else
     MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, offsets, mtile_off, A, wt->w_down, wt->s_down, H,
-                                 F, E, y, st));
-  }
-  MOE_CHECK(mark(13));
-  MOE_CHECK(mark(14));
-  MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st));
-  MOE_CHECK(mark(15));
+                                 F, E, y, st, tm(kG2)));
+  MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st, tm(kComb)));
 
   if (dbg) {
     auto cp = [&](void *dst, const void *src, size_t bytes) -> hipError_t {

@@ -2,54 +2,71 @@
 //
 // "MiniMax-M3 W8A8 inference on K100AI" (mhpq.cn/news/1068415) §1.1: decode
 // is bound by reading expert weights, and W8A8 halves those bytes (§1.3);
-// §4.3: one kernel runs a whole batch of experts instead of many small GEMMs.
-// Here every block streams one panel of one expert's fragment-tiled weights
+// §4.3: one kernel runs a whole batch of experts instead of many small GEMMs,
+// and the matmuls stay in INT8 with no dequantise between them.
+// Every block streams one panel of one expert's fragment-tiled weights
 // exactly once, from HBM, as contiguous 1 KB wavefront loads, and multiplies
 // it with all rows routed to that expert (INT8 x INT8 -> INT32 on
 // v_mfma_i32_16x16x64_i8). The weight panel is the MFMA A operand (16 output
 // channels), the token rows the B operand (16 rows per tile), so the few
 // rows of a decode step cost no extra weight traffic.
 //
-// Grid (panels, E); block = 4 wavefronts splitting K; partial INT32 sums are
-// reduced exactly through LDS, then the epilogue:
+// Block = 4 wavefronts = (4/KS) panel groups x KS K-splits. A group owns NPW
+// panel units (GEMM1 unit: the 16 gate rows f..f+15 and the matching 16 up
+// rows; GEMM2 unit: 16 output channels); its KS wavefronts take the 1 KB
+// k-tiles ks, ks+KS, ks+2KS, ... so that at any moment the block reads
+// adjacent tiles of each panel. With KS > 1 the partial INT32 sums are
+// reduced exactly through LDS. Grid (units / ((4/KS)*NPW), E). Epilogue:
 //   GEMM1 (gate/up, K = H): g = acc_g*sx*s_g, u = acc_u*sx*s_u,
 //         h = silu(g)*u (fp32) -> h[row][f]; row max |h| -> amax (atomic max
 //         on the float bits, order independent);
 //   GEMM2 (down, K = F):    y[row][n] = acc*sh*s_d[n] (fp32).
-#include "moe_internal.h"
+// Requantisation and combine are launches of their own: handing a unit of
+// work to its last-finishing block needs a device-scope release per block,
+// which writes back the XCD's L2 and cost more than the launches it saved.
+#include "layer_device.h"
 
 namespace moe {
 namespace {
 
 constexpr int kRT = 2;  // row tiles of 16 held per pass (32 rows)
 
-// kGateUp: GEMM1 (panel pair gate p / up F/16+p). Otherwise GEMM2 with NP
-// consecutive output panels per block.
-template <bool kGateUp, int NP>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(
-    const int8_t *__restrict__ act, const float *__restrict__ act_scale,
-    const int32_t *__restrict__ sorted, int k, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, const int8_t *__restrict__ w,
-    const float *__restrict__ wscale, int K, int F, int H, float *__restrict__ out,
-    uint32_t *__restrict__ amax, int32_t *__restrict__ acc1_dbg) {
-  constexpr int NA = kGateUp ? 2 : NP;  // A panels per k tile
+struct StreamArgs {
+  const int8_t *act;        // GEMM1: qx [T][H]; GEMM2: qh [A][F]
+  const float *act_scale;   // GEMM1: sx [T];    GEMM2: sh [A]
+  const int32_t *sorted;    // GEMM1 only
+  int k;
+  const int32_t *counts, *offsets;
+  const int8_t *w;          // fragment-tiled weights
+  const float *wscale;
+  int K, F, H;
+  float *out;               // GEMM1: h [A][F]; GEMM2: y [A][H]
+  uint32_t *amax;           // GEMM1 only
+  int32_t *acc1_dbg;        // GEMM1 only, may be NULL
+};
+
+template <bool kGateUp, int NPW, int KS, int U>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
+  constexpr int NA = kGateUp ? 2 * NPW : NPW;  // weight panels per group
+  constexpr int NG = 4 / KS;                   // panel groups per block
   const int e = blockIdx.y;
-  const int p = blockIdx.x;
-  const int R = counts[e];
+  const int R = a.counts[e];
   if (R == 0) return;
-  const int row0 = offsets[e];
+  const int row0 = a.offsets[e];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave / KS, ks = wave % KS;
+  const int K = a.K, F = a.F, H = a.H;
   const int KT = K >> 6;
-  const int kt0 = (wave * KT) >> 2, kt1 = ((wave + 1) * KT) >> 2;
-  const int N = kGateUp ? 2 * F : H;  // rows of the expert's weight matrix
-  const int8_t *wexp = w + (size_t)e * (size_t)N * (size_t)K;
+  const int u0 = (blockIdx.x * NG + grp) * NPW;  // first panel unit of this group
+  const int N = kGateUp ? 2 * F : H;             // rows of the expert's weight matrix
+  const int8_t *wexp = a.w + (size_t)e * (size_t)N * (size_t)K;
   const int8_t *wp[NA];
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    const int nt = kGateUp ? (a == 0 ? p : (F >> 4) + p) : p * NP + a;
-    wp[a] = wexp + frag_tile(nt, 0, K) + lane * 16;
+  for (int i = 0; i < NA; ++i) {
+    const int nt = kGateUp ? (i < NPW ? u0 + i : (F >> 4) + u0 + i - NPW) : u0 + i;
+    wp[i] = wexp + frag_tile(nt, 0, K) + lane * 16;
   }
-  __shared__ v4i red[4][NA * kRT][64];
+  __shared__ v4i red[KS > 1 ? 4 : 1][KS > 1 ? NA * kRT : 1][64];
 
   for (int base = 0; base < R; base += 16 * kRT) {
     const int8_t *bp[kRT];
@@ -59,54 +76,77 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
       const int r = base + rt * 16 + (lane & 15);
       bv[rt] = r < R;
       size_t arow = 0;
-      if (bv[rt]) arow = kGateUp ? (size_t)(sorted[row0 + r] / k) : (size_t)(row0 + r);
-      bp[rt] = act + arow * (size_t)K + (lane >> 4) * 16;
+      if (bv[rt]) arow = kGateUp ? (size_t)(a.sorted[row0 + r] / a.k) : (size_t)(row0 + r);
+      bp[rt] = a.act + arow * (size_t)K + (lane >> 4) * 16;
     }
     v4i acc[NA][kRT];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) acc[a][rt] = v4i{0, 0, 0, 0};
-#pragma unroll 4
-    for (int kt = kt0; kt < kt1; ++kt) {
-      v4i af[NA], bf[kRT];
+      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = v4i{0, 0, 0, 0};
+    // This wavefront's k-tiles, U at a time: all loads of a batch are issued
+    // before its MFMAs, so U*NA weight tiles are in flight per wavefront.
+    const int nk = (KT - ks + KS - 1) / KS;
+    auto load = [&](int it, v4i *af, v4i *bf) {
+      const int kt = ks + it * KS;
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
-        af[a] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp[a] + ((size_t)kt << 10)));
+      for (int i = 0; i < NA; ++i)
+        af[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp[i] + ((size_t)kt << 10)));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
         bf[rt] = bv[rt] ? *reinterpret_cast<const v4i *>(bp[rt] + kt * 64) : v4i{0, 0, 0, 0};
+    };
+    auto mma = [&](const v4i *af, const v4i *bf) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int i = 0; i < NA; ++i)
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[a][rt] = mfma16(af[a], bf[rt], acc[a][rt]);
+        for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma16(af[i], bf[rt], acc[i][rt]);
+    };
+    int it = 0;
+    for (; it + U <= nk; it += U) {
+      v4i af[U][NA], bf[U][kRT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load(it + u, af[u], bf[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) mma(af[u], bf[u]);
     }
+    for (; it < nk; ++it) {
+      v4i af[NA], bf[kRT];
+      load(it, af, bf);
+      mma(af, bf);
+    }
+    if (KS > 1) {
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+      for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) red[wave][a * kRT + rt][lane] = acc[a][rt];
-    __syncthreads();
-    // Epilogue: combination c = (panel group, row tile) handled by wave c % 4.
-    constexpr int NC = (kGateUp ? 1 : NP) * kRT;
-    for (int c = wave; c < NC; c += 4) {
-      const int rt = c % kRT, pg = c / kRT;
+        for (int rt = 0; rt < kRT; ++rt) red[wave][i * kRT + rt][lane] = acc[i][rt];
+      __syncthreads();
+    }
+    // Epilogue: combination c = (unit q, row tile rt) of the group, taken by
+    // its wavefront ks == c % KS. Lane holds row base + rt*16 + (lane & 15)
+    // and the 4 output channels ch0..ch0+3 of the unit, ch0 = (lane >> 4)*4.
+    const int ch0 = (lane >> 4) * 4;
+#pragma unroll
+    for (int c = 0; c < NPW * kRT; ++c) {
+      if (c % KS != ks) continue;
+      const int q = c / kRT, rt = c % kRT;
       const int r = base + rt * 16 + (lane & 15);
       const bool valid = r < R;
-      const int ch0 = (lane >> 4) * 4;  // first of this lane's 4 output channels
-      if (kGateUp) {
-        v4i g = red[0][rt][lane], u = red[0][kRT + rt][lane];
+      const int row = row0 + r;
+      auto total = [&](int i) -> v4i {
+        if (KS == 1) return acc[i][rt];
+        v4i sum = red[grp * KS][i * kRT + rt][lane];
 #pragma unroll
-        for (int wv = 1; wv < 4; ++wv) {
-          g += red[wv][rt][lane];
-          u += red[wv][kRT + rt][lane];
-        }
+        for (int w = 1; w < KS; ++w) sum += red[grp * KS + w][i * kRT + rt][lane];
+        return sum;
+      };
+      if (kGateUp) {
         float hmax = 0.0f;
+        const v4i g = total(q), u = total(NPW + q);
         if (valid) {
-          const int row = row0 + r;
-          const int t = sorted[row] / k;
-          const float sxv = act_scale[t];
-          const int f0 = p * 16 + ch0;
-          const float *sg = wscale + (size_t)e * 2 * F + f0;
+          const float sxv = a.act_scale[a.sorted[row] / a.k];
+          const int f0 = (u0 + q) * 16 + ch0;
+          const float *sg = a.wscale + (size_t)e * 2 * F + f0;
           const float *su = sg + F;
           v4f hv;
 #pragma unroll
@@ -116,56 +156,61 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
             hv[i] = gv / (1.0f + expf(-gv)) * uv;
             hmax = __builtin_fmaxf(hmax, __builtin_fabsf(hv[i]));
           }
-          *reinterpret_cast<v4f *>(out + (size_t)row * F + f0) = hv;
-          if (acc1_dbg) {
-            *reinterpret_cast<v4i *>(acc1_dbg + (size_t)row * 2 * F + f0) = g;
-            *reinterpret_cast<v4i *>(acc1_dbg + (size_t)row * 2 * F + F + f0) = u;
+          *reinterpret_cast<v4f *>(a.out + (size_t)row * F + f0) = hv;
+          if (a.acc1_dbg) {
+            *reinterpret_cast<v4i *>(a.acc1_dbg + (size_t)row * 2 * F + f0) = g;
+            *reinterpret_cast<v4i *>(a.acc1_dbg + (size_t)row * 2 * F + F + f0) = u;
           }
         }
         hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, 16, 64));
         hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, 32, 64));
-        if (valid && lane < 16) atomicMax(amax + row0 + r, __float_as_uint(hmax));
+        if (valid && lane < 16) atomicMax(a.amax + row, __float_as_uint(hmax));
       } else {
-        v4i s = red[0][pg * kRT + rt][lane];
-#pragma unroll
-        for (int wv = 1; wv < 4; ++wv) s += red[wv][pg * kRT + rt][lane];
+        const v4i sacc = total(q);
         if (valid) {
-          const int row = row0 + r;
-          const float shv = act_scale[row];
-          const int n0 = (p * NP + pg) * 16 + ch0;
-          const float *sd = wscale + (size_t)e * H + n0;
+          const float shv = a.act_scale[row];
+          const int n0 = (u0 + q) * 16 + ch0;
+          const float *sd = a.wscale + (size_t)e * H + n0;
           v4f yv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yv[i] = (float)s[i] * shv * sd[i];
-          *reinterpret_cast<v4f *>(out + (size_t)row * H + n0) = yv;
+          for (int i = 0; i < 4; ++i) yv[i] = (float)sacc[i] * shv * sd[i];
+          *reinterpret_cast<v4f *>(a.out + (size_t)row * H + n0) = yv;
         }
       }
     }
-    __syncthreads();
+    if (KS > 1) __syncthreads();
   }
 }
 
-constexpr int kDownPanels = 4;
+// Shapes chosen by timing the decode step (hidden 4096, FFN 1536, 64
+// experts, ~4 rows each) on MI355X: GEMM1 streams 2 gate + 2 up panels per
+// block (256 KB), GEMM2 2 panels (48 KB); both split K over the 4 waves.
+constexpr int kNpwGateUp = 2, kKsGateUp = 4, kUGateUp = 2;
+constexpr int kNpwDown = 2, kKsDown = 4, kUDown = 4;
 
 }  // namespace
 
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *counts, const int32_t *offsets, const int8_t *w_gu,
                                const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                               int32_t *acc1_dbg, hipStream_t st) {
-  dim3 grid((unsigned)(F / 16), (unsigned)E);
-  gemm_stream_kernel<true, 1><<<grid, dim3(256), 0, st>>>(qx, sx, sorted, k, counts, offsets, w_gu,
-                                                          s_gu, H, F, H, h, amax, acc1_dbg);
-  return hipGetLastError();
+                               int32_t *acc1_dbg, hipStream_t st, Timing tm) {
+  StreamArgs a{};
+  a.act = qx; a.act_scale = sx; a.sorted = sorted; a.k = k; a.counts = counts;
+  a.offsets = offsets; a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H;
+  a.out = h; a.amax = amax; a.acc1_dbg = acc1_dbg;
+  const dim3 grid((unsigned)(F / (16 * (4 / kKsGateUp) * kNpwGateUp)), (unsigned)E);
+  return launch_kernel(gemm_stream_kernel<true, kNpwGateUp, kKsGateUp, kUGateUp>, grid, dim3(256), st, tm,
+                       a);
 }
 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *offsets, const int8_t *w_d, const float *s_d, int H,
-                               int F, int E, float *y, hipStream_t st) {
-  dim3 grid((unsigned)(H / (16 * kDownPanels)), (unsigned)E);
-  gemm_stream_kernel<false, kDownPanels><<<grid, dim3(256), 0, st>>>(
-      qh, sh, nullptr, 1, counts, offsets, w_d, s_d, F, F, H, y, nullptr, nullptr);
-  return hipGetLastError();
+                               int F, int E, float *y, hipStream_t st, Timing tm) {
+  StreamArgs a{};
+  a.act = qh; a.act_scale = sh; a.k = 1; a.counts = counts; a.offsets = offsets; a.w = w_d;
+  a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
+  const dim3 grid((unsigned)(H / (16 * (4 / kKsDown) * kNpwDown)), (unsigned)E);
+  return launch_kernel(gemm_stream_kernel<false, kNpwDown, kKsDown, kUDown>, grid, dim3(256), st, tm, a);
 }
 
 }  // namespace moe

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(
     const int32_t *__restrict__ sorted, int k, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ mtile_off, int E,
     const int8_t *__restrict__ w, const float *__restrict__ wscale, int K, int F, int H,
-    float *__restrict__ out, uint32_t *__restrict__ amax, int32_t *__restrict__ acc1_dbg) {
+    void *__restrict__ out_v, uint32_t *__restrict__ amax, int32_t *__restrict__ acc1_dbg) {
   __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * BK];
   __shared__ float row_scale[BM];
   __shared__ int32_t row_tok[BM];
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(
           const float g = (float)acc[rt][0][i] * sxv * sg;
           const float u = (float)acc[rt][1][i] * sxv * su;
           hv = g / (1.0f + expf(-g)) * u;
-          out[(size_t)row * F + f] = hv;
+          static_cast<float *>(out_v)[(size_t)row * F + f] = hv;
           if (acc1_dbg) {
             acc1_dbg[(size_t)row * 2 * F + f] = acc[rt][0][i];
             acc1_dbg[(size_t)row * 2 * F + F + f] = acc[rt][1][i];
@@ -213,7 +213,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(
           const int m = rt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
           if (m0 + m < R) {
             const int row = row0 + m0 + m;
-            out[(size_t)row * H + n] = (float)acc[rt][ct][i] * row_scale[m] * sd;
+            static_cast<float *>(out_v)[(size_t)row * H + n] =
+                (float)acc[rt][ct][i] * row_scale[m] * sd;
           }
         }
       }
@@ -227,25 +228,22 @@ hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *
                               const int32_t *counts, const int32_t *offsets,
                               const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st) {
+                              int32_t *acc1_dbg, hipStream_t st, Timing tm) {
   const int64_t mtiles = (A + BM - 1) / BM + E;
-  dim3 grid((unsigned)mtiles, (unsigned)(F / 128));
-  gemm_tiled_kernel<true><<<grid, dim3(256), 0, st>>>(qx, sx, sorted, k, counts, offsets,
-                                                      mtile_off, E, w_gu, s_gu, H, F, H, h, amax,
-                                                      acc1_dbg);
-  return hipGetLastError();
+  const dim3 grid((unsigned)mtiles, (unsigned)(F / 128));
+  return launch_kernel(gemm_tiled_kernel<true>, grid, dim3(256), st, tm, qx, sx, sorted, k, counts,
+                       offsets, mtile_off, E, w_gu, s_gu, H, F, H, (void *)h, amax, acc1_dbg);
 }
 
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
-                              hipStream_t st) {
+                              const int8_t *w_d, const float *s_d, int H, int F, int E,
+                              float *y, hipStream_t st, Timing tm) {
   const int64_t mtiles = (A + BM - 1) / BM + E;
-  dim3 grid((unsigned)mtiles, (unsigned)(H / 256));
-  gemm_tiled_kernel<false><<<grid, dim3(256), 0, st>>>(qh, sh, nullptr, 1, counts, offsets,
-                                                       mtile_off, E, w_d, s_d, F, F, H, y, nullptr,
-                                                       nullptr);
-  return hipGetLastError();
+  const dim3 grid((unsigned)mtiles, (unsigned)(H / 256));
+  return launch_kernel(gemm_tiled_kernel<false>, grid, dim3(256), st, tm, qh, sh,
+                       (const int32_t *)nullptr, 1, counts, offsets, mtile_off, E, w_d, s_d, F, F,
+                       H, (void *)y, (uint32_t *)nullptr, (int32_t *)nullptr);
 }
 
 }  // namespace moe

@@ -1,0 +1,213 @@
+// layer_device.h -- device building blocks of the layer shared by more than
+// one kernel: the per-token router, the per-row INT8 quantisers and the
+// gate-weighted combine of one token. Included by the HIP sources only.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ routing
+// "超大规模模型推理的Day0适配实践" §四: the fused MoE operator's top-k must equal
+// the reference exactly, tie-break included; ties go to the lower expert
+// index. An expert is ranked by a 64-bit key: the upper half orders the
+// logit (IEEE order, with -0.0 and +0.0 equal because the value is
+// canonicalised by adding +0.0), the lower half is ~index so that the lower
+// index wins a tie. A NaN logit gets the lowest order and is only chosen
+// when nothing else is left; every valid expert's key is > 0, so 0 marks
+// "taken" or "no expert".
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t o = 0u;
+  if (v == v) {
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, 64);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    v = u > v ? u : v;
+  }
+  return v;
+}
+
+// One wavefront routes one token: experts lane + 64*i (i < NV) are held by
+// the lane, k rounds of a wave-wide key maximum pick the top k in order.
+// Softmax weights renormalised over the chosen k: exp(l_j - l_0) / sum.
+// Lane j < k returns slot j's expert and weight; other lanes return -1.
+template <int NV>
+__device__ __forceinline__ int route_token_wave(const float *__restrict__ row, int E, int k,
+                                                float *w_out) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(row[e], e) : 0ull;
+  }
+  uint64_t mine = 0ull;
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = key[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) b = key[i] > b ? key[i] : b;
+    b = wave_max_u64(b);
+    const int e = key_expert(b);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (lane + 64 * i == e) key[i] = 0ull;
+    if (lane == j) mine = b;
+  }
+  const float l = key_logit(mine);
+  const float m = __shfl(l, 0, 64);
+  const float ex = lane < k ? expf(l - m) : 0.0f;
+  const float den = wave_sum(ex);
+  *w_out = ex / den;
+  return lane < k ? key_expert(mine) : -1;
+}
+
+// ------------------------------------------------------------ quantisation
+// "MiniMax-M3 W8A8 inference on K100AI" §3.2/§6.4: per-token symmetric INT8
+// after the SmoothQuant rescaling. amax = max |x_j * inv_s_j|,
+// code = rint(fl32(v * fl32(127/amax))) clamped to [-127, 127], scale =
+// amax/127; an all-zero row gets scale 0 and codes 0.
+// One wavefront per row; the row (H bf16) is read once, 16 bytes per lane
+// per chunk, and kept in registers between the max and the code pass while
+// it fits (H <= 64 * 8 * MAXC), re-read otherwise.
+template <int MAXC>
+__device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
+                                                const float *__restrict__ inv_s, int H,
+                                                int8_t *__restrict__ qr, float *__restrict__ sx) {
+  const int lane = threadIdx.x & 63;
+  const int nchunk = H >> 3;
+  const bool cached = nchunk <= 64 * MAXC;
+  v4i raw[MAXC];
+  float amax = 0.0f;
+  auto scale8 = [&](v4i r, int c, float *o) {
+    const v4f s0 = *reinterpret_cast<const v4f *>(inv_s + c * 8);
+    const v4f s1 = *reinterpret_cast<const v4f *>(inv_s + c * 8 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = (uint32_t)r[i];
+      const float slo = i < 2 ? s0[2 * i] : s1[2 * i - 4];
+      const float shi = i < 2 ? s0[2 * i + 1] : s1[2 * i - 3];
+      o[2 * i] = __uint_as_float(w << 16) * slo;
+      o[2 * i + 1] = __uint_as_float(w & 0xffff0000u) * shi;
+    }
+  };
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      raw[i] = c < nchunk ? *reinterpret_cast<const v4i *>(xr + c * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) {
+        float v[8];
+        scale8(raw[i], c, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+      }
+    }
+  } else {
+    for (int c = lane; c < nchunk; c += 64) {
+      float v[8];
+      scale8(*reinterpret_cast<const v4i *>(xr + c * 8), c, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) *sx = amax / 127.0f;
+  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  auto emit = [&](v4i r, int c) {
+    float v[8];
+    scale8(r, c, v);
+    uint32_t p0 = 0u, p1 = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p0 |= (uint32_t)(q8(v[j], rr) & 0xff) << (8 * j);
+      p1 |= (uint32_t)(q8(v[4 + j], rr) & 0xff) << (8 * j);
+    }
+    *reinterpret_cast<uint2 *>(qr + c * 8) = make_uint2(p0, p1);
+  };
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nchunk) emit(raw[i], c);
+    }
+  } else {
+    for (int c = lane; c < nchunk; c += 64) emit(*reinterpret_cast<const v4i *>(xr + c * 8), c);
+  }
+}
+
+// Requantisation of one SwiGLU row h[0..F) whose max |h| is known (the same
+// rule as above, "MiniMax-M3 W8A8 inference on K100AI" §4.3: the two matmuls
+// stay in INT8). One wavefront per row, 16-byte loads, 4-byte stores.
+__device__ __forceinline__ void requant_row(const float *__restrict__ hr, float amax, int F,
+                                            int8_t *__restrict__ qr, float *__restrict__ sh) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) *sh = amax / 127.0f;
+  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const int n4 = F >> 2;
+#pragma unroll 4
+  for (int c = lane; c < n4; c += 64) {
+    const v4f v = *reinterpret_cast<const v4f *>(hr + c * 4);
+    const uint32_t p = (uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
+                       ((uint32_t)(q8(v[2], rr) & 0xff) << 16) |
+                       ((uint32_t)(q8(v[3], rr) & 0xff) << 24);
+    *reinterpret_cast<uint32_t *>(qr + c * 4) = p;
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum. Eight
+// consecutive outputs n0..n0+7 of token t:
+//   out[t][n] = bf16( sum over slots j < k with row_of[t*k+j] >= 0 of
+//                     w[t][j] * y[row][n] )
+// summed in fp32 in slot order (independent of scheduling), bf16 with ties
+// to even. y is fp32 [rows][H]: its only rounding is the final one to
+// bfloat16. Dropped slots add nothing; the remaining weights are not
+// renormalised.
+__device__ __forceinline__ void combine8(const float *__restrict__ y,
+                                         const float *__restrict__ wts,
+                                         const int32_t *__restrict__ row_of, int64_t t, int H,
+                                         int k, int n0, uint16_t *__restrict__ out) {
+  v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = row_of[t * k + j];
+    if (r < 0) continue;
+    const float w = wts[t * k + j];
+    const float *yr = y + (int64_t)r * H + n0;
+    const v4f v0 = *reinterpret_cast<const v4f *>(yr);
+    const v4f v1 = *reinterpret_cast<const v4f *>(yr + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc0[i] += w * v0[i];
+      acc1[i] += w * v1[i];
+    }
+  }
+  v4i o;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    o[i] = (int)((uint32_t)f32_to_bf16(acc0[2 * i]) | ((uint32_t)f32_to_bf16(acc0[2 * i + 1]) << 16));
+    o[2 + i] =
+        (int)((uint32_t)f32_to_bf16(acc1[2 * i]) | ((uint32_t)f32_to_bf16(acc1[2 * i + 1]) << 16));
+  }
+  *reinterpret_cast<v4i *>(out + t * H + n0) = o;
+}
+
+}  // namespace moe

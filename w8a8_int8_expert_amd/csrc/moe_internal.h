@@ -3,6 +3,7 @@
 // Not part of the public ABI (include/moe_w8a8.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -22,6 +23,9 @@ constexpr int kTiledBN = 256;
 // Maximum experts (LDS histograms are sized for it).
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
+// Up to this many assignments (T*k) the routing, grouping and activation
+// quantisation run as one fused launch (one block does the grouping).
+constexpr int kSmallA = 2048;
 
 // ------------------------------------------------------------ device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
@@ -65,6 +69,23 @@ __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
 }
 #endif
 
+// ------------------------------------------------------------------ launches
+// Optional timing of one launch: the events are stamped by the kernel's own
+// dispatch (hipExtLaunchKernel: start and end of its execution), so timing a
+// stage adds no marker packet, and no gap, between the layer's kernels.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                                Timing tm, Args... args) {
+  if (tm.start || tm.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- workspace
 // Regions of the forward workspace (byte offsets from its base).
 struct FwdLayout {
@@ -77,37 +98,45 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k);
 size_t calib_ws_bytes(int H);
 
 // ----------------------------------------------------------------- launchers
-// Each returns hipGetLastError() after enqueueing on `st`.
+// Each returns hipGetLastError() after enqueueing on `st` (timed by `tm`).
+// Fused small-batch prologue: route (or copy pre-routed ids), group, clear
+// the per-row max buffer (A words), and quantise the activations.
+hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
+                                 int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
+                                 int32_t *counts, int32_t *offsets, int32_t *mtile_off,
+                                 int32_t *sorted, int32_t *row_of, const uint16_t *x,
+                                 const float *inv_s, int H, int8_t *qx, float *sx, uint32_t *amax,
+                                 hipStream_t st, Timing tm);
 hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
-                             int32_t *blk_hist, uint32_t *amax, hipStream_t st);
+                             int32_t *blk_hist, uint32_t *amax, hipStream_t st, Timing tm);
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
-                       int32_t *offsets, int32_t *mtile_off, hipStream_t st);
+                       int32_t *offsets, int32_t *mtile_off, hipStream_t st, Timing tm);
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
-                          int32_t *row_of, hipStream_t st);
+                          int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
-                            float *sx, hipStream_t st);
+                            float *sx, hipStream_t st, Timing tm);
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *offsets, int E,
-                          int64_t A, int F, int8_t *qh, float *sh, hipStream_t st);
+                          int64_t A, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm);
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *counts, const int32_t *offsets, const int8_t *w_gu,
                                const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                               int32_t *acc1_dbg, hipStream_t st);
+                               int32_t *acc1_dbg, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *offsets, const int8_t *w_d, const float *s_d, int H,
-                               int F, int E, float *y, hipStream_t st);
+                               int F, int E, float *y, hipStream_t st, Timing tm);
 hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                               const int32_t *counts, const int32_t *offsets,
                               const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st);
+                              int32_t *acc1_dbg, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
-                              hipStream_t st);
+                              const int8_t *w_d, const float *s_d, int H, int F, int E,
+                              float *y, hipStream_t st, Timing tm);
 hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
-                          int H, int k, uint16_t *out, hipStream_t st);
+                          int H, int k, uint16_t *out, hipStream_t st, Timing tm);
 // calibrate
 hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const float *w_gate,
                                const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,

@@ -8,98 +8,46 @@
 // order inside an expert group is (token, slot) and the capacity rule of the
 // same page (§二.2, capacity factor; overflow dropped) keeps the first C.
 //
-// Three launches:
-//   route_hist  one block per 64 tokens: route (or copy pre-routed ids),
-//               per-block expert histogram in LDS, clear the row max buffer;
-//   scan        one block: per-expert exclusive scan over blocks, capacity,
-//               expert offsets and the M-tile table of the tiled GEMMs;
-//   scatter     one block per 64 tokens: stable ranks from wave ballots,
-//               writes sorted[] and row_of[].
-#include "moe_internal.h"
+// Two ways through, chosen by the number of assignments A = T*k:
+//  small A (a decode step): ONE launch, prologue_small_kernel. Block 0 routes
+//      every token (one wavefront per token), histograms in LDS, scans, and
+//      scatters stably with one wavefront's ballots; blocks 1.. quantise the
+//      activations (one wavefront per token) at the same time.
+//  large A (prefill): route_hist (one block per 64 tokens: route, per-block
+//      LDS histogram) -> scan (one block: per-expert scan over blocks,
+//      capacity, offsets, M-tile table) -> scatter (one block per 64 tokens:
+//      stable ranks from wave ballots); activation quantisation is its own
+//      launch (quant.hip).
+// Both clear the per-row max buffer that GEMM1 fills later in the call.
+#include "layer_device.h"
 
 namespace moe {
 namespace {
 
-// (value, index) ordering of the router: higher logit first, then lower
-// index. Comparisons are IEEE (so -0.0 ties +0.0). idx == INT32_MAX marks
-// "no candidate"; a NaN never beats a candidate, so the winner is always a
-// valid untaken expert.
-__device__ __forceinline__ bool route_better(float av, int ai, float bv, int bi) {
-  if (ai == INT32_MAX) return false;
-  if (bi == INT32_MAX) return true;
-  return av > bv || (av == bv && ai < bi);
+// Stable rank of each lane's expert among the lanes before it with the same
+// expert (ballots over the id bits); -1 ids never match a valid one.
+__device__ __forceinline__ void ballot_rank(int e, bool valid, int nbits, int *rank, int *cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t mask = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t bal = __ballot(bit);
+    mask &= bit ? bal : ~bal;
+  }
+  *rank = __popcll(mask & lt_mask);
+  *cnt = __popcll(mask);
 }
 
-__global__ __launch_bounds__(256) void route_hist_kernel(
-    const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
-    const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax) {
-  __shared__ int32_t hist[kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += 256) hist[e] = 0;
-  // Clear the per-row max of this block's share of permuted rows (rows are
-  // < T*k; block b owns [b*64*k, (b+1)*64*k)).
-  {
-    const int64_t A = T * (int64_t)k;
-    const int64_t r0 = (int64_t)blockIdx.x * kRouteTokens * k;
-    const int64_t r1 = r0 + (int64_t)kRouteTokens * k < A ? r0 + (int64_t)kRouteTokens * k : A;
-    for (int64_t r = r0 + tid; r < r1; r += 256) amax[r] = 0u;
-  }
-  __syncthreads();
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
-  for (int tt = wave; tt < kRouteTokens; tt += 4) {
-    const int64_t t = t0 + tt;
-    if (t >= T) break;
-    if (logits == nullptr) {
-      if (lane < k) {
-        const int32_t e = ids_in[t * k + lane];
-        ids[t * k + lane] = e;
-        wts[t * k + lane] = w_in[t * k + lane];
-        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-      }
-      continue;
-    }
-    // Lane holds experts lane, lane+64, ...; `taken` marks chosen ones.
-    float v[kMaxExperts / 64];
-    uint32_t taken = 0;
-    const float *row = logits + t * E;
-#pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) v[i] = row[e];
-      else { v[i] = 0.0f; taken |= 1u << i; }
-    }
-    float my_logit = 0.0f;
-    int my_id = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = 0.0f;
-      int bi = INT32_MAX;
-#pragma unroll
-      for (int i = 0; i < kMaxExperts / 64; ++i) {
-        if (taken & (1u << i)) continue;
-        if (route_better(v[i], lane + 64 * i, bv, bi)) { bv = v[i]; bi = lane + 64 * i; }
-      }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (route_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == j) { my_logit = bv; my_id = bi; }
-    }
-    // Renormalised softmax over the chosen k: exp(l_j - l_0) / sum.
-    const float m = __shfl(my_logit, 0, 64);
-    const float ex = lane < k ? expf(my_logit - m) : 0.0f;
-    const float den = wave_sum(ex);
-    if (lane < k) {
-      ids[t * k + lane] = my_id;
-      wts[t * k + lane] = ex / den;
-      atomicAdd(&hist[my_id], 1);
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) blk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
+__device__ __forceinline__ int id_bits(int E) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  return nbits;
+}
+
+// Clear n int32 words starting at p with the threads of this block.
+__device__ __forceinline__ void block_clear(uint32_t *p, int64_t n) {
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 // Inclusive wave scan of ints (64 lanes).
@@ -113,6 +61,159 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Block-wide exclusive scan of one int per thread (blockDim.x == 1024);
+// returns the exclusive prefix, *total gets the sum. Uses wsum[16].
+__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) base += wsum[w];
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+// Kept counts per expert from the totals: capacity, offsets, counts and the
+// M-tile table of the tiled GEMMs. One thread per expert (E <= 1024, 1024
+// threads). Returns this thread's expert offset (0 past E).
+__device__ __forceinline__ int finish_counts(int total, int E, int64_t capacity,
+                                             int32_t *__restrict__ counts,
+                                             int32_t *__restrict__ offsets,
+                                             int32_t *__restrict__ mtile_off, int *wsum) {
+  const int tid = threadIdx.x;
+  int kept = 0, tiles = 0;
+  if (tid < E) {
+    kept = total;
+    if (capacity > 0 && (int64_t)kept > capacity) kept = (int)capacity;
+    tiles = (kept + kTiledBM - 1) / kTiledBM;
+    counts[tid] = kept;
+  }
+  int all;
+  const int off = block_excl_scan(kept, wsum, &all);
+  if (tid < E) offsets[tid] = off;
+  if (tid == 0) offsets[E] = all;
+  const int toff = block_excl_scan(tiles, wsum, &all);
+  if (tid < E) mtile_off[tid] = toff;
+  if (tid == 0) mtile_off[E] = all;
+  return off;
+}
+
+// ------------------------------------------------------------- small A path
+template <int NV>
+__global__ __launch_bounds__(1024) void prologue_small_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
+    const float *__restrict__ w_in, int T, int E, int k, int64_t capacity,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, const uint16_t *__restrict__ x,
+    const float *__restrict__ inv_s, int H, int8_t *__restrict__ qx, float *__restrict__ sx,
+    uint32_t *__restrict__ amax) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x > 0) {
+    const int64_t t = (int64_t)(blockIdx.x - 1) * 16 + wave;
+    if (t < T) quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t);
+    return;
+  }
+  __shared__ int32_t hist[kMaxExperts];
+  __shared__ int32_t run[kMaxExperts];
+  __shared__ int32_t lds_ids[kSmallA];
+  __shared__ int32_t lds_off[kMaxExperts];
+  __shared__ int wsum[16];
+  const int A = T * k;
+  for (int e = tid; e < E; e += 1024) { hist[e] = 0; run[e] = 0; }
+  block_clear(amax, A);
+  __syncthreads();
+  for (int t = wave; t < T; t += 16) {
+    int e;
+    float w;
+    if (logits) {
+      e = route_token_wave<NV>(logits + (int64_t)t * E, E, k, &w);
+    } else {
+      e = lane < k ? ids_in[t * k + lane] : -1;
+      w = lane < k ? w_in[t * k + lane] : 0.0f;
+    }
+    if (lane < k) {
+      ids[t * k + lane] = e;
+      wts[t * k + lane] = w;
+      lds_ids[t * k + lane] = e;
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  const int off = finish_counts(tid < E ? hist[tid] : 0, E, capacity, counts, offsets, mtile_off,
+                                wsum);
+  if (tid < E) lds_off[tid] = off;
+  __syncthreads();
+  if (wave != 0) return;
+  const int nbits = id_bits(E);
+  for (int base = 0; base < A; base += 64) {
+    const int a = base + lane;
+    int e = a < A ? lds_ids[a] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = -1;
+    int rank, cnt;
+    ballot_rank(e, valid, nbits, &rank, &cnt);
+    if (a < A) {
+      int32_t row = -1;
+      if (valid) {
+        const int r = run[e] + rank;
+        if (capacity <= 0 || (int64_t)r < capacity) {
+          row = lds_off[e] + r;
+          sorted[row] = a;
+        }
+      }
+      row_of[a] = row;
+    }
+    // Every lane has read run[] above before the group's last lane adds the
+    // group size: one wavefront's LDS accesses complete in issue order.
+    if (valid && rank == cnt - 1) run[e] += cnt;
+  }
+}
+
+// ------------------------------------------------------------- large A path
+template <int NV>
+__global__ __launch_bounds__(1024) void route_hist_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
+    const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
+    float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax) {
+  __shared__ int32_t hist[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 1024) hist[e] = 0;
+  // This block's share of the per-row max buffer: rows [b*64*k, (b+1)*64*k).
+  {
+    const int64_t A = T * (int64_t)k;
+    const int64_t r0 = (int64_t)blockIdx.x * kRouteTokens * k;
+    const int64_t r1 = r0 + (int64_t)kRouteTokens * k < A ? r0 + (int64_t)kRouteTokens * k : A;
+    for (int64_t r = r0 + tid; r < r1; r += 1024) amax[r] = 0u;
+  }
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
+  for (int tt = wave; tt < kRouteTokens; tt += 16) {
+    const int64_t t = t0 + tt;
+    if (t >= T) break;
+    int e;
+    float w;
+    if (logits) {
+      e = route_token_wave<NV>(logits + t * E, E, k, &w);
+    } else {
+      e = lane < k ? ids_in[t * k + lane] : -1;
+      w = lane < k ? w_in[t * k + lane] : 0.0f;
+    }
+    if (lane < k) {
+      ids[t * k + lane] = e;
+      wts[t * k + lane] = w;
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) blk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
 // One block of 1024 threads. Wave w scans the block histograms of experts
 // w, w+16, ...: blk_hist[b][e] becomes the number of assignments to e in
 // blocks before b. Then capacity, offsets and the M-tile table.
@@ -122,7 +223,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
                                                     int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ mtile_off) {
   __shared__ int32_t total[kMaxExperts];
-  __shared__ int32_t wsum[16];
+  __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t per_lane = (nblk + 63) / 64;
   for (int e = wave; e < E; e += 16) {
@@ -131,37 +232,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
     int s = 0;
     for (int64_t b = b0; b < b1; ++b) s += blk_hist[b * E + e];
     const int incl = wave_incl_scan(s);
-    int run = incl - s;  // exclusive prefix of this lane's first block
+    int r = incl - s;  // exclusive prefix of this lane's first block
     for (int64_t b = b0; b < b1; ++b) {
       const int c = blk_hist[b * E + e];
-      blk_hist[b * E + e] = run;
-      run += c;
+      blk_hist[b * E + e] = r;
+      r += c;
     }
     if (lane == 63) total[e] = incl;
   }
   __syncthreads();
-  // Kept counts and their exclusive scans (E <= 1024 = one per thread).
-  int kept = 0, tiles = 0;
-  if (tid < E) {
-    kept = total[tid];
-    if (capacity > 0 && (int64_t)kept > capacity) kept = (int)capacity;
-    tiles = (kept + kTiledBM - 1) / kTiledBM;
-    counts[tid] = kept;
-  }
-  // Block-wide exclusive scans of the kept counts (-> offsets) and of the
-  // M tiles per expert (-> mtile_off), one after the other.
-  for (int pass = 0; pass < 2; ++pass) {
-    const int v = pass == 0 ? kept : tiles;
-    const int incl = wave_incl_scan(v);
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    int32_t *dst = pass == 0 ? offsets : mtile_off;
-    if (tid < E) dst[tid] = base + incl - v;
-    if (tid == E - 1) dst[E] = base + incl;
-    __syncthreads();
-  }
+  finish_counts(tid < E ? total[tid] : 0, E, capacity, counts, offsets, mtile_off, wsum);
 }
 
 // Stable scatter. Assignments of this block are processed in rounds of 256
@@ -174,7 +254,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     int32_t *__restrict__ sorted, int32_t *__restrict__ row_of) {
   __shared__ int32_t running[kMaxExperts];
   __shared__ int32_t wcnt[4][kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int e = tid; e < E; e += 256) {
     running[e] = blk_base[(int64_t)blockIdx.x * E + e];
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
@@ -183,9 +263,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   const int64_t A = T * (int64_t)k;
   const int64_t a0 = (int64_t)blockIdx.x * kRouteTokens * k;
   const int64_t a1 = a0 + (int64_t)kRouteTokens * k < A ? a0 + (int64_t)kRouteTokens * k : A;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nbits = id_bits(E);
   for (int64_t base = a0; base < a1; base += 256) {
     const int64_t a = base + tid;
     int e = -1;
@@ -194,14 +272,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
       if (e < 0 || e >= E) e = -1;
     }
     const bool valid = e >= 0;
-    uint64_t mask = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bal = __ballot(bit);
-      mask &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(mask & lt_mask);
-    const int cnt = __popcll(mask);
+    int rank, cnt;
+    ballot_rank(e, valid, nbits, &rank, &cnt);
     const bool leader = valid && (rank == cnt - 1);
     if (leader) wcnt[wave][e] = cnt;
     __syncthreads();
@@ -226,31 +298,66 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   }
 }
 
+// Experts held per lane by the router: the smallest of 1, 2, 4, 8, 16 with
+// 64 * NV >= E.
+int route_nv(int E) {
+  int nv = 1;
+  while (64 * nv < E) nv *= 2;
+  return nv;
+}
+
 }  // namespace
+
+hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
+                                 int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
+                                 int32_t *counts, int32_t *offsets, int32_t *mtile_off,
+                                 int32_t *sorted, int32_t *row_of, const uint16_t *x,
+                                 const float *inv_s, int H, int8_t *qx, float *sx, uint32_t *amax,
+                                 hipStream_t st, Timing tm) {
+  const dim3 grid(1 + (unsigned)((T + 15) / 16)), block(1024);
+#define MOE_PROLOGUE(NV)                                                                     \
+  return launch_kernel(prologue_small_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, \
+                       E, k, capacity, ids, wts, counts, offsets, mtile_off, sorted, row_of, x, \
+                       inv_s, H, qx, sx, amax)
+  switch (route_nv(E)) {
+    case 1: MOE_PROLOGUE(1);
+    case 2: MOE_PROLOGUE(2);
+    case 4: MOE_PROLOGUE(4);
+    case 8: MOE_PROLOGUE(8);
+    default: MOE_PROLOGUE(16);
+  }
+#undef MOE_PROLOGUE
+}
 
 hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
-                             int32_t *blk_hist, uint32_t *amax, hipStream_t st) {
-  const int64_t nblk = (T + kRouteTokens - 1) / kRouteTokens;
-  route_hist_kernel<<<dim3((unsigned)nblk), dim3(256), 0, st>>>(logits, ids_in, w_in, T, E, k,
-                                                                 ids, wts, blk_hist, amax);
-  return hipGetLastError();
+                             int32_t *blk_hist, uint32_t *amax, hipStream_t st, Timing tm) {
+  const dim3 grid((unsigned)((T + kRouteTokens - 1) / kRouteTokens)), block(1024);
+#define MOE_ROUTE(NV)                                                                        \
+  return launch_kernel(route_hist_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, E, \
+                       k, ids, wts, blk_hist, amax)
+  switch (route_nv(E)) {
+    case 1: MOE_ROUTE(1);
+    case 2: MOE_ROUTE(2);
+    case 4: MOE_ROUTE(4);
+    case 8: MOE_ROUTE(8);
+    default: MOE_ROUTE(16);
+  }
+#undef MOE_ROUTE
 }
 
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
-                       int32_t *offsets, int32_t *mtile_off, hipStream_t st) {
-  scan_kernel<<<dim3(1), dim3(1024), 0, st>>>(blk_hist, nblk, E, capacity, counts, offsets,
-                                               mtile_off);
-  return hipGetLastError();
+                       int32_t *offsets, int32_t *mtile_off, hipStream_t st, Timing tm) {
+  return launch_kernel(scan_kernel, dim3(1), dim3(1024), st, tm, blk_hist, nblk, E, capacity,
+                       counts, offsets, mtile_off);
 }
 
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
-                          int32_t *row_of, hipStream_t st) {
+                          int32_t *row_of, hipStream_t st, Timing tm) {
   const int64_t nblk = (T + kRouteTokens - 1) / kRouteTokens;
-  scatter_kernel<<<dim3((unsigned)nblk), dim3(256), 0, st>>>(ids, blk_hist, offsets, T, E, k,
-                                                              capacity, sorted, row_of);
-  return hipGetLastError();
+  return launch_kernel(scatter_kernel, dim3((unsigned)nblk), dim3(256), st, tm, ids, blk_hist,
+                       offsets, T, E, k, capacity, sorted, row_of);
 }
 
 }  // namespace moe
