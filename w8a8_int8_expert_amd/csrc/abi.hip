@@ -30,6 +30,8 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   FwdLayout L{};
   const int64_t A = T * k;
   L.nblk = (T + kRouteTokens - 1) / kRouteTokens;
+  L.P = A + 15 * (A < E ? A : (int64_t)E);
+  const size_t P16 = (size_t)((L.P + 15) / 16) * 16;  // rows of the tiled operands
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
   L.ids = take(sizeof(int32_t) * A);
@@ -37,16 +39,18 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   L.blk_hist = take(sizeof(int32_t) * (size_t)L.nblk * E);
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
+  L.poffsets = take(sizeof(int32_t) * (E + 1));
   L.mtile_off = take(sizeof(int32_t) * (E + 1));
-  L.sorted = take(sizeof(int32_t) * A);
+  L.sorted = take(sizeof(int32_t) * (size_t)L.P);
   L.row_of = take(sizeof(int32_t) * A);
   L.qx = take((size_t)T * H);
   L.sx = take(sizeof(float) * T);
-  L.h = take(sizeof(float) * (size_t)A * F);
-  L.amax = take(sizeof(uint32_t) * (size_t)L.nblk * kRouteTokens * k);
-  L.qh = take((size_t)A * F);
-  L.sh = take(sizeof(float) * A);
-  L.y = take(sizeof(float) * (size_t)A * H);
+  L.a1 = take(P16 * H);
+  L.h = take(sizeof(float) * (size_t)L.P * F);
+  L.amax = take(sizeof(uint32_t) * (size_t)L.P);
+  L.qh = take(P16 * F);
+  L.sh = take(sizeof(float) * (size_t)L.P);
+  L.y = take(sizeof(float) * (size_t)L.P * H);
   L.total = o;
   return L;
 }
@@ -142,11 +146,13 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   int32_t *blk_hist = (int32_t *)(ws + L.blk_hist);
   int32_t *counts = (int32_t *)(ws + L.counts);
   int32_t *offsets = (int32_t *)(ws + L.offsets);
+  int32_t *poffsets = (int32_t *)(ws + L.poffsets);
   int32_t *mtile_off = (int32_t *)(ws + L.mtile_off);
   int32_t *sorted = (int32_t *)(ws + L.sorted);
   int32_t *row_of = (int32_t *)(ws + L.row_of);
   int8_t *qx = (int8_t *)(ws + L.qx);
   float *sx = (float *)(ws + L.sx);
+  int8_t *a1 = (int8_t *)(ws + L.a1);
   float *h = (float *)(ws + L.h);
   uint32_t *amax = (uint32_t *)(ws + L.amax);
   int8_t *qh = (int8_t *)(ws + L.qh);
@@ -159,13 +165,14 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
 
   // Stage events: pair s is stamped by the dispatch of the launch that
   // performs stage s; a launch that fuses several stages takes the pair of
-  // the first of them.
+  // the first of them, and a stage of two launches is timed from the start
+  // of the first to the end of the second.
   void **ev = dbg ? dbg->stage_events : nullptr;
-  auto tm = [&](int s) -> Timing {
+  auto tm = [&](int s, bool start = true, bool stop = true) -> Timing {
     Timing t;
     if (ev) {
-      t.start = (hipEvent_t)ev[2 * s];
-      t.stop = (hipEvent_t)ev[2 * s + 1];
+      if (start) t.start = (hipEvent_t)ev[2 * s];
+      if (stop) t.stop = (hipEvent_t)ev[2 * s + 1];
     }
     return t;
   };
@@ -173,30 +180,37 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
 
   if (small) {
     MOE_CHECK(launch_prologue_small(router_logits, topk_ids, topk_w, (int)T, E, k, capacity, ids,
-                                    wts, counts, offsets, mtile_off, sorted, row_of, x,
-                                    wt->inv_smooth, H, qx, sx, amax, st, tm(kRoute)));
+                                    wts, counts, offsets, poffsets, mtile_off, sorted, row_of,
+                                    (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, st,
+                                    tm(kRoute)));
   } else {
     MOE_CHECK(launch_route_hist(router_logits, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
-                                amax, st, tm(kRoute)));
-    MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, mtile_off, st,
+                                amax, sorted, L.P, st, tm(kRoute)));
+    MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, poffsets, mtile_off, st,
                           tm(kScan)));
-    MOE_CHECK(launch_scatter(ids, blk_hist, offsets, T, E, k, capacity, sorted, row_of, st,
+    MOE_CHECK(launch_scatter(ids, blk_hist, poffsets, T, E, k, capacity, sorted, row_of, st,
                              tm(kScatter)));
-    MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ)));
   }
-  if (path == 1)
-    MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, offsets, wt->w_gate_up,
+  if (path == 1) {
+    if (!small) MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ)));
+    MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, poffsets, offsets, wt->w_gate_up,
                                   wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
-  else
-    MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, offsets, mtile_off, A, wt->w_gate_up,
-                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
-  MOE_CHECK(launch_requant(h, amax, offsets, E, A, F, qh, sh, st, tm(kReq)));
+  } else {
+    if (!small)
+      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ, true, false)));
+    MOE_CHECK(launch_gather_tiles(qx, sorted, k, poffsets, E, L.P, H, a1, st,
+                                  tm(kActQ, small, true)));
+    MOE_CHECK(launch_gemm1_tiled(a1, sx, sorted, k, counts, poffsets, offsets, mtile_off, A,
+                                 wt->w_gate_up, wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st,
+                                 tm(kG1)));
+  }
+  MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, st, tm(kReq)));
   if (path == 1)
-    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, offsets, wt->w_down, wt->s_down, H, F, E, y, st,
-                                  tm(kG2)));
+    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, poffsets, wt->w_down, wt->s_down, H, F, E, y,
+                                  st, tm(kG2)));
   else
-    MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, offsets, mtile_off, A, wt->w_down, wt->s_down, H,
-                                 F, E, y, st, tm(kG2)));
+    MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, poffsets, mtile_off, A, wt->w_down, wt->s_down,
+                                 H, F, E, y, st, tm(kG2)));
   MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st, tm(kComb)));
 
   if (dbg) {
@@ -208,14 +222,13 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
     MOE_CHECK(cp(dbg->topk_w, wts, sizeof(float) * A));
     MOE_CHECK(cp(dbg->expert_counts, counts, sizeof(int32_t) * E));
     MOE_CHECK(cp(dbg->expert_offsets, offsets, sizeof(int32_t) * (E + 1)));
-    MOE_CHECK(cp(dbg->sorted_assign, sorted, sizeof(int32_t) * A));
-    MOE_CHECK(cp(dbg->row_of, row_of, sizeof(int32_t) * A));
     MOE_CHECK(cp(dbg->qx, qx, (size_t)T * H));
     MOE_CHECK(cp(dbg->sx, sx, sizeof(float) * T));
-    MOE_CHECK(cp(dbg->h, h, sizeof(float) * (size_t)A * F));
-    MOE_CHECK(cp(dbg->qh, qh, (size_t)A * F));
-    MOE_CHECK(cp(dbg->sh, sh, sizeof(float) * A));
-    MOE_CHECK(cp(dbg->y, y, sizeof(float) * (size_t)A * H));
+    if (dbg->sorted_assign || dbg->h || dbg->qh || dbg->sh || dbg->y)
+      MOE_CHECK(launch_debug_rows(offsets, poffsets, E, A, sorted, h, qh, sh, y, F, H,
+                                  dbg->sorted_assign, dbg->h, dbg->qh, dbg->sh, dbg->y, st));
+    if (dbg->row_of)
+      MOE_CHECK(launch_debug_row_of(row_of, ids, offsets, poffsets, A, dbg->row_of, st));
   }
   return MOE_W8A8_OK;
 }

@@ -32,17 +32,18 @@ namespace {
 constexpr int kRT = 2;  // row tiles of 16 held per pass (32 rows)
 
 struct StreamArgs {
-  const int8_t *act;        // GEMM1: qx [T][H]; GEMM2: qh [A][F]
-  const float *act_scale;   // GEMM1: sx [T];    GEMM2: sh [A]
+  const int8_t *act;        // GEMM1: qx [T][H] by token; GEMM2: qh fragment-tiled by row
+  const float *act_scale;   // GEMM1: sx [T];    GEMM2: sh [rows]
   const int32_t *sorted;    // GEMM1 only
   int k;
-  const int32_t *counts, *offsets;
+  const int32_t *counts, *offsets;  // offsets: padded (16-row aligned) group starts
+  const int32_t *dense_off;         // GEMM1: dense group starts (debug rows)
   const int8_t *w;          // fragment-tiled weights
   const float *wscale;
   int K, F, H;
   float *out;               // GEMM1: h [A][F]; GEMM2: y [A][H]
   uint32_t *amax;           // GEMM1 only
-  int32_t *acc1_dbg;        // GEMM1 only, may be NULL
+  int32_t *acc1_dbg;        // GEMM1 only, may be NULL; dense rows
 };
 
 template <bool kGateUp, int NPW, int KS, int U>
@@ -75,10 +76,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
     for (int rt = 0; rt < kRT; ++rt) {
       const int r = base + rt * 16 + (lane & 15);
       bv[rt] = r < R;
-      size_t arow = 0;
-      if (bv[rt]) arow = kGateUp ? (size_t)(a.sorted[row0 + r] / a.k) : (size_t)(row0 + r);
-      bp[rt] = a.act + arow * (size_t)K + (lane >> 4) * 16;
+      if (kGateUp) {
+        const size_t tok = bv[rt] ? (size_t)(a.sorted[row0 + r] / a.k) : 0;
+        bp[rt] = a.act + tok * (size_t)K + (lane >> 4) * 16;
+      } else {
+        // Row tile (row0 + base)/16 + rt of the tiled operand: lane l holds
+        // row l%16 of it, exactly the operand order below.
+        bp[rt] = a.act + frag_tile(((row0 + base) >> 4) + rt, 0, K) + lane * 16;
+      }
     }
+    const int astep = kGateUp ? 64 : 1024;  // bytes per k tile of the operand row
     v4i acc[NA][kRT];
 #pragma unroll
     for (int i = 0; i < NA; ++i)
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
         af[i] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(wp[i] + ((size_t)kt << 10)));
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
-        bf[rt] = bv[rt] ? *reinterpret_cast<const v4i *>(bp[rt] + kt * 64) : v4i{0, 0, 0, 0};
+        bf[rt] = bv[rt] ? *reinterpret_cast<const v4i *>(bp[rt] + (size_t)kt * astep)
+                        : v4i{0, 0, 0, 0};
     };
     auto mma = [&](const v4i *af, const v4i *bf) {
 #pragma unroll
@@ -158,8 +166,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
           }
           *reinterpret_cast<v4f *>(a.out + (size_t)row * F + f0) = hv;
           if (a.acc1_dbg) {
-            *reinterpret_cast<v4i *>(a.acc1_dbg + (size_t)row * 2 * F + f0) = g;
-            *reinterpret_cast<v4i *>(a.acc1_dbg + (size_t)row * 2 * F + F + f0) = u;
+            const size_t drow = (size_t)(a.dense_off[e] + r);
+            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + f0) = g;
+            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + F + f0) = u;
           }
         }
         hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, 16, 64));
@@ -191,12 +200,13 @@ constexpr int kNpwDown = 2, kKsDown = 4, kUDown = 4;
 }  // namespace
 
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
-                               const int32_t *counts, const int32_t *offsets, const int8_t *w_gu,
-                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                               int32_t *acc1_dbg, hipStream_t st, Timing tm) {
+                               const int32_t *counts, const int32_t *offsets,
+                               const int32_t *dense_off, const int8_t *w_gu, const float *s_gu,
+                               int H, int F, int E, float *h, uint32_t *amax, int32_t *acc1_dbg,
+                               hipStream_t st, Timing tm) {
   StreamArgs a{};
   a.act = qx; a.act_scale = sx; a.sorted = sorted; a.k = k; a.counts = counts;
-  a.offsets = offsets; a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H;
+  a.offsets = offsets; a.dense_off = dense_off; a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H;
   a.out = h; a.amax = amax; a.acc1_dbg = acc1_dbg;
   const dim3 grid((unsigned)(F / (16 * (4 / kKsGateUp) * kNpwGateUp)), (unsigned)E);
   return launch_kernel(gemm_stream_kernel<true, kNpwGateUp, kKsGateUp, kUGateUp>, grid, dim3(256), st, tm,

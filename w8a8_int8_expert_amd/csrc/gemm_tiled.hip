@@ -6,244 +6,322 @@
 // dequantised afterwards; "一晚上完成MoE模型推理优化…" §4.1: the activation
 // that follows a linear layer is fused into it (SwiGLU in GEMM1's epilogue).
 //
-// One block computes a 128-row x 256-column tile of one expert on
-// v_mfma_i32_32x32x32_i8:
-//   rows    = 128 consecutive permuted rows of the expert (the M tile);
-//   columns = GEMM1: 128 gate rows and the matching 128 up rows of the
-//             expert's [2F][H] weights (wave w owns gate/up columns
-//             f0+32w..f0+32w+31, so g and u of one h element meet in the
-//             same lane); GEMM2: 256 output channels (64 per wave).
-// Activations (GEMM1: gathered rows of qx; GEMM2: contiguous rows of qh) are
-// staged through LDS, double buffered, in an XOR-swizzled layout that makes
-// the 16-byte fragment reads conflict free. Weight fragments come straight
-// from the fragment-tiled layout into registers (each wave owns its columns,
-// so they are not shared and need no LDS).
-// M tiles of all experts are numbered consecutively (mtile_off, written by
-// the scan kernel); blocks past the last tile exit at once. Blocks are
-// renumbered so that each XCD (one L2) works on a contiguous range of tiles.
-#include "moe_internal.h"
+// One block (8 wavefronts, two per SIMD) computes a 256-row x 256-column
+// tile of one expert:
+//   rows    = 256 consecutive permuted rows of the expert (the M tile);
+//   columns = GEMM1: 128 gate channels and the same 128 up channels of the
+//             expert's [2F][H] weights; GEMM2: 256 output channels.
+// Both operands are stored fragment-tiled (16 rows x 64 k per 1 KB, the lane
+// order of the INT8 matrix instructions): the weights by calibration, the
+// activations by the kernel that produces them (expert groups start on a
+// 16-row boundary). K advances 64 at a time through a 4-stage ring of 32 KB
+// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4: a
+// wavefront moves one contiguous 1 KB tile per instruction, lane l's 16
+// bytes landing at byte 16*l), issued three stages ahead of use. Reading a
+// 32x32x32 operand from such a tile is a conflict-free ds_read_b128.
+// A 256x256 tile moves 2 bytes per 256 int8 operations, which is what keeps
+// the loads under the matrix time: the L2 -> LDS path sustains about 27
+// bytes per clock per CU, the INT8 matrix cores 8192 operations.
+// Wavefront (wm, wn) owns rows 128*wm.. and, for GEMM1, 32 gate + the
+// matching 32 up columns (so g and u of one h element meet in one lane); it
+// accumulates a 128x64 INT32 tile in 8 v_mfma_i32_32x32x32_i8 accumulators.
+// The epilogue goes through the wavefront's own slice of the (then free)
+// stage buffers so that every global store writes 16 bytes per lane along a
+// row.
+//
+// Tiles of all experts are numbered (N group, M tile, N tile in group): the
+// blocks that run together share a few weight panels and reuse each
+// activation tile across the group. Block ids are renumbered so that each
+// XCD (one L2) takes a contiguous range of that order. M tiles past the last
+// expert's exit at once (the grid is sized by an upper bound).
+#include "layer_device.h"
+
+// The direct-to-LDS loads are issued from inline assembly: the compiler's own
+// intrinsic makes every later LDS read wait for all outstanding loads, which
+// would drain the stage ring on each step. The assembly sets M0 (the LDS base
+// of the wavefront's 1 KB) itself, and the waits are explicit below.
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace moe {
 namespace {
 
-constexpr int BM = kTiledBM;   // 128
-constexpr int BK = 64;         // K per step (one fragment tile column)
+constexpr int BM = kTiledBM;  // 256 rows
+constexpr int BN = 256;       // output columns (GEMM1: 128 gate + 128 up)
+constexpr int BK = 64;        // k bytes per stage
+constexpr int kStages = 4;
+constexpr int kWaves = 8;
+constexpr int kATiles = BM / 16, kBTiles = BN / 16;      // 1 KB tiles per stage
+constexpr int kStageBytes = (kATiles + kBTiles) * 1024;  // 32 KB
+constexpr int kLoadsPerWave = (kATiles + kBTiles) / kWaves;
+// Epilogue staging: 32 rows per pass, row pitch padded by 8 floats so that
+// the two 32-lane halves of a wavefront (rows r and r+4) use disjoint banks.
+constexpr int kEpiPitch1 = 32 + 8;  // GEMM1: 32 h columns per wavefront
+constexpr int kEpiPitch2 = 64 + 8;  // GEMM2: 64 y columns per wavefront
+constexpr int kSlice = kStages * kStageBytes / kWaves;
+static_assert(32 * kEpiPitch2 * 4 <= kSlice, "epilogue slice");
 
-__device__ __forceinline__ int lds_a_off(int m, int seg) {
-  return m * BK + ((seg ^ ((m >> 2) & 3)) << 4);
+struct TiledArgs {
+  const int8_t *act;        // fragment-tiled activations [rows/16][K/64] x 1 KB
+  const float *act_scale;   // GEMM1: sx [T] by token; GEMM2: sh [rows]
+  const int32_t *sorted;    // GEMM1: assignment of each permuted row
+  int k;
+  const int32_t *counts, *offsets, *mtile_off;  // offsets: 16-aligned group starts
+  const int32_t *dense_off;                     // GEMM1: dense group starts (debug rows)
+  int E;
+  int mt_max;               // upper bound on the number of M tiles
+  int nt;                   // N tiles per expert
+  int gn;                   // N tiles per group (divides nt)
+  const int8_t *w;          // fragment-tiled weights
+  const float *wscale;
+  int K, F, H;
+  float *out;               // GEMM1: h [rows][F]; GEMM2: y [rows][H]
+  uint32_t *amax;           // GEMM1: row max |h| (float bits)
+  int32_t *acc1_dbg;        // GEMM1: optional INT32 accumulators, dense rows [A][2F]
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
+}
+// 16 bytes per lane from global memory into LDS at lds_base + 16*lane. An
+// LDS-DMA load needs one wait state after M0 is written.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+// Wait until at most N of this wavefront's loads are in flight and its LDS
+// accesses are done, then meet the other wavefronts of the block.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// silu(g) * u with the hardware exponential and reciprocal.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 template <bool kGateUp>
-__global__ __launch_bounds__(256, 2) void gemm_tiled_kernel(
-    const int8_t *__restrict__ act, const float *__restrict__ act_scale,
-    const int32_t *__restrict__ sorted, int k, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ mtile_off, int E,
-    const int8_t *__restrict__ w, const float *__restrict__ wscale, int K, int F, int H,
-    void *__restrict__ out_v, uint32_t *__restrict__ amax, int32_t *__restrict__ acc1_dbg) {
-  __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * BK];
+__global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
   __shared__ float row_scale[BM];
-  __shared__ int32_t row_tok[BM];
 
-  // XCD-aware renumbering of the linear block id, then (m tile, n tile).
-  const int nbx = gridDim.x, nby = gridDim.y;
-  const int nb = nbx * nby;
-  const int b = blockIdx.x + nbx * blockIdx.y;
-  const int xcd = b & 7, idx = b >> 3, q = nb >> 3, rem = nb & 7;
-  const int logical = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-  const int mt = logical % nbx;   // global M tile (x: M tiles)
-  const int ntile = logical / nbx;
-
-  if (mt >= mtile_off[E]) return;
+  // XCD-contiguous renumbering of the block id, then (group, M tile, N tile).
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int xcd = b & 7, idx = b >> 3, q8 = nb >> 3, rem = nb & 7;
+  const int L = xcd < rem ? xcd * (q8 + 1) + idx : rem * (q8 + 1) + (xcd - rem) * q8 + idx;
+  const int per_group = a.mt_max * a.gn;
+  const int grp = L / per_group, r_in = L - grp * per_group;
+  const int mt = r_in / a.gn;
+  const int ntile = grp * a.gn + (r_in - mt * a.gn);
+  const int E = a.E;
+  if (mt >= a.mtile_off[E]) return;
   int lo = 0, hi = E;  // largest e with mtile_off[e] <= mt
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (mtile_off[mid] <= mt) lo = mid; else hi = mid;
+    if (a.mtile_off[mid] <= mt) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int R = counts[e];
-  const int row0 = offsets[e];
-  const int m0 = (mt - mtile_off[e]) * BM;
+  const int R = a.counts[e];
+  const int row0 = a.offsets[e];  // multiple of 16
+  const int m0 = (mt - a.mtile_off[e]) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = kGateUp ? 2 * F : H;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int K = a.K, F = a.F, H = a.H;
   const int KT = K / BK;
 
-  // Row bookkeeping: token (GEMM1) and activation scale of each tile row.
   if (tid < BM) {
     const int r = m0 + tid;
-    int tok = -1;
     float sc = 0.0f;
-    if (r < R) {
-      const int row = row0 + r;
-      tok = kGateUp ? sorted[row] / k : row;
-      sc = act_scale[tok];
-    }
-    row_tok[tid] = tok;
+    if (r < R) sc = kGateUp ? a.act_scale[a.sorted[row0 + r] / a.k] : a.act_scale[row0 + r];
     row_scale[tid] = sc;
   }
-  __syncthreads();
 
-  // Global -> LDS assignment: thread owns 16-byte chunks (row, seg) for rows
-  // tid>>2 and 64 + (tid>>2), segment tid&3.
-  const int seg = tid & 3;
-  const int8_t *asrc[2];
-  bool aval[2];
+  // This wavefront's share of each stage: activation tiles 2w, 2w+1 and
+  // weight tiles 2w, 2w+1. Activation tiles past the expert's last row tile
+  // are clamped to it (their rows are computed and never stored).
+  const int8_t *src[kLoadsPerWave];
+  int dst[kLoadsPerWave];
+  const int N = kGateUp ? 2 * F : H;
+  const int8_t *wexp = a.w + (size_t)e * (size_t)N * (size_t)K;
+  const int last_rt = (row0 + R - 1) >> 4;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = (tid >> 2) + 64 * i;
-    const int tok = row_tok[m];
-    aval[i] = tok >= 0;
-    asrc[i] = act + (size_t)(tok >= 0 ? tok : 0) * (size_t)K + seg * 16;
+  for (int t = 0; t < 2; ++t) {
+    const int ti = 2 * wave + t;
+    int rt = ((row0 + m0) >> 4) + ti;
+    rt = rt < last_rt ? rt : last_rt;
+    src[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
+    dst[t] = ti * 1024;
+    int wt;  // 16-channel weight tile
+    if (kGateUp) wt = ti < 8 ? ntile * 8 + ti : (F >> 4) + ntile * 8 + (ti - 8);
+    else wt = ntile * 16 + ti;
+    src[2 + t] = wexp + frag_tile(wt, 0, K) + lane * 16;
+    dst[2 + t] = (kATiles + ti) * 1024;
   }
-
-  // Weight fragment pointers: column tile ct of this wave.
-  const int8_t *wexp = w + (size_t)e * (size_t)N * (size_t)K;
-  const int8_t *bsrc[2];
-  int ncol[2];
+  auto issue = [&](int kt) {
+    int8_t *st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    int nc0;
-    if (kGateUp) nc0 = (ct == 0 ? 0 : F) + ntile * 128 + wave * 32;
-    else nc0 = ntile * 256 + wave * 64 + ct * 32;
-    const int n = nc0 + (lane & 31);
-    ncol[ct] = n;
-    bsrc[ct] = wexp + frag_tile(n >> 4, 0, K) + ((((lane >> 5) << 4) + (n & 15)) << 4);
-  }
+    for (int t = 0; t < kLoadsPerWave; ++t)
+      dma16(src[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + dst[t])));
+  };
 
   v16i acc[4][2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rt][ct][i] = 0;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  // Prologue: stage k tile 0.
-  v4i anext[2], bcur[2][2], bnext[2][2];
+  // Operand offsets inside a stage: 32x32x32 fragment of row (or column)
+  // block 32*blk, k half hk: tile 2*blk + (lane%32)/16, lane row lane%16,
+  // k group 2*hk + lane/32.
+  const int frag = (((lane >> 5) * 16) + (lane & 15)) * 16 + ((lane & 31) >> 4) * 1024;
+  int boff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    anext[i] = aval[i] ? *reinterpret_cast<const v4i *>(asrc[i]) : v4i{0, 0, 0, 0};
-    *reinterpret_cast<v4i *>(&lds_a[0][lds_a_off((tid >> 2) + 64 * i, seg)]) = anext[i];
+  for (int cb = 0; cb < 2; ++cb) {
+    const int t0 = kGateUp ? 8 * cb + 2 * wn : 4 * wn + 2 * cb;
+    boff[cb] = (kATiles + t0) * 1024 + frag;
   }
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      bcur[ct][hf] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(bsrc[ct] + hf * 512));
-  __syncthreads();
+  const int aoff = (8 * wm) * 1024 + frag;
 
+  const int pre = KT < kStages - 1 ? KT : kStages - 1;
+  for (int s2 = 0; s2 < pre; ++s2) issue(s2);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
+    const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
+    if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
+    else if (ahead == 1) wait_barrier<kLoadsPerWave>();
+    else wait_barrier<0>();
+    if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+    const int8_t *st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        anext[i] = aval[i] ? *reinterpret_cast<const v4i *>(asrc[i] + (size_t)(kt + 1) * BK)
-                           : v4i{0, 0, 0, 0};
+    for (int hk = 0; hk < 2; ++hk) {
+      v4i af[4], bf[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          bnext[ct][hf] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(
-              bsrc[ct] + ((size_t)(kt + 1) << 10) + hf * 512));
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int m = rt * 32 + (lane & 31);
-      v4i afr[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        afr[hf] = *reinterpret_cast<const v4i *>(&lds_a[cur][lds_a_off(m, 2 * hf + (lane >> 5))]);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) acc[rt][ct] = mfma32(afr[hf], bcur[ct][hf], acc[rt][ct]);
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<v4i *>(&lds_a[cur ^ 1][lds_a_off((tid >> 2) + 64 * i, seg)]) = anext[i];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) bcur[ct][hf] = bnext[ct][hf];
-    }
-    __syncthreads();
   }
+  // Every wavefront is done with the stage buffers before they are reused.
+  wait_barrier<0>();
 
-  // Epilogue. Lane holds column (lane & 31) of each 32x32 tile and rows
-  // rt*32 + (i/4)*8 + (lane/32)*4 + i%4, i < 16.
+  // Epilogue, 32 rows (row block i) at a time through this wavefront's LDS
+  // slice. Lane holds column (lane & 31) of each 32x32 accumulator tile and
+  // rows 8*(v/4) + 4*(lane/32) + v%4, v < 16.
+  float *slice = reinterpret_cast<float *>(lds + wave * kSlice);
+  const int mw = 128 * wm;
+  const int rl = 4 * (lane >> 5);  // lane's row offset inside a group of 8
   if (kGateUp) {
-    const int f = ncol[0];  // gate column == h column
-    const float sg = wscale[(size_t)e * 2 * F + f];
-    const float su = wscale[(size_t)e * 2 * F + F + f];
+    const int f0 = ntile * 128 + 32 * wn;  // first h column of this wavefront
+    const float *sgu = a.wscale + (size_t)e * 2 * F;
+    const float sg = sgu[f0 + (lane & 31)], su = sgu[F + f0 + (lane & 31)];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = rt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        const bool valid = m0 + m < R;
-        float hv = 0.0f;
-        if (valid) {
-          const int row = row0 + m0 + m;
-          const float sxv = row_scale[m];
-          const float g = (float)acc[rt][0][i] * sxv * sg;
-          const float u = (float)acc[rt][1][i] * sxv * su;
-          hv = g / (1.0f + expf(-g)) * u;
-          static_cast<float *>(out_v)[(size_t)row * F + f] = hv;
-          if (acc1_dbg) {
-            acc1_dbg[(size_t)row * 2 * F + f] = acc[rt][0][i];
-            acc1_dbg[(size_t)row * 2 * F + F + f] = acc[rt][1][i];
-          }
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + rl + (v & 3);
+        const float sxv = row_scale[mw + 32 * i + r];
+        const float hv = swiglu((float)acc[i][0][v] * sxv * sg, (float)acc[i][1][v] * sxv * su);
+        slice[r * kEpiPitch1 + (lane & 31)] = hv;
+        if (a.acc1_dbg && m0 + mw + 32 * i + r < R) {
+          const size_t row = (size_t)(a.dense_off[e] + m0 + mw + 32 * i + r);
+          a.acc1_dbg[row * 2 * F + f0 + (lane & 31)] = acc[i][0][v];
+          a.acc1_dbg[row * 2 * F + F + f0 + (lane & 31)] = acc[i][1][v];
         }
-        float mx = __builtin_fabsf(hv);
+      }
+      // 32 rows x 32 columns: 8 lanes per row, 4 floats each.
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (valid && (lane & 31) == 0) atomicMax(amax + row0 + m0 + m, __float_as_uint(mx));
+      for (int j = 0; j < 4; ++j) {
+        const int c = j * 64 + lane;
+        const int r = c >> 3, c4 = (c & 7) * 4;
+        const v4f hv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch1 + c4);
+        float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(hv[0]), __builtin_fabsf(hv[1])),
+                                   __builtin_fmaxf(__builtin_fabsf(hv[2]), __builtin_fabsf(hv[3])));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2, 64));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4, 64));
+        const int m = mw + 32 * i + r;
+        if (m0 + m < R) {
+          const size_t row = (size_t)(row0 + m0 + m);
+          __builtin_nontemporal_store(hv, reinterpret_cast<v4f *>(a.out + row * F + f0 + c4));
+          if ((lane & 7) == 0) atomicMax(a.amax + row, __float_as_uint(mx));
+        }
       }
     }
   } else {
+    const int n0 = ntile * 256 + 64 * wn;  // first y column of this wavefront
+    const float sd0 = a.wscale[(size_t)e * H + n0 + (lane & 31)];
+    const float sd1 = a.wscale[(size_t)e * H + n0 + 32 + (lane & 31)];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int n = ncol[ct];
-      const float sd = wscale[(size_t)e * H + n];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + rl + (v & 3);
+        const float shv = row_scale[mw + 32 * i + r];
+        slice[r * kEpiPitch2 + (lane & 31)] = (float)acc[i][0][v] * shv * sd0;
+        slice[r * kEpiPitch2 + 32 + (lane & 31)] = (float)acc[i][1][v] * shv * sd1;
+      }
+      // 32 rows x 64 columns: 16 lanes per row, 4 floats each.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = rt * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-          if (m0 + m < R) {
-            const int row = row0 + m0 + m;
-            static_cast<float *>(out_v)[(size_t)row * H + n] =
-                (float)acc[rt][ct][i] * row_scale[m] * sd;
-          }
+      for (int j = 0; j < 8; ++j) {
+        const int c = j * 64 + lane;
+        const int r = c >> 4, c4 = (c & 15) * 4;
+        const int m = mw + 32 * i + r;
+        if (m0 + m < R) {
+          const v4f yv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch2 + c4);
+          __builtin_nontemporal_store(
+              yv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * H + n0 + c4));
         }
       }
     }
   }
+}
+
+// N tiles per L2 group: the largest divisor of nt that is at most 4.
+int group_n(int nt) {
+  for (int g = 4; g > 1; --g)
+    if (nt % g == 0) return g;
+  return 1;
 }
 
 }  // namespace
 
-hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
+hipError_t launch_gemm1_tiled(const int8_t *a1, const float *sx, const int32_t *sorted, int k,
                               const int32_t *counts, const int32_t *offsets,
-                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
-                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st, Timing tm) {
-  const int64_t mtiles = (A + BM - 1) / BM + E;
-  const dim3 grid((unsigned)mtiles, (unsigned)(F / 128));
-  return launch_kernel(gemm_tiled_kernel<true>, grid, dim3(256), st, tm, qx, sx, sorted, k, counts,
-                       offsets, mtile_off, E, w_gu, s_gu, H, F, H, (void *)h, amax, acc1_dbg);
+                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
+                              uint32_t *amax, int32_t *acc1_dbg, hipStream_t st, Timing tm) {
+  TiledArgs a{};
+  a.act = a1; a.act_scale = sx; a.sorted = sorted; a.k = k; a.counts = counts;
+  a.offsets = offsets; a.dense_off = dense_off; a.mtile_off = mtile_off; a.E = E;
+  a.mt_max = (int)((A + BM - 1) / BM + E);
+  a.nt = F / 128; a.gn = group_n(a.nt);
+  a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H; a.out = h; a.amax = amax;
+  a.acc1_dbg = acc1_dbg;
+  const dim3 grid((unsigned)((int64_t)a.mt_max * a.nt));
+  return launch_kernel(gemm_tiled_kernel<true>, grid, dim3(512), st, tm, a);
 }
 
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E,
                               float *y, hipStream_t st, Timing tm) {
-  const int64_t mtiles = (A + BM - 1) / BM + E;
-  const dim3 grid((unsigned)mtiles, (unsigned)(H / 256));
-  return launch_kernel(gemm_tiled_kernel<false>, grid, dim3(256), st, tm, qh, sh,
-                       (const int32_t *)nullptr, 1, counts, offsets, mtile_off, E, w_d, s_d, F, F,
-                       H, (void *)y, (uint32_t *)nullptr, (int32_t *)nullptr);
+  TiledArgs a{};
+  a.act = qh; a.act_scale = sh; a.k = 1; a.counts = counts; a.offsets = offsets;
+  a.mtile_off = mtile_off; a.E = E;
+  a.mt_max = (int)((A + BM - 1) / BM + E);
+  a.nt = H / 256; a.gn = group_n(a.nt);
+  a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
+  const dim3 grid((unsigned)((int64_t)a.mt_max * a.nt));
+  return launch_kernel(gemm_tiled_kernel<false>, grid, dim3(512), st, tm, a);
 }
 
 }  // namespace moe

@@ -1,5 +1,5 @@
 // layer_device.h -- device building blocks of the layer shared by more than
-// one kernel: the per-token router, the per-row INT8 quantisers and the
+// one kernel: the per-token router, the per-token INT8 quantiser and the
 // gate-weighted combine of one token. Included by the HIP sources only.
 #pragma once
 
@@ -151,25 +151,6 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
     }
   } else {
     for (int c = lane; c < nchunk; c += 64) emit(*reinterpret_cast<const v4i *>(xr + c * 8), c);
-  }
-}
-
-// Requantisation of one SwiGLU row h[0..F) whose max |h| is known (the same
-// rule as above, "MiniMax-M3 W8A8 inference on K100AI" §4.3: the two matmuls
-// stay in INT8). One wavefront per row, 16-byte loads, 4-byte stores.
-__device__ __forceinline__ void requant_row(const float *__restrict__ hr, float amax, int F,
-                                            int8_t *__restrict__ qr, float *__restrict__ sh) {
-  const int lane = threadIdx.x & 63;
-  if (lane == 0) *sh = amax / 127.0f;
-  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
-  const int n4 = F >> 2;
-#pragma unroll 4
-  for (int c = lane; c < n4; c += 64) {
-    const v4f v = *reinterpret_cast<const v4f *>(hr + c * 4);
-    const uint32_t p = (uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
-                       ((uint32_t)(q8(v[2], rr) & 0xff) << 16) |
-                       ((uint32_t)(q8(v[3], rr) & 0xff) << 24);
-    *reinterpret_cast<uint32_t *>(qr + c * 4) = p;
   }
 }
 

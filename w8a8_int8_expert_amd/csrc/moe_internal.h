@@ -17,9 +17,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // Tokens routed (and histogrammed) per block of the routing kernel.
 constexpr int kRouteTokens = 64;
 // Rows per M tile of the tiled grouped GEMMs.
-constexpr int kTiledBM = 128;
-// Output channels per block of the tiled GEMMs (gate+up rows for GEMM1).
-constexpr int kTiledBN = 256;
+constexpr int kTiledBM = 256;
 // Maximum experts (LDS histograms are sized for it).
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
@@ -88,10 +86,13 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // ---------------------------------------------------------------- workspace
 // Regions of the forward workspace (byte offsets from its base).
+// Permuted rows inside the layer are "padded": every expert's group starts on
+// a 16-row boundary, so P <= A + 15*min(E, A) rows for A = T*k assignments.
 struct FwdLayout {
-  size_t ids, wts, blk_hist, counts, offsets, mtile_off, sorted, row_of, qx, sx, h, amax, qh,
-      sh, y, total;
+  size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, a1,
+      h, amax, qh, sh, y, total;
   int64_t nblk;  // routing blocks
+  int64_t P;     // padded permuted rows (upper bound)
 };
 FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k);
 // Calibrate workspace: ax[H], aw[H] as uint32 float bits.
@@ -99,44 +100,60 @@ size_t calib_ws_bytes(int H);
 
 // ----------------------------------------------------------------- launchers
 // Each returns hipGetLastError() after enqueueing on `st` (timed by `tm`).
+// Rows of sorted/h/amax/qh/sh/y are padded rows; offsets are dense group
+// starts, poffsets the padded ones; qh (and a1) are fragment-tiled.
 // Fused small-batch prologue: route (or copy pre-routed ids), group, clear
-// the per-row max buffer (A words), and quantise the activations.
+// the per-row max and sorted[] over P rows, and quantise the activations.
 hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
                                  int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
-                                 int32_t *counts, int32_t *offsets, int32_t *mtile_off,
-                                 int32_t *sorted, int32_t *row_of, const uint16_t *x,
-                                 const float *inv_s, int H, int8_t *qx, float *sx, uint32_t *amax,
-                                 hipStream_t st, Timing tm);
+                                 int32_t *counts, int32_t *offsets, int32_t *poffsets,
+                                 int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
+                                 const uint16_t *x, const float *inv_s, int H, int8_t *qx,
+                                 float *sx, uint32_t *amax, hipStream_t st, Timing tm);
 hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
-                             int32_t *blk_hist, uint32_t *amax, hipStream_t st, Timing tm);
+                             int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
+                             hipStream_t st, Timing tm);
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
-                       int32_t *offsets, int32_t *mtile_off, hipStream_t st, Timing tm);
-hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
+                       int32_t *offsets, int32_t *poffsets, int32_t *mtile_off, hipStream_t st,
+                       Timing tm);
+hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *poffsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
                           int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
                             float *sx, hipStream_t st, Timing tm);
-hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *offsets, int E,
-                          int64_t A, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm);
+hipError_t launch_gather_tiles(const int8_t *qx, const int32_t *sorted, int k,
+                               const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
+                               hipStream_t st, Timing tm);
+hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
+                          int64_t P, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm);
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
-                               const int32_t *counts, const int32_t *offsets, const int8_t *w_gu,
-                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                               int32_t *acc1_dbg, hipStream_t st, Timing tm);
+                               const int32_t *counts, const int32_t *poffsets,
+                               const int32_t *dense_off, const int8_t *w_gu, const float *s_gu,
+                               int H, int F, int E, float *h, uint32_t *amax, int32_t *acc1_dbg,
+                               hipStream_t st, Timing tm);
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
-                               const int32_t *offsets, const int8_t *w_d, const float *s_d, int H,
+                               const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
                                int F, int E, float *y, hipStream_t st, Timing tm);
-hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
-                              const int32_t *counts, const int32_t *offsets,
-                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
-                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st, Timing tm);
+hipError_t launch_gemm1_tiled(const int8_t *a1, const float *sx, const int32_t *sorted, int k,
+                              const int32_t *counts, const int32_t *poffsets,
+                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
+                              uint32_t *amax, int32_t *acc1_dbg, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
-                              const int32_t *offsets, const int32_t *mtile_off, int64_t A,
+                              const int32_t *poffsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E,
                               float *y, hipStream_t st, Timing tm);
 hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm);
+// stage outputs in dense rows (debug only)
+hipError_t launch_debug_rows(const int32_t *offsets, const int32_t *poffsets, int E, int64_t A,
+                             const int32_t *sorted_p, const float *h_p, const int8_t *qh_t,
+                             const float *sh_p, const float *y_p, int F, int H, int32_t *sorted,
+                             float *h, int8_t *qh, float *sh, float *y, hipStream_t st);
+hipError_t launch_debug_row_of(const int32_t *row_of_p, const int32_t *ids, const int32_t *offsets,
+                               const int32_t *poffsets, int64_t A, int32_t *row_of,
+                               hipStream_t st);
 // calibrate
 hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const float *w_gate,
                                const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,

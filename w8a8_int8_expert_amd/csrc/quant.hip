@@ -1,7 +1,7 @@
-// quant.hip -- per-token activation quantisation and per-row requantisation
-// as launches of their own (the multi-block path of a large batch; a small
-// batch quantises inside the fused prologue, and the streaming GEMM1
-// requantises in its last block per expert).
+// quant.hip -- per-token activation quantisation (a launch of its own for a
+// large batch; a small batch quantises inside the fused prologue), per-row
+// requantisation of the SwiGLU output into GEMM2's tiled operand, and the
+// gather that lays out GEMM1's tiled operand for the tiled path.
 //
 // "MiniMax-M3 W8A8 inference on K100AI" (mhpq.cn/news/1068415) §3.2 and §6.4:
 // activations are quantised per token (one outlier token must not set the
@@ -24,16 +24,60 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
   quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t);
 }
 
-// h fp32 [A][F] with row max |h| in amax (float bits) -> qh int8, sh fp32.
-// Rows past the number of kept rows (offsets[E]) are left alone.
+// h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
+// fragment-tiled (16 rows x 64 k per 1 KB, the layout of the weights: the
+// activation operand of GEMM2) and sh fp32 [rows]. Block = one 16-row tile x
+// 256 columns; thread = 16 consecutive values of one row, which quantise to
+// exactly one 16-byte chunk of a tile. Rows past the padded row count are
+// left alone; padding rows (max 0) get codes 0 unless their h is undefined,
+// which only rows that are never stored downstream can be.
 __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ h,
                                                       const uint32_t *__restrict__ amax_bits,
-                                                      const int32_t *__restrict__ offsets, int E,
+                                                      const int32_t *__restrict__ poffsets, int E,
                                                       int F, int8_t *__restrict__ qh,
                                                       float *__restrict__ sh) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= offsets[E]) return;
-  requant_row(h + r * F, __uint_as_float(amax_bits[r]), F, qh + r * F, sh + r);
+  const int rt = blockIdx.x;
+  const int row = rt * 16 + (threadIdx.x >> 4);
+  if (row >= poffsets[E]) return;
+  const int c0 = blockIdx.y * 256 + (threadIdx.x & 15) * 16;
+  if (c0 >= F) return;
+  const float amax = __uint_as_float(amax_bits[row]);
+  if (c0 == 0) sh[row] = amax / 127.0f;
+  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float *hr = h + (size_t)row * F + c0;
+  v4i q;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const v4f v = *reinterpret_cast<const v4f *>(hr + 4 * w);
+    q[w] = (int)((uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
+                 ((uint32_t)(q8(v[2], rr) & 0xff) << 16) | ((uint32_t)(q8(v[3], rr) & 0xff) << 24));
+  }
+  const int kt = c0 >> 6, g = (c0 & 63) >> 4;
+  *reinterpret_cast<v4i *>(qh + frag_tile(rt, kt, F) + ((g * 16 + (row & 15)) << 4)) = q;
+}
+
+// GEMM1's activation operand for the tiled path: the quantised token rows in
+// permuted (padded) row order, fragment-tiled, so that the GEMM streams
+// contiguous 1 KB tiles instead of gathering 64-byte row pieces. Block = one
+// 16-row tile; wavefront w builds k tiles w, w+4, ...: lane l copies row
+// l%16, k bytes 16*(l/16).. of the tile. Padding rows are zero.
+__global__ __launch_bounds__(256) void gather_tiles_kernel(const int8_t *__restrict__ qx,
+                                                           const int32_t *__restrict__ sorted,
+                                                           int k,
+                                                           const int32_t *__restrict__ poffsets,
+                                                           int E, int H, int8_t *__restrict__ a1) {
+  const int rt = blockIdx.x;
+  if (rt * 16 >= poffsets[E]) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int asg = sorted[rt * 16 + (lane & 15)];
+  const int8_t *src = qx + (size_t)(asg >= 0 ? asg / k : 0) * H + (lane >> 4) * 16;
+  int8_t *dst = a1 + frag_tile(rt, 0, H) + lane * 16;
+  const int KT = H >> 6;
+#pragma unroll 4
+  for (int kt = wave; kt < KT; kt += 4) {
+    const v4i v = asg >= 0 ? *reinterpret_cast<const v4i *>(src + kt * 64) : v4i{0, 0, 0, 0};
+    *reinterpret_cast<v4i *>(dst + ((size_t)kt << 10)) = v;
+  }
 }
 
 }  // namespace
@@ -44,10 +88,17 @@ hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, in
                        T, H, qx, sx);
 }
 
-hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *offsets, int E,
-                          int64_t A, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm) {
-  return launch_kernel(requant_kernel, dim3((unsigned)((A + 3) / 4)), dim3(256), st, tm, h, amax,
-                       offsets, E, F, qh, sh);
+hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
+                          int64_t P, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm) {
+  const dim3 grid((unsigned)((P + 15) / 16), (unsigned)((F + 255) / 256));
+  return launch_kernel(requant_kernel, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh, sh);
+}
+
+hipError_t launch_gather_tiles(const int8_t *qx, const int32_t *sorted, int k,
+                               const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
+                               hipStream_t st, Timing tm) {
+  return launch_kernel(gather_tiles_kernel, dim3((unsigned)((P + 15) / 16)), dim3(256), st, tm, qx,
+                       sorted, k, poffsets, E, H, a1);
 }
 
 }  // namespace moe

@@ -18,7 +18,13 @@
 //      capacity, offsets, M-tile table) -> scatter (one block per 64 tokens:
 //      stable ranks from wave ballots); activation quantisation is its own
 //      launch (quant.hip).
-// Both clear the per-row max buffer that GEMM1 fills later in the call.
+// Inside the layer every expert's group of permuted rows starts on a 16-row
+// boundary ("padded" rows: the activation operands of the grouped GEMMs are
+// stored as 16-row x 64-k tiles, and no tile may hold two experts' rows).
+// Both paths write the dense offsets (the grouping as the order defines it),
+// the padded offsets, sorted[] and row_of[] in padded rows (-1 marks padding
+// and dropped assignments), and clear the per-row max buffer that GEMM1
+// fills later in the call.
 #include "layer_device.h"
 
 namespace moe {
@@ -45,9 +51,9 @@ __device__ __forceinline__ int id_bits(int E) {
   return nbits;
 }
 
-// Clear n int32 words starting at p with the threads of this block.
-__device__ __forceinline__ void block_clear(uint32_t *p, int64_t n) {
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+// Fill n int32 words starting at p with v, with the threads of this block.
+__device__ __forceinline__ void block_fill(uint32_t *p, int64_t n, uint32_t v) {
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = v;
 }
 
 // Inclusive wave scan of ints (64 lanes).
@@ -78,29 +84,35 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
   return base + incl - v;
 }
 
-// Kept counts per expert from the totals: capacity, offsets, counts and the
-// M-tile table of the tiled GEMMs. One thread per expert (E <= 1024, 1024
-// threads). Returns this thread's expert offset (0 past E).
+// Kept counts per expert from the totals: capacity, dense offsets, 16-row
+// aligned (padded) offsets, counts and the M-tile table of the tiled GEMMs.
+// One thread per expert (E <= 1024, 1024 threads). Returns this thread's
+// padded offset (0 past E).
 __device__ __forceinline__ int finish_counts(int total, int E, int64_t capacity,
                                              int32_t *__restrict__ counts,
                                              int32_t *__restrict__ offsets,
+                                             int32_t *__restrict__ poffsets,
                                              int32_t *__restrict__ mtile_off, int *wsum) {
   const int tid = threadIdx.x;
-  int kept = 0, tiles = 0;
+  int kept = 0, tiles = 0, padded = 0;
   if (tid < E) {
     kept = total;
     if (capacity > 0 && (int64_t)kept > capacity) kept = (int)capacity;
     tiles = (kept + kTiledBM - 1) / kTiledBM;
+    padded = (kept + 15) & ~15;
     counts[tid] = kept;
   }
   int all;
   const int off = block_excl_scan(kept, wsum, &all);
   if (tid < E) offsets[tid] = off;
   if (tid == 0) offsets[E] = all;
+  const int poff = block_excl_scan(padded, wsum, &all);
+  if (tid < E) poffsets[tid] = poff;
+  if (tid == 0) poffsets[E] = all;
   const int toff = block_excl_scan(tiles, wsum, &all);
   if (tid < E) mtile_off[tid] = toff;
   if (tid == 0) mtile_off[E] = all;
-  return off;
+  return poff;
 }
 
 // ------------------------------------------------------------- small A path
@@ -109,10 +121,10 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
     const float *__restrict__ w_in, int T, int E, int k, int64_t capacity,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
-    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, const uint16_t *__restrict__ x,
-    const float *__restrict__ inv_s, int H, int8_t *__restrict__ qx, float *__restrict__ sx,
-    uint32_t *__restrict__ amax) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ poffsets,
+    int32_t *__restrict__ mtile_off, int32_t *__restrict__ sorted, int32_t *__restrict__ row_of,
+    int P, const uint16_t *__restrict__ x, const float *__restrict__ inv_s, int H,
+    int8_t *__restrict__ qx, float *__restrict__ sx, uint32_t *__restrict__ amax) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
     const int64_t t = (int64_t)(blockIdx.x - 1) * 16 + wave;
@@ -126,7 +138,8 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
   __shared__ int wsum[16];
   const int A = T * k;
   for (int e = tid; e < E; e += 1024) { hist[e] = 0; run[e] = 0; }
-  block_clear(amax, A);
+  block_fill(amax, P, 0u);
+  block_fill(reinterpret_cast<uint32_t *>(sorted), P, 0xFFFFFFFFu);
   __syncthreads();
   for (int t = wave; t < T; t += 16) {
     int e;
@@ -145,8 +158,8 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     }
   }
   __syncthreads();
-  const int off = finish_counts(tid < E ? hist[tid] : 0, E, capacity, counts, offsets, mtile_off,
-                                wsum);
+  const int off = finish_counts(tid < E ? hist[tid] : 0, E, capacity, counts, offsets, poffsets,
+                                mtile_off, wsum);
   if (tid < E) lds_off[tid] = off;
   __syncthreads();
   if (wave != 0) return;
@@ -180,16 +193,21 @@ template <int NV>
 __global__ __launch_bounds__(1024) void route_hist_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
     const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
-    float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax) {
+    float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax,
+    int32_t *__restrict__ sorted, int64_t P) {
   __shared__ int32_t hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) hist[e] = 0;
-  // This block's share of the per-row max buffer: rows [b*64*k, (b+1)*64*k).
+  // This block's share of the padded rows: [b*64*k, (b+1)*64*k), and the
+  // last block also takes the rows past T*k.
   {
-    const int64_t A = T * (int64_t)k;
     const int64_t r0 = (int64_t)blockIdx.x * kRouteTokens * k;
-    const int64_t r1 = r0 + (int64_t)kRouteTokens * k < A ? r0 + (int64_t)kRouteTokens * k : A;
-    for (int64_t r = r0 + tid; r < r1; r += 1024) amax[r] = 0u;
+    int64_t r1 = r0 + (int64_t)kRouteTokens * k;
+    if (blockIdx.x == gridDim.x - 1 || r1 > P) r1 = P;
+    for (int64_t r = r0 + tid; r < r1; r += 1024) {
+      amax[r] = 0u;
+      sorted[r] = -1;
+    }
   }
   __syncthreads();
   const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
@@ -221,6 +239,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
                                                     int E, int64_t capacity,
                                                     int32_t *__restrict__ counts,
                                                     int32_t *__restrict__ offsets,
+                                                    int32_t *__restrict__ poffsets,
                                                     int32_t *__restrict__ mtile_off) {
   __shared__ int32_t total[kMaxExperts];
   __shared__ int wsum[16];
@@ -241,10 +260,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
     if (lane == 63) total[e] = incl;
   }
   __syncthreads();
-  finish_counts(tid < E ? total[tid] : 0, E, capacity, counts, offsets, mtile_off, wsum);
+  finish_counts(tid < E ? total[tid] : 0, E, capacity, counts, offsets, poffsets, mtile_off,
+                wsum);
 }
 
-// Stable scatter. Assignments of this block are processed in rounds of 256
+// Stable scatter into padded rows (`offsets` are the padded offsets here).
+// Assignments of this block are processed in rounds of 256
 // (4 waves x 64 lanes, wave order = assignment order). A lane's rank among
 // equal experts of its wave comes from ballots over the id bits; earlier
 // waves of the round and earlier rounds are added through LDS counters.
@@ -310,15 +331,15 @@ int route_nv(int E) {
 
 hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
                                  int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
-                                 int32_t *counts, int32_t *offsets, int32_t *mtile_off,
-                                 int32_t *sorted, int32_t *row_of, const uint16_t *x,
-                                 const float *inv_s, int H, int8_t *qx, float *sx, uint32_t *amax,
-                                 hipStream_t st, Timing tm) {
+                                 int32_t *counts, int32_t *offsets, int32_t *poffsets,
+                                 int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
+                                 const uint16_t *x, const float *inv_s, int H, int8_t *qx,
+                                 float *sx, uint32_t *amax, hipStream_t st, Timing tm) {
   const dim3 grid(1 + (unsigned)((T + 15) / 16)), block(1024);
 #define MOE_PROLOGUE(NV)                                                                     \
   return launch_kernel(prologue_small_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, \
-                       E, k, capacity, ids, wts, counts, offsets, mtile_off, sorted, row_of, x, \
-                       inv_s, H, qx, sx, amax)
+                       E, k, capacity, ids, wts, counts, offsets, poffsets, mtile_off, sorted,  \
+                       row_of, P, x, inv_s, H, qx, sx, amax)
   switch (route_nv(E)) {
     case 1: MOE_PROLOGUE(1);
     case 2: MOE_PROLOGUE(2);
@@ -331,11 +352,12 @@ hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, con
 
 hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
-                             int32_t *blk_hist, uint32_t *amax, hipStream_t st, Timing tm) {
+                             int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
+                             hipStream_t st, Timing tm) {
   const dim3 grid((unsigned)((T + kRouteTokens - 1) / kRouteTokens)), block(1024);
 #define MOE_ROUTE(NV)                                                                        \
   return launch_kernel(route_hist_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, E, \
-                       k, ids, wts, blk_hist, amax)
+                       k, ids, wts, blk_hist, amax, sorted, P)
   switch (route_nv(E)) {
     case 1: MOE_ROUTE(1);
     case 2: MOE_ROUTE(2);
@@ -347,9 +369,10 @@ hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const f
 }
 
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
-                       int32_t *offsets, int32_t *mtile_off, hipStream_t st, Timing tm) {
+                       int32_t *offsets, int32_t *poffsets, int32_t *mtile_off, hipStream_t st,
+                       Timing tm) {
   return launch_kernel(scan_kernel, dim3(1), dim3(1024), st, tm, blk_hist, nblk, E, capacity,
-                       counts, offsets, mtile_off);
+                       counts, offsets, poffsets, mtile_off);
 }
 
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
