@@ -34,8 +34,12 @@ STAGE_INDEX = {s: i for i, s in enumerate(
     ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine"))}
 # Sources of the kernels whose counter-measured traffic may be reused.
 KERNEL_SOURCES = {
-    "gemm1_stream": ["w8a8_int8_expert_amd/csrc/gemm_stream.hip"],
-    "gemm1_tiled": ["w8a8_int8_expert_amd/csrc/gemm_tiled.hip"],
+    "gemm1_stream": ["w8a8_int8_expert_amd/csrc/gemm_stream.hip",
+                     "w8a8_int8_expert_amd/csrc/layer_device.h",
+                     "w8a8_int8_expert_amd/csrc/moe_internal.h"],
+    "gemm1_tiled": ["w8a8_int8_expert_amd/csrc/gemm_tiled.hip",
+                    "w8a8_int8_expert_amd/csrc/layer_device.h",
+                    "w8a8_int8_expert_amd/csrc/moe_internal.h"],
 }
 
 

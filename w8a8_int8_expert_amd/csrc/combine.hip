@@ -3,20 +3,19 @@
 // "超大规模模型推理的Day0适配实践" §四: after the grouped GEMMs the MoE operator
 // un-sorts the rows and takes the weighted sum per token (combine8 in
 // layer_device.h: fp32 in slot order, bfloat16 with ties to even).
-// Grid (T, H/512), one wavefront per block; each lane owns 8 consecutive
-// outputs (two 16-byte loads of fp32 y per kept slot, one 16-byte store), so
-// even a decode step of a few tokens spreads over many CUs.
+// Grid (T, H/2048), 256 threads per block; each thread owns 8 consecutive
+// outputs (two 16-byte loads of fp32 y per kept slot, one 16-byte store).
 #include "layer_device.h"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ y,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const float *__restrict__ wts,
                                                       const int32_t *__restrict__ row_of,
                                                       int64_t T, int H, int k,
                                                       uint16_t *__restrict__ out) {
-  const int n = (blockIdx.y * 64 + threadIdx.x) * 8;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (n < H) combine8(y, wts, row_of, blockIdx.x, H, k, n, out);
 }
 
@@ -24,8 +23,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ y
 
 hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm) {
-  const dim3 grid((unsigned)T, (unsigned)((H + 511) / 512));
-  return launch_kernel(combine_kernel, grid, dim3(64), st, tm, y, wts, row_of, T, H, k, out);
+  const dim3 grid((unsigned)T, (unsigned)((H + 2047) / 2048));
+  return launch_kernel(combine_kernel, grid, dim3(256), st, tm, y, wts, row_of, T, H, k, out);
 }
 
 }  // namespace moe

@@ -14,11 +14,13 @@
 // Both operands are stored fragment-tiled (16 rows x 64 k per 1 KB, the lane
 // order of the INT8 matrix instructions): the weights by calibration, the
 // activations by the kernel that produces them (expert groups start on a
-// 16-row boundary). K advances 64 at a time through a 4-stage ring of 32 KB
-// LDS buffers filled by direct global->LDS loads (global_load_lds_dwordx4: a
-// wavefront moves one contiguous 1 KB tile per instruction, lane l's 16
-// bytes landing at byte 16*l), issued three stages ahead of use. Reading a
-// 32x32x32 operand from such a tile is a conflict-free ds_read_b128.
+// 16-row boundary). K advances 64 at a time through a 5-stage ring of 32 KB
+// LDS buffers (all 160 KB) filled by direct global->LDS loads
+// (global_load_lds_dwordx4: a wavefront moves one contiguous 1 KB tile per
+// instruction, lane l's 16 bytes landing at byte 16*l), issued four stages
+// ahead of use: about 128 KB per CU in flight, which the L2 latency under
+// load needs. Reading a 32x32x32 operand from such a tile is a conflict-free
+// ds_read_b128.
 // A 256x256 tile moves 2 bytes per 256 int8 operations, which is what keeps
 // the loads under the matrix time: the L2 -> LDS path sustains about 27
 // bytes per clock per CU, the INT8 matrix cores 8192 operations.
@@ -29,11 +31,11 @@
 // stage buffers so that every global store writes 16 bytes per lane along a
 // row.
 //
-// Tiles of all experts are numbered (N group, M tile, N tile in group): the
-// blocks that run together share a few weight panels and reuse each
-// activation tile across the group. Block ids are renumbered so that each
-// XCD (one L2) takes a contiguous range of that order. M tiles past the last
-// expert's exit at once (the grid is sized by an upper bound).
+// Tiles are numbered expert by expert, and within an expert (N group, M tile,
+// N tile in group), so that the blocks that run together on one XCD (one L2)
+// share a few weight panels and reuse each activation tile across the group;
+// each XCD takes one contiguous eighth of that order. The grid is sized by
+// an upper bound on the tile count; surplus blocks exit at once.
 #include "layer_device.h"
 
 // The direct-to-LDS loads are issued from inline assembly: the compiler's own
@@ -48,7 +50,7 @@ namespace {
 constexpr int BM = kTiledBM;  // 256 rows
 constexpr int BN = 256;       // output columns (GEMM1: 128 gate + 128 up)
 constexpr int BK = 64;        // k bytes per stage
-constexpr int kStages = 4;
+constexpr int kStages = 5;
 constexpr int kWaves = 8;
 constexpr int kATiles = BM / 16, kBTiles = BN / 16;      // 1 KB tiles per stage
 constexpr int kStageBytes = (kATiles + kBTiles) * 1024;  // 32 KB
@@ -57,8 +59,10 @@ constexpr int kLoadsPerWave = (kATiles + kBTiles) / kWaves;
 // the two 32-lane halves of a wavefront (rows r and r+4) use disjoint banks.
 constexpr int kEpiPitch1 = 32 + 8;  // GEMM1: 32 h columns per wavefront
 constexpr int kEpiPitch2 = 64 + 8;  // GEMM2: 64 y columns per wavefront
-constexpr int kSlice = kStages * kStageBytes / kWaves;
+constexpr int kSlice = 16384;                 // per-wavefront epilogue staging
+constexpr int kRowScaleAt = kWaves * kSlice;  // then 256 row scales
 static_assert(32 * kEpiPitch2 * 4 <= kSlice, "epilogue slice");
+static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "row scales");
 
 struct TiledArgs {
   const int8_t *act;        // fragment-tiled activations [rows/16][K/64] x 1 KB
@@ -104,39 +108,40 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 template <bool kGateUp>
 __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
+  // All 160 KB: the stage ring, then (after the K loop) the epilogue staging
+  // and the row scales.
   __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
-  __shared__ float row_scale[BM];
+  float *row_scale = reinterpret_cast<float *>(lds + kRowScaleAt);
 
-  // XCD-contiguous renumbering of the block id, then (group, M tile, N tile).
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int xcd = b & 7, idx = b >> 3, q8 = nb >> 3, rem = nb & 7;
-  const int L = xcd < rem ? xcd * (q8 + 1) + idx : rem * (q8 + 1) + (xcd - rem) * q8 + idx;
-  const int per_group = a.mt_max * a.gn;
-  const int grp = L / per_group, r_in = L - grp * per_group;
-  const int mt = r_in / a.gn;
-  const int ntile = grp * a.gn + (r_in - mt * a.gn);
+  // Tiles in expert-major order (expert, N group, M tile, N tile in group),
+  // cut into 8 equal contiguous chunks of the actual tile count, chunk x on
+  // XCD x (blocks are dealt to the XCDs round-robin by id). An XCD thus runs
+  // an expert's N groups back to back: the expert's weights are read once
+  // and its activation tiles are re-read while still in the caches.
   const int E = a.E;
-  if (mt >= a.mtile_off[E]) return;
-  int lo = 0, hi = E;  // largest e with mtile_off[e] <= mt
+  const int ntiles = a.mtile_off[E] * a.nt;
+  const int chunk = (ntiles + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int L = xcd * chunk + idx;
+  if (idx >= chunk || L >= ntiles) return;
+  int lo = 0, hi = E;  // largest e with mtile_off[e] * nt <= L
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (a.mtile_off[mid] <= mt) lo = mid; else hi = mid;
+    if (a.mtile_off[mid] * a.nt <= L) lo = mid; else hi = mid;
   }
   const int e = lo;
+  const int mtiles = a.mtile_off[e + 1] - a.mtile_off[e];
+  const int local = L - a.mtile_off[e] * a.nt;
+  const int grp = local / (mtiles * a.gn), r_in = local - grp * (mtiles * a.gn);
+  const int mtl = r_in / a.gn;
+  const int ntile = grp * a.gn + (r_in - mtl * a.gn);
   const int R = a.counts[e];
   const int row0 = a.offsets[e];  // multiple of 16
-  const int m0 = (mt - a.mtile_off[e]) * BM;
+  const int m0 = mtl * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int K = a.K, F = a.F, H = a.H;
   const int KT = K / BK;
-
-  if (tid < BM) {
-    const int r = m0 + tid;
-    float sc = 0.0f;
-    if (r < R) sc = kGateUp ? a.act_scale[a.sorted[row0 + r] / a.k] : a.act_scale[row0 + r];
-    row_scale[tid] = sc;
-  }
 
   // This wavefront's share of each stage: activation tiles 2w, 2w+1 and
   // weight tiles 2w, 2w+1. Activation tiles past the expert's last row tile
@@ -190,7 +195,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   for (int s2 = 0; s2 < pre; ++s2) issue(s2);
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
-    if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
+    static_assert(kStages - 2 <= 3, "wait cases");
+    if (ahead >= 3) wait_barrier<3 * kLoadsPerWave>();
+    else if (ahead == 2) wait_barrier<2 * kLoadsPerWave>();
     else if (ahead == 1) wait_barrier<kLoadsPerWave>();
     else wait_barrier<0>();
     if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
@@ -212,6 +219,13 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   }
   // Every wavefront is done with the stage buffers before they are reused.
   wait_barrier<0>();
+  if (tid < BM) {
+    const int r = m0 + tid;
+    float sc = 0.0f;
+    if (r < R) sc = kGateUp ? a.act_scale[a.sorted[row0 + r] / a.k] : a.act_scale[row0 + r];
+    row_scale[tid] = sc;
+  }
+  __syncthreads();
 
   // Epilogue, 32 rows (row block i) at a time through this wavefront's LDS
   // slice. Lane holds column (lane & 31) of each 32x32 accumulator tile and
@@ -306,7 +320,7 @@ hipError_t launch_gemm1_tiled(const int8_t *a1, const float *sx, const int32_t *
   a.nt = F / 128; a.gn = group_n(a.nt);
   a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H; a.out = h; a.amax = amax;
   a.acc1_dbg = acc1_dbg;
-  const dim3 grid((unsigned)((int64_t)a.mt_max * a.nt));
+  const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
   return launch_kernel(gemm_tiled_kernel<true>, grid, dim3(512), st, tm, a);
 }
 
@@ -320,7 +334,7 @@ hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *
   a.mt_max = (int)((A + BM - 1) / BM + E);
   a.nt = H / 256; a.gn = group_n(a.nt);
   a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
-  const dim3 grid((unsigned)((int64_t)a.mt_max * a.nt));
+  const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
   return launch_kernel(gemm_tiled_kernel<false>, grid, dim3(512), st, tm, a);
 }
 

@@ -168,17 +168,32 @@ __device__ __forceinline__ void combine8(const float *__restrict__ y,
                                          const int32_t *__restrict__ row_of, int64_t t, int H,
                                          int k, int n0, uint16_t *__restrict__ out) {
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = row_of[t * k + j];
-    if (r < 0) continue;
-    const float w = wts[t * k + j];
-    const float *yr = y + (int64_t)r * H + n0;
-    const v4f v0 = *reinterpret_cast<const v4f *>(yr);
-    const v4f v1 = *reinterpret_cast<const v4f *>(yr + 4);
+  // Slots 8 at a time: all loads of a batch are issued before the sums,
+  // which then run in slot order over the kept slots.
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    v4f v0[8], v1[8];
+    float w[8];
+    bool kept[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc0[i] += w * v0[i];
-      acc1[i] += w * v1[i];
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int32_t r = j < k ? row_of[t * k + j] : -1;
+      kept[u] = r >= 0;
+      w[u] = kept[u] ? wts[t * k + j] : 0.0f;
+      if (kept[u]) {
+        const float *yr = y + (int64_t)r * H + n0;
+        v0[u] = *reinterpret_cast<const v4f *>(yr);
+        v1[u] = *reinterpret_cast<const v4f *>(yr + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!kept[u]) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc0[i] += w[u] * v0[u][i];
+        acc1[i] += w[u] * v1[u][i];
+      }
     }
   }
   v4i o;

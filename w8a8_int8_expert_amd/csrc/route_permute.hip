@@ -229,12 +229,14 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) blk_hist[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = tid; e < E; e += 1024) blk_hist[(int64_t)e * gridDim.x + blockIdx.x] = hist[e];
 }
 
 // One block of 1024 threads. Wave w scans the block histograms of experts
-// w, w+16, ...: blk_hist[b][e] becomes the number of assignments to e in
-// blocks before b. Then capacity, offsets and the M-tile table.
+// w, w+16, ... (stored expert-major, blk_hist[e][b], so a lane reads a
+// contiguous run of blocks): blk_hist[e][b] becomes the number of
+// assignments to e in blocks before b. Then capacity, offsets and the M-tile
+// table.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hist, int64_t nblk,
                                                     int E, int64_t capacity,
                                                     int32_t *__restrict__ counts,
@@ -246,15 +248,17 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t per_lane = (nblk + 63) / 64;
   for (int e = wave; e < E; e += 16) {
+    int32_t *row = blk_hist + (int64_t)e * nblk;
     const int64_t b0 = lane * per_lane;
     const int64_t b1 = b0 + per_lane < nblk ? b0 + per_lane : nblk;
     int s = 0;
-    for (int64_t b = b0; b < b1; ++b) s += blk_hist[b * E + e];
+#pragma unroll 8
+    for (int64_t b = b0; b < b1; ++b) s += row[b];
     const int incl = wave_incl_scan(s);
     int r = incl - s;  // exclusive prefix of this lane's first block
     for (int64_t b = b0; b < b1; ++b) {
-      const int c = blk_hist[b * E + e];
-      blk_hist[b * E + e] = r;
+      const int c = row[b];
+      row[b] = r;
       r += c;
     }
     if (lane == 63) total[e] = incl;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   __shared__ int32_t wcnt[4][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int e = tid; e < E; e += 256) {
-    running[e] = blk_base[(int64_t)blockIdx.x * E + e];
+    running[e] = blk_base[(int64_t)e * gridDim.x + blockIdx.x];
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
   }
   __syncthreads();
