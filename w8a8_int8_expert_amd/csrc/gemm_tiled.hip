@@ -66,9 +66,7 @@ static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "row scales");
 
 struct TiledArgs {
   const int8_t *act;        // fragment-tiled activations [rows/16][K/64] x 1 KB
-  const float *act_scale;   // GEMM1: sx [T] by token; GEMM2: sh [rows]
-  const int32_t *sorted;    // GEMM1: assignment of each permuted row
-  int k;
+  const float *row_scale;   // per padded row: GEMM1 sx of the row's token; GEMM2 sh
   const int32_t *counts, *offsets, *mtile_off;  // offsets: 16-aligned group starts
   const int32_t *dense_off;                     // GEMM1: dense group starts (debug rows)
   int E;
@@ -222,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   if (tid < BM) {
     const int r = m0 + tid;
     float sc = 0.0f;
-    if (r < R) sc = kGateUp ? a.act_scale[a.sorted[row0 + r] / a.k] : a.act_scale[row0 + r];
+    if (r < R) sc = a.row_scale[row0 + r];
     row_scale[tid] = sc;
   }
   __syncthreads();
@@ -308,13 +306,13 @@ int group_n(int nt) {
 
 }  // namespace
 
-hipError_t launch_gemm1_tiled(const int8_t *a1, const float *sx, const int32_t *sorted, int k,
-                              const int32_t *counts, const int32_t *offsets,
-                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
-                              uint32_t *amax, int32_t *acc1_dbg, hipStream_t st, Timing tm) {
+hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *counts,
+                              const int32_t *offsets, const int32_t *dense_off,
+                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
+                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
+                              int32_t *acc1_dbg, hipStream_t st, Timing tm) {
   TiledArgs a{};
-  a.act = a1; a.act_scale = sx; a.sorted = sorted; a.k = k; a.counts = counts;
+  a.act = a1; a.row_scale = rs; a.counts = counts;
   a.offsets = offsets; a.dense_off = dense_off; a.mtile_off = mtile_off; a.E = E;
   a.mt_max = (int)((A + BM - 1) / BM + E);
   a.nt = F / 128; a.gn = group_n(a.nt);
@@ -329,7 +327,7 @@ hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *
                               const int8_t *w_d, const float *s_d, int H, int F, int E,
                               float *y, hipStream_t st, Timing tm) {
   TiledArgs a{};
-  a.act = qh; a.act_scale = sh; a.k = 1; a.counts = counts; a.offsets = offsets;
+  a.act = qh; a.row_scale = sh; a.counts = counts; a.offsets = offsets;
   a.mtile_off = mtile_off; a.E = E;
   a.mt_max = (int)((A + BM - 1) / BM + E);
   a.nt = H / 256; a.gn = group_n(a.nt);

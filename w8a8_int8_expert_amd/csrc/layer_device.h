@@ -42,14 +42,53 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Renormalised softmax over the chosen k, from slot j's key on lane j:
+// exp(l_j - l_0) / sum over the k slots, summed in slot order.
+__device__ __forceinline__ float topk_weight(uint64_t mine, int k) {
+  const int lane = threadIdx.x & 63;
+  const float l = key_logit(mine);
+  const float m = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(l), 0));
+  const float ex = lane < k ? expf(l - m) : 0.0f;
+  float den = 0.0f;
+  for (int j = 0; j < k; ++j)
+    den += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ex), j));
+  return ex / den;
+}
+
 // One wavefront routes one token: experts lane + 64*i (i < NV) are held by
-// the lane, k rounds of a wave-wide key maximum pick the top k in order.
-// Softmax weights renormalised over the chosen k: exp(l_j - l_0) / sum.
+// the lane. Up to 64 experts (NV = 1): the wavefront's keys go through its
+// 64-entry LDS slot `keys`, every lane counts the keys above its own (keys
+// are distinct), which is its expert's rank, and one permute moves the key of
+// rank j to lane j. More experts: k rounds of a wave-wide key maximum pick
+// the top k in order.
 // Lane j < k returns slot j's expert and weight; other lanes return -1.
 template <int NV>
 __device__ __forceinline__ int route_token_wave(const float *__restrict__ row, int E, int k,
-                                                float *w_out) {
+                                                float *w_out, uint64_t *keys) {
   const int lane = threadIdx.x & 63;
+  if (NV == 1) {
+    const uint64_t key = lane < E ? route_key(row[lane], lane) : 0ull;
+    keys[lane] = key;
+    // A wavefront's LDS accesses complete in issue order; keep the compiler
+    // from moving the reads above the write.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; j += 2) {
+      const ulonglong2 kj = *reinterpret_cast<const ulonglong2 *>(keys + j);
+      rank += (kj.x > key ? 1 : 0) + (kj.y > key ? 1 : 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // Lanes past E hold key 0 and share rank E >= k; their pushes land on
+    // lanes that return -1.
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)(uint32_t)(key >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(rank * 4, (int)(uint32_t)key);
+    const uint64_t mine = ((uint64_t)hi << 32) | lo;
+    *w_out = topk_weight(mine, k);
+    return lane < k ? key_expert(mine) : -1;
+  }
   uint64_t key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -68,11 +107,7 @@ __device__ __forceinline__ int route_token_wave(const float *__restrict__ row, i
       if (lane + 64 * i == e) key[i] = 0ull;
     if (lane == j) mine = b;
   }
-  const float l = key_logit(mine);
-  const float m = __shfl(l, 0, 64);
-  const float ex = lane < k ? expf(l - m) : 0.0f;
-  const float den = wave_sum(ex);
-  *w_out = ex / den;
+  *w_out = topk_weight(mine, k);
   return lane < k ? key_expert(mine) : -1;
 }
 

@@ -90,7 +90,7 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // a 16-row boundary, so P <= A + 15*min(E, A) rows for A = T*k assignments.
 struct FwdLayout {
   size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, a1,
-      h, amax, qh, sh, y, total;
+      rs, h, amax, qh, sh, y, total;
   int64_t nblk;  // routing blocks
   int64_t P;     // padded permuted rows (upper bound)
 };
@@ -122,9 +122,9 @@ hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int
                           int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
                             float *sx, hipStream_t st, Timing tm);
-hipError_t launch_gather_tiles(const int8_t *qx, const int32_t *sorted, int k,
+hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
-                               hipStream_t st, Timing tm);
+                               float *rs, hipStream_t st, Timing tm);
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
                           int64_t P, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm);
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
@@ -135,15 +135,15 @@ hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
                                int F, int E, float *y, hipStream_t st, Timing tm);
-hipError_t launch_gemm1_tiled(const int8_t *a1, const float *sx, const int32_t *sorted, int k,
-                              const int32_t *counts, const int32_t *poffsets,
-                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
-                              uint32_t *amax, int32_t *acc1_dbg, hipStream_t st, Timing tm);
+hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *counts,
+                              const int32_t *offsets, const int32_t *dense_off,
+                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
+                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
+                              int32_t *acc1_dbg, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
-                              const int32_t *poffsets, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_d, const float *s_d, int H, int F, int E,
-                              float *y, hipStream_t st, Timing tm);
+                              const int32_t *offsets, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
+                              hipStream_t st, Timing tm);
 hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm);
 // stage outputs in dense rows (debug only)

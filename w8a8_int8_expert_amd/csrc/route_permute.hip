@@ -116,6 +116,8 @@ __device__ __forceinline__ int finish_counts(int total, int E, int64_t capacity,
 }
 
 // ------------------------------------------------------------- small A path
+constexpr int kSmallQuantTokens = 4;  // tokens quantised per block (blocks 1..)
+
 template <int NV>
 __global__ __launch_bounds__(1024) void prologue_small_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
@@ -127,10 +129,14 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     int8_t *__restrict__ qx, float *__restrict__ sx, uint32_t *__restrict__ amax) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
-    const int64_t t = (int64_t)(blockIdx.x - 1) * 16 + wave;
-    if (t < T) quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t);
+    // Four tokens per block: the quantisation is spread over many compute
+    // units instead of stacking 16 wavefronts' arithmetic on one.
+    const int64_t t = (int64_t)(blockIdx.x - 1) * kSmallQuantTokens + wave;
+    if (wave < kSmallQuantTokens && t < T)
+      quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t);
     return;
   }
+  __shared__ uint64_t wave_keys[16][64];
   __shared__ int32_t hist[kMaxExperts];
   __shared__ int32_t run[kMaxExperts];
   __shared__ int32_t lds_ids[kSmallA];
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     int e;
     float w;
     if (logits) {
-      e = route_token_wave<NV>(logits + (int64_t)t * E, E, k, &w);
+      e = route_token_wave<NV>(logits + (int64_t)t * E, E, k, &w, wave_keys[wave]);
     } else {
       e = lane < k ? ids_in[t * k + lane] : -1;
       w = lane < k ? w_in[t * k + lane] : 0.0f;
@@ -195,6 +201,7 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax,
     int32_t *__restrict__ sorted, int64_t P) {
+  __shared__ uint64_t wave_keys[16][64];
   __shared__ int32_t hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) hist[e] = 0;
@@ -217,7 +224,7 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     int e;
     float w;
     if (logits) {
-      e = route_token_wave<NV>(logits + t * E, E, k, &w);
+      e = route_token_wave<NV>(logits + t * E, E, k, &w, wave_keys[wave]);
     } else {
       e = lane < k ? ids_in[t * k + lane] : -1;
       w = lane < k ? w_in[t * k + lane] : 0.0f;
@@ -339,7 +346,7 @@ hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, con
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
                                  const uint16_t *x, const float *inv_s, int H, int8_t *qx,
                                  float *sx, uint32_t *amax, hipStream_t st, Timing tm) {
-  const dim3 grid(1 + (unsigned)((T + 15) / 16)), block(1024);
+  const dim3 grid(1 + (unsigned)((T + kSmallQuantTokens - 1) / kSmallQuantTokens)), block(1024);
 #define MOE_PROLOGUE(NV)                                                                     \
   return launch_kernel(prologue_small_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, \
                        E, k, capacity, ids, wts, counts, offsets, poffsets, mtile_off, sorted,  \
