@@ -33,7 +33,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
 # Steps between two steps that carry stage events (decode; prefill steps all do).
 EVENT_STRIDE = 10
 STAGE_INDEX = {s: i for i, s in enumerate(
-    ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine"))}
+    ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine", "router"))}
 # Sources of the kernels whose counter-measured traffic may be reused.
 KERNEL_SOURCES = {
     "gemm1_stream": ["w8a8_int8_expert_amd/csrc/gemm_stream.hip",
@@ -132,7 +132,7 @@ def time_workload(gl: GpuLayer, wl, inputs, steps, warmup, hip, timed_stages, st
     torch.cuda.synchronize()
     counts_h = counts.cpu().numpy()
 
-    ev_arr = (ctypes.c_void_p * 16)()
+    ev_arr = (ctypes.c_void_p * 18)()
     tdbg = m.moe_w8a8_debug()
     tdbg.stage_events = ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p))
     for _ in range(warmup):
@@ -166,6 +166,37 @@ def time_workload(gl: GpuLayer, wl, inputs, steps, warmup, hip, timed_stages, st
             hip.destroy(a)
             hip.destroy(b)
     return dict(seconds=t1 - t0, stage_ms=stage_ms, counts=counts_h, out=out)
+
+
+def time_router(gl: GpuLayer, wl, inputs, w_router, steps, warmup):
+    """Router-projection mode: the whole layer routed from x and the bf16
+    router matrix (ms per step), and the projection entry point alone."""
+    torch = gl.torch
+    dev = torch.device("cuda")
+    x = torch.from_numpy(inputs.x.view("int16")).to(dev).view(torch.bfloat16)
+    out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
+    lg = torch.empty(wl.T, wl.E, dtype=torch.float32, device=dev)
+    gl.g.set_router(torch.from_numpy(w_router.view("int16")).to(dev).view(torch.bfloat16))
+    gl.g.workspace(wl.T)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    fwd_s = timed(lambda: gl.g.forward(x, None, None, None, wl.capacity_factor, out=out))
+    lg_s = timed(lambda: gl.g.router_logits(x, out=lg))
+    gl.g.set_router(None)
+    flops = 2.0 * wl.T * wl.E * wl.H
+    return {"forward_ms_per_step": round(fwd_s * 1e3, 5),
+            "forward_tokens_per_s": round(wl.T / fwd_s, 1),
+            "logits_us": round(lg_s * 1e6, 2),
+            "logits_TFLOPs": round(flops / lg_s / 1e12, 2)}
 
 
 def launched_stages(wl):
@@ -227,6 +258,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -319,6 +351,15 @@ def main():
             "stage_us": {k: round(v * 1e3, 1) for k, v in pr["stage_ms"].items()},
         }
         del pr
+    if wl.name == "decode" and not args.no_router:
+        log("timing router-projection mode")
+        w_router = synth.make_router(layer_wl)
+        rp = {"decode": time_router(gl, wl, inputs, w_router, args.steps, args.warmup)}
+        if not args.no_prefill:
+            pwl = synth.workload("prefill")
+            rp["prefill"] = time_router(gl, pwl, synth.make_inputs(pwl, layer), w_router,
+                                        args.prefill_steps, 3)
+        res["router_projection"] = rp
     res["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle for %.0f s" % args.cpu_seconds)

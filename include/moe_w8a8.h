@@ -3,8 +3,10 @@
  * for AMD Instinct MI355X (gfx950).
  *
  * The layer (one call to moe_w8a8_forward) computes, for T tokens x[T][H]:
- *   1. route    top-k experts per token from router logits, ties to the lower
- *               expert index, softmax weights renormalised over the chosen k
+ *   1. route    top-k experts per token from router logits (given, or
+ *               projected from x by the bf16 router matrix in the same call),
+ *               ties to the lower expert index, softmax weights renormalised
+ *               over the chosen k
  *               ("超大规模模型推理的Day0适配实践" §四: the fused MoE operator's
  *               top-k must equal the reference, tie-break included);
  *   2. permute  group the T*k (token, slot) assignments expert by expert,
@@ -83,6 +85,10 @@ typedef struct {
  *   s_down    : fp32 [E][H]   dequantisation scale per output channel.
  *   smooth    : fp32 [H]      SmoothQuant scale s_j.
  *   inv_smooth: fp32 [H]      1/s_j rounded to fp32 (what forward multiplies by).
+ *   w_router  : bf16 [E][H]   router projection, row e for expert e, or NULL.
+ *               Not quantised ("MiniMax-M3 W8A8 inference on K100AI" §6.1:
+ *               the layers at the routing stay in 16-bit floating point) and
+ *               not written by moe_w8a8_calibrate.
  * Code of W'[n][k] is q with W' ~= q * scale[n]; codes lie in [-127, 127]. */
 typedef struct {
   int8_t *w_gate_up;
@@ -91,6 +97,7 @@ typedef struct {
   float *s_down;
   float *smooth;
   float *inv_smooth;
+  uint16_t *w_router;
 } moe_w8a8_weights;
 
 /* Optional per-stage outputs of moe_w8a8_forward for checking; every pointer
@@ -125,16 +132,20 @@ typedef struct {
    * beyond), 1 = streaming, 2 = tiled. Any other value: MOE_W8A8_ERR_INVALID.
    * Every choice computes the same result. */
   int32_t gemm_path;
-  /* NULL, or an array of 16 hipEvent_t (as void*) to time the layer's
+  /* NULL, or an array of 18 hipEvent_t (as void*) to time the layer's
    * kernels on its own stream: entries 2s and 2s+1 are stamped with the
    * start and the end of the execution of the launch that performs stage s
    * (s = 0 route, 1 scan, 2 scatter, 3 activation quant, 4 GEMM1, 5 requant,
-   * 6 GEMM2, 7 combine), by that launch's own dispatch (hipExtLaunchKernel),
-   * so timing inserts nothing between the kernels. Stages fused into one
-   * launch are timed by the pair of the first of them: for T*k <= 2048,
-   * stages 0-3 are one launch and pairs 1-3 are left untouched. NULL entries
-   * are skipped. */
+   * 6 GEMM2, 7 combine, 8 router projection), by that launch's own dispatch
+   * (hipExtLaunchKernel), so timing inserts nothing between the kernels.
+   * Stages fused into one launch are timed by the pair of the first of them:
+   * for T*k <= 2048, stages 0-3 are one launch and pairs 1-3 are left
+   * untouched. NULL entries are skipped. */
   void **stage_events;
+  /* fp32 [T][E]: the router logits the routing used (the projection's
+   * result in router-projection mode, a copy of router_logits otherwise;
+   * untouched in pre-routed mode). */
+  float *router_logits;
 } moe_w8a8_debug;
 
 /* Bytes of device workspace that moe_w8a8_forward needs for T tokens, and
@@ -169,11 +180,16 @@ int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
 
 /* Forward pass of the layer for T tokens (steps 1-6 above).
  *   x           bf16 [T][H] input tokens.
- *   router_logits fp32 [T][E], or NULL for pre-routed mode, in which case
- *   topk_ids    int32 [T][k] and topk_w fp32 [T][k] give the assignments and
- *               their weights (ids outside [0, E) are treated as dropped; the
- *               weights are used as given). Exactly one of router_logits and
- *               (topk_ids, topk_w) must be non-NULL.
+ *   Routing input, one of three modes:
+ *   router_logits fp32 [T][E] given; or
+ *   topk_ids    int32 [T][k] and topk_w fp32 [T][k] (pre-routed mode): the
+ *               assignments and their weights (ids outside [0, E) are treated
+ *               as dropped; the weights are used as given); or
+ *   neither (router-projection mode): the logits are x . w_router^T from
+ *               weights->w_router, as moe_w8a8_router_logits computes them,
+ *               and the routing of step 1 is taken on them.
+ *   Giving router_logits together with topk_ids or topk_w, only one of
+ *   topk_ids and topk_w, or neither with w_router NULL is an error.
  *   capacity_factor  > 0: each expert keeps at most
  *               C = ceil(capacity_factor * T * k / E) assignments (evaluated
  *               in fp64), the first C in (token, slot) order; dropped slots
@@ -186,7 +202,7 @@ int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
  *   debug       NULL, or a host struct of optional device outputs (above).
  * T == 0 is a successful no-op whatever the other pointers are (empty
  * tensors may carry NULL addresses). Errors: MOE_W8A8_ERR_INVALID (NULL required
- * pointer, T < 0, T*k >= 2^31, both or neither routing inputs),
+ * pointer, T < 0, T*k >= 2^31, routing inputs as above),
  * MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
 int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
                      const uint16_t *x, int64_t T,
@@ -196,6 +212,25 @@ int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
                      uint16_t *out,
                      void *workspace, size_t workspace_bytes,
                      const moe_w8a8_debug *debug, void *stream);
+
+/* Router projection ("超大规模模型推理的Day0适配实践" §四: the gate belongs to
+ * the fused MoE operator and the top-k it feeds must be exact; "MiniMax-M3
+ * W8A8 inference on K100AI" §6.1: the routing layers stay in 16-bit float):
+ *   logits[t][e] = sum_j x[t][j] * w_router[e][j]
+ * with x bf16 [T][H], w_router bf16 [E][H] (device), accumulated in fp32 on
+ * the bf16 matrix instructions (each product exact), written to logits fp32
+ * [T][E] (device). The order of the sum depends on H only, never on T: H
+ * is cut into parts of 512 channels, each part into 4 runs of 128 summed
+ * ((r0 + r1) + r2) + r3, and the parts are added in order; within a run the
+ * matrix instructions accumulate 16 channels at a time. A token's logits are
+ * therefore the same whatever batch it comes in.
+ * Workspace: at least moe_w8a8_workspace_size(dims, T) bytes (the per-part
+ * sums; none is needed when H <= 512).
+ * T == 0 is a successful no-op. Errors: MOE_W8A8_ERR_INVALID (NULL pointer,
+ * T < 0), MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
+int moe_w8a8_router_logits(const moe_w8a8_dims *dims, const uint16_t *x, int64_t T,
+                           const uint16_t *w_router, float *logits,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a return code (never NULL). */
 const char *moe_w8a8_strerror(int code);

@@ -52,6 +52,7 @@ def _load():
         "oracle_calibrate": (ctypes.c_int, [_I32, _I32, _I32, _F32, _P, _I64, _P, _P, _P,
                                             _P, _P, _P, _P, _P, _P, _P]),
         "oracle_route": (None, [_I64, _I32, _I32, _P, _P, _P]),
+        "oracle_router_logits": (None, [_I64, _I32, _I32, _P, _P, _P]),
         "oracle_capacity": (_I64, [_F32, _I64, _I32, _I32]),
         "oracle_permute": (_I64, [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P]),
         "oracle_act_quant": (None, [_I64, _I32, _P, _P, _P, _P]),
@@ -134,6 +135,19 @@ def route(logits, k: int):
     w = np.empty((T, k), np.float32)
     _load().oracle_route(T, E, k, _ptr(lg), _ptr(ids), _ptr(w))
     return ids, w
+
+
+def router_logits(x_bf16, w_router_bf16):
+    """Router projection in fp64; x uint16 (bf16) [T][H], w uint16 (bf16)
+    [E][H] -> float64 [T][E]."""
+    x = _c(x_bf16, np.uint16)
+    w = _c(w_router_bf16, np.uint16)
+    T, H = x.shape
+    E = w.shape[0]
+    assert w.shape[1] == H
+    out = np.empty((T, E), np.float64)
+    _load().oracle_router_logits(T, H, E, _ptr(x), _ptr(w), _ptr(out))
+    return out
 
 
 def capacity(cf: float, T: int, k: int, E: int) -> int:

@@ -214,6 +214,26 @@ void oracle_route(int64_t T, int32_t E, int32_t k, const float *logits,
   }
 }
 
+/* Router projection. [Day0 §四]: the gate (the router's linear map) is the
+ * first operator of the fused MoE operator; [K100AI §6.1]: the layers at the
+ * routing stay in 16-bit floating point, not INT8. Reading: x bf16 [T][H],
+ * router matrix bf16 [E][H]; the logits are the exact dot products
+ *   logits[t][e] = sum_j x[t][j] * w[e][j],
+ * evaluated in fp64 (each product of two bf16 values is exact; the sum of H
+ * of them carries a relative error of about H * 2^-53). */
+void oracle_router_logits(int64_t T, int32_t H, int32_t E, const uint16_t *x,
+                          const uint16_t *w, double *logits) {
+  #pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < H; ++j)
+        acc += (double)bf16_bits_to_f32(x[t * H + j]) * (double)bf16_bits_to_f32(w[(int64_t)e * H + j]);
+      logits[t * E + e] = acc;
+    }
+  }
+}
+
 /* --------------------------------------------------------------- permute */
 
 /* Expert capacity. [Day0 §二.2]: the capacity factor bounds the tokens an

@@ -134,6 +134,15 @@ def make_layer(wl: Workload) -> Layer:
     return Layer(w_gate, w_up, w_down, calib, channels)
 
 
+def make_router(wl: Workload) -> np.ndarray:
+    """bf16 [E][H] router matrix, N(0, 1/H) rounded to bf16, from the fifth
+    stream of the layer seed (the first four make the layer)."""
+    r = _streams(wl.layer_seed, 5)[4]
+    w = r.standard_normal((wl.E, wl.H), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(wl.H))
+    return f32_to_bf16_bits(w)
+
+
 def make_inputs(wl: Workload, layer: Layer, T: Optional[int] = None) -> Inputs:
     T = wl.T if T is None else T
     r_x, r_route, r_scale = _streams(wl.input_seed, 3)

@@ -54,8 +54,10 @@ def tensor_bits(t) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, want=("all",)):
-    """Run moe_w8a8_forward with every debug buffer; returns host arrays."""
+def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, project=False):
+    """Run moe_w8a8_forward with every debug buffer; returns host arrays.
+    project=True routes by the layer's router matrix (set_router) instead of
+    the inputs' logits; the logits it used come back as "router_logits"."""
     import torch
     import w8a8_int8_expert_amd as m
     dev = layer_gpu.device
@@ -63,7 +65,8 @@ def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, want=("all",
     H, F, E = layer_gpu.d.hidden, layer_gpu.d.ffn, layer_gpu.d.num_experts
     A = max(T * k, 1)
     x = bf16_tensor(inputs.x, dev)
-    logits = torch.from_numpy(inputs.logits).to(dev) if inputs.logits is not None else None
+    logits = torch.from_numpy(inputs.logits).to(dev) \
+        if inputs.logits is not None and not project else None
     ids = torch.from_numpy(inputs.ids).to(dev) if inputs.ids is not None else None
     w = torch.from_numpy(inputs.w).to(dev) if inputs.w is not None else None
     dbgt = dict(
@@ -79,9 +82,12 @@ def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, want=("all",
         h=torch.empty(A * F, dtype=torch.float32, device=dev),
         qh=torch.empty(A * F, dtype=torch.int8, device=dev),
         sh=torch.empty(A, dtype=torch.float32, device=dev),
-        y=torch.empty(A * H, dtype=torch.float32, device=dev))
-    dbg = m.moe_w8a8_debug(*(dbgt[f].data_ptr() for f, _ in m.moe_w8a8_debug._fields_[:-2]),
-                           gemm_path, None)
+        y=torch.empty(A * H, dtype=torch.float32, device=dev),
+        router_logits=torch.empty(max(T, 1) * E, dtype=torch.float32, device=dev))
+    dbg = m.moe_w8a8_debug()
+    for name, t in dbgt.items():
+        setattr(dbg, name, t.data_ptr())
+    dbg.gemm_path = gemm_path
     out = layer_gpu.forward(x, router_logits=logits, topk_ids=ids, topk_w=w,
                             capacity_factor=capacity_factor, debug=dbg)
     torch.cuda.synchronize()
@@ -94,7 +100,8 @@ def run_gpu(layer_gpu, inputs, k, capacity_factor=0.0, gemm_path=0, want=("all",
         counts=dbgt["expert_counts"].cpu().numpy(), offsets=offs, kept=kept,
         sorted=dbgt["sorted_assign"].cpu().numpy()[:kept],
         row_of=dbgt["row_of"].cpu().numpy()[: T * k].reshape(T, k),
-        qx=dbgt["qx"].cpu().numpy()[: T * H].reshape(T, H), sx=dbgt["sx"].cpu().numpy()[:T])
+        qx=dbgt["qx"].cpu().numpy()[: T * H].reshape(T, H), sx=dbgt["sx"].cpu().numpy()[:T],
+        router_logits=dbgt["router_logits"].cpu().numpy()[: T * E].reshape(T, E))
     return res
 
 

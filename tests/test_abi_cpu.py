@@ -76,7 +76,7 @@ def test_forward_validation(lib):
     assert _fwd(m.dims(0, 512, 8, 2)) == m.MOE_W8A8_ERR_INVALID
     assert _fwd(d, T=-1) == m.MOE_W8A8_ERR_INVALID
     assert _fwd(d, logits=FAKE, ids=FAKE, w=FAKE) == m.MOE_W8A8_ERR_INVALID  # both
-    assert _fwd(d, logits=None) == m.MOE_W8A8_ERR_INVALID                    # neither
+    assert _fwd(d, logits=None) == m.MOE_W8A8_ERR_INVALID       # neither, no router matrix
     assert _fwd(d, logits=None, ids=FAKE, w=None) == m.MOE_W8A8_ERR_INVALID  # half pre-routed
     assert _fwd(d, x=None) == m.MOE_W8A8_ERR_INVALID
     assert _fwd(d, out=None) == m.MOE_W8A8_ERR_INVALID
@@ -96,6 +96,21 @@ def test_forward_validation(lib):
     assert _fwd(d, T=1 << 30, ws_bytes=1) == m.MOE_W8A8_ERR_INVALID         # T*k >= 2^31
     # T == 0 is a successful no-op (nothing is enqueued)
     assert _fwd(d, T=0, ws=None, ws_bytes=0, x=None, out=None) == m.MOE_W8A8_OK
+
+
+def test_router_logits_validation(lib):
+    d = m.dims(1024, 512, 8, 2)   # H > 512: the per-part sums need the workspace
+    def rl(d=d, x=FAKE, T=4, w=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        return m.moe_w8a8_router_logits(d, x, T, w, out, ws, ws_bytes, stream=0)
+    assert rl(x=None) == m.MOE_W8A8_ERR_INVALID
+    assert rl(w=None) == m.MOE_W8A8_ERR_INVALID
+    assert rl(out=None) == m.MOE_W8A8_ERR_INVALID
+    assert rl(T=-1) == m.MOE_W8A8_ERR_INVALID
+    assert rl(d=m.dims(1024, 512, 8, 9)) == m.MOE_W8A8_ERR_INVALID         # k > E
+    assert rl(d=m.dims(1000, 512, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED     # H % 256
+    assert rl(ws=None) == m.MOE_W8A8_ERR_WORKSPACE
+    assert rl(ws_bytes=m.moe_w8a8_workspace_size(d, 4) - 1) == m.MOE_W8A8_ERR_WORKSPACE
+    assert rl(T=0, x=None, w=None, out=None, ws=None, ws_bytes=0) == m.MOE_W8A8_OK
 
 
 def test_calibrate_validation(lib):

@@ -160,6 +160,49 @@ def test_routing_all_equal():
 
 # ------------------------------------------------------------------ permute
 
+# ------------------------------------------------------- router projection
+
+def test_router_logits_bruteforce():
+    """fp64 dot products against Python's exact rational sum of the bf16
+    products (a transposed operand or a dropped term fails)."""
+    rng = np.random.default_rng(11)
+    T, E, H = 3, 5, 24
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    w = f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(0.1))
+    xf, wf = bf16_bits_to_f32(x), bf16_bits_to_f32(w)
+    got = oracle.router_logits(x, w)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(xf[t, j])) * Fraction(float(wf[e, j])) for j in range(H))
+            assert abs(got[t, e] - float(exact)) <= 1e-15 * max(1.0, abs(float(exact)))
+
+
+def test_router_logits_one_hot_and_sign():
+    """x = unit vector j selects column j of the router matrix exactly; the
+    map is odd in x."""
+    rng = np.random.default_rng(12)
+    E, H = 7, 64
+    w = f32_to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32))
+    eye = f32_to_bf16_bits(np.eye(H, dtype=np.float32))
+    got = oracle.router_logits(eye, w)
+    assert np.array_equal(got, bf16_bits_to_f32(w).T.astype(np.float64))
+    x = f32_to_bf16_bits(rng.standard_normal((4, H), dtype=np.float32))
+    neg = f32_to_bf16_bits(-bf16_bits_to_f32(x))
+    assert np.array_equal(oracle.router_logits(neg, w), -oracle.router_logits(x, w))
+
+
+def test_router_logits_integer_closed_form():
+    """Small integers are exact in bf16 and fp64: x[t][j] = t + 1, w[e][j] =
+    (j % 5) - e gives logits (t + 1) * sum_j ((j % 5) - e)."""
+    T, E, H = 4, 3, 40
+    xf = np.repeat(np.arange(1, T + 1, dtype=np.float32)[:, None], H, axis=1)
+    wf = np.array([[(j % 5) - e for j in range(H)] for e in range(E)], np.float32)
+    got = oracle.router_logits(f32_to_bf16_bits(xf), f32_to_bf16_bits(wf))
+    want = np.array([[(t + 1) * sum((j % 5) - e for j in range(H)) for e in range(E)]
+                     for t in range(T)], np.float64)
+    assert np.array_equal(got, want)
+
+
 def test_permute_golden(golden_dir):
     g = _load(golden_dir, "permute_capacity.json")
     ids = np.array(g["ids"], np.int32)

@@ -33,20 +33,21 @@ class moe_w8a8_dims(ctypes.Structure):
 
 class moe_w8a8_weights(ctypes.Structure):
     _fields_ = [("w_gate_up", _P), ("w_down", _P), ("s_gate_up", _P), ("s_down", _P),
-                ("smooth", _P), ("inv_smooth", _P)]
+                ("smooth", _P), ("inv_smooth", _P), ("w_router", _P)]
 
 
 class moe_w8a8_debug(ctypes.Structure):
     _fields_ = [("topk_ids", _P), ("topk_w", _P), ("expert_counts", _P), ("expert_offsets", _P),
                 ("sorted_assign", _P), ("row_of", _P), ("qx", _P), ("sx", _P), ("acc1", _P),
                 ("h", _P), ("qh", _P), ("sh", _P), ("y", _P), ("gemm_path", ctypes.c_int32),
-                ("stage_events", ctypes.POINTER(_P))]
+                ("stage_events", ctypes.POINTER(_P)), ("router_logits", _P)]
 
-STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine")
+STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine",
+          "router")
 
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_forward",
-           "moe_w8a8_strerror")
+           "moe_w8a8_router_logits", "moe_w8a8_strerror")
 
 _lib = None
 
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_w8a8_forward.restype = ctypes.c_int
     lib.moe_w8a8_forward.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_float, _P,
                                      _P, ctypes.c_size_t, G, _P]
+    lib.moe_w8a8_router_logits.restype = ctypes.c_int
+    lib.moe_w8a8_router_logits.argtypes = [D, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t,
+                                           _P]
     lib.moe_w8a8_strerror.restype = ctypes.c_char_p
     lib.moe_w8a8_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -123,6 +127,13 @@ def moe_w8a8_forward(d, weights: moe_w8a8_weights, x, T, router_logits, topk_ids
         _stream(stream)))
 
 
+def moe_w8a8_router_logits(d, x, T, w_router, logits, workspace, workspace_bytes,
+                           stream=None) -> int:
+    return int(load_library().moe_w8a8_router_logits(
+        ctypes.byref(d), _ptr(x), int(T), _ptr(w_router), _ptr(logits), _ptr(workspace),
+        int(workspace_bytes), _stream(stream)))
+
+
 class MoEW8A8Error(RuntimeError):
     pass
 
@@ -150,8 +161,35 @@ class MoEW8A8:
         self.inv_smooth = torch.empty(H, dtype=torch.float32, **kw)
         self.weights = moe_w8a8_weights(*(t.data_ptr() for t in (
             self.w_gate_up, self.w_down, self.s_gate_up, self.s_down, self.smooth,
-            self.inv_smooth)))
+            self.inv_smooth)), None)
+        self.w_router = None
         self._ws = None
+
+    def set_router(self, w_router):
+        """bf16 [E][H] router matrix (kept on the device; copied), or None."""
+        import torch
+        if w_router is None:
+            self.w_router = None
+            self.weights.w_router = None
+            return
+        H, E = self.d.hidden, self.d.num_experts
+        if tuple(w_router.shape) != (E, H) or w_router.dtype != torch.bfloat16:
+            raise MoEW8A8Error("router matrix must be bf16 [E][H]")
+        self.w_router = w_router.to(self.device).contiguous().clone()
+        self.weights.w_router = self.w_router.data_ptr()
+
+    def router_logits(self, x, out=None):
+        """fp32 [T][E] logits x . w_router^T (needs set_router)."""
+        import torch
+        if self.w_router is None:
+            raise MoEW8A8Error("no router matrix (set_router)")
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty(T, self.d.num_experts, dtype=torch.float32, device=self.device)
+        ws = self.workspace(T)
+        _check(moe_w8a8_router_logits(self.d, x, T, self.w_router, out, ws, ws.numel()),
+               "moe_w8a8_router_logits")
+        return out
 
     def workspace(self, T: int):
         import torch
@@ -170,7 +208,8 @@ class MoEW8A8:
 
     def forward(self, x, router_logits=None, topk_ids=None, topk_w=None,
                 capacity_factor: float = 0.0, out=None, debug: Optional[moe_w8a8_debug] = None):
-        """x: bf16 [T][H] -> bf16 [T][H]."""
+        """x: bf16 [T][H] -> bf16 [T][H]. Routing: router_logits, or (topk_ids,
+        topk_w), or neither with a router matrix set (set_router)."""
         import torch
         T = x.shape[0]
         if out is None:

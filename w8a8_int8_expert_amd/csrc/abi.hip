@@ -52,6 +52,7 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   L.qh = take(P16 * F);
   L.sh = take(sizeof(float) * (size_t)L.P);
   L.y = take(sizeof(float) * (size_t)L.P * H);
+  L.rpart = take(sizeof(float) * (size_t)router_parts(H) * (size_t)T * (size_t)E);
   L.total = o;
   return L;
 }
@@ -86,6 +87,29 @@ extern "C" const char *moe_w8a8_strerror(int code) {
     if ((expr) != hipSuccess) return MOE_W8A8_ERR_HIP;   \
   } while (0)
 
+extern "C" int moe_w8a8_router_logits(const moe_w8a8_dims *d, const uint16_t *x, int64_t T,
+                                      const uint16_t *w_router, float *logits, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (!dims_valid(d) || T < 0) return MOE_W8A8_ERR_INVALID;
+  if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
+  if (!x || !w_router || !logits) return MOE_W8A8_ERR_INVALID;
+  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
+  const int H = d->hidden, E = d->num_experts;
+  const int parts = router_parts(H);
+  hipStream_t st = (hipStream_t)stream;
+  if (parts == 1) {
+    MOE_CHECK(launch_router_proj(x, w_router, T, E, H, logits, st, Timing{}));
+    return MOE_W8A8_OK;
+  }
+  const FwdLayout L = fwd_layout(T, H, d->ffn, E, d->top_k);
+  if (!workspace || workspace_bytes < L.total) return MOE_W8A8_ERR_WORKSPACE;
+  float *rpart = (float *)((char *)workspace + L.rpart);
+  MOE_CHECK(launch_router_proj(x, w_router, T, E, H, rpart, st, Timing{}));
+  MOE_CHECK(launch_router_sum(rpart, parts, T, E, logits, st));
+  return MOE_W8A8_OK;
+}
+
 extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uint16_t *calib_x,
                                   int64_t n_calib, const float *w_gate, const float *w_up,
                                   const float *w_down, const moe_w8a8_weights *out,
@@ -119,7 +143,9 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
   const bool routed = router_logits != nullptr;
   const bool pre = topk_ids != nullptr || topk_w != nullptr;
-  if (routed == pre || (pre && (!topk_ids || !topk_w))) return MOE_W8A8_ERR_INVALID;
+  const bool project = !routed && !pre;
+  if ((routed && pre) || (pre && (!topk_ids || !topk_w)) || (project && !wt->w_router))
+    return MOE_W8A8_ERR_INVALID;
   if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
   if (!x || !out || !wt->w_gate_up || !wt->w_down || !wt->s_gate_up || !wt->s_down ||
       !wt->inv_smooth)
@@ -178,15 +204,22 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
     }
     return t;
   };
-  enum { kRoute, kScan, kScatter, kActQ, kG1, kReq, kG2, kComb };
+  enum { kRoute, kScan, kScatter, kActQ, kG1, kReq, kG2, kComb, kRouter };
+
+  LogitPlanes lp{router_logits, 1, 0};
+  if (project) {
+    float *rpart = (float *)(ws + L.rpart);
+    MOE_CHECK(launch_router_proj(x, wt->w_router, T, E, H, rpart, st, tm(kRouter)));
+    lp = LogitPlanes{rpart, router_parts(H), T * (int64_t)E};
+  }
 
   if (small) {
-    MOE_CHECK(launch_prologue_small(router_logits, topk_ids, topk_w, (int)T, E, k, capacity, ids,
+    MOE_CHECK(launch_prologue_small(lp, topk_ids, topk_w, (int)T, E, k, capacity, ids,
                                     wts, counts, offsets, poffsets, mtile_off, sorted, row_of,
                                     (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, st,
                                     tm(kRoute)));
   } else {
-    MOE_CHECK(launch_route_hist(router_logits, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
+    MOE_CHECK(launch_route_hist(lp, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
                                 amax, sorted, L.P, st, tm(kRoute)));
     MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, poffsets, mtile_off, st,
                           tm(kScan)));
@@ -229,6 +262,12 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
     MOE_CHECK(cp(dbg->expert_offsets, offsets, sizeof(int32_t) * (E + 1)));
     MOE_CHECK(cp(dbg->qx, qx, (size_t)T * H));
     MOE_CHECK(cp(dbg->sx, sx, sizeof(float) * T));
+    if (dbg->router_logits) {
+      if (project)
+        MOE_CHECK(launch_router_sum(lp.p, lp.nparts, T, E, dbg->router_logits, st));
+      else if (routed)
+        MOE_CHECK(cp(dbg->router_logits, router_logits, sizeof(float) * T * E));
+    }
     if (dbg->sorted_assign || dbg->h || dbg->qh || dbg->sh || dbg->y)
       MOE_CHECK(launch_debug_rows(offsets, poffsets, E, A, sorted, h, qh, sh, y, F, H,
                                   dbg->sorted_assign, dbg->h, dbg->qh, dbg->sh, dbg->y, st));

@@ -55,19 +55,26 @@ __device__ __forceinline__ float topk_weight(uint64_t mine, int k) {
   return ex / den;
 }
 
-// One wavefront routes one token: experts lane + 64*i (i < NV) are held by
+// One wavefront routes token t: experts lane + 64*i (i < NV) are held by
 // the lane. Up to 64 experts (NV = 1): the wavefront's keys go through its
 // 64-entry LDS slot `keys`, every lane counts the keys above its own (keys
 // are distinct), which is its expert's rank, and one permute moves the key of
 // rank j to lane j. More experts: k rounds of a wave-wide key maximum pick
 // the top k in order.
 // Lane j < k returns slot j's expert and weight; other lanes return -1.
+__device__ __forceinline__ float logit_of(const LogitPlanes &lp, const float *row, int e) {
+  float v = row[e];
+  for (int s = 1; s < lp.nparts; ++s) v += row[(int64_t)s * lp.stride + e];
+  return v;
+}
+
 template <int NV>
-__device__ __forceinline__ int route_token_wave(const float *__restrict__ row, int E, int k,
+__device__ __forceinline__ int route_token_wave(const LogitPlanes &lp, int64_t t, int E, int k,
                                                 float *w_out, uint64_t *keys) {
   const int lane = threadIdx.x & 63;
+  const float *row = lp.p + t * E;
   if (NV == 1) {
-    const uint64_t key = lane < E ? route_key(row[lane], lane) : 0ull;
+    const uint64_t key = lane < E ? route_key(logit_of(lp, row, lane), lane) : 0ull;
     keys[lane] = key;
     // A wavefront's LDS accesses complete in issue order; keep the compiler
     // from moving the reads above the write.
@@ -93,7 +100,7 @@ __device__ __forceinline__ int route_token_wave(const float *__restrict__ row, i
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], e) : 0ull;
+    key[i] = e < E ? route_key(logit_of(lp, row, e), e) : 0ull;
   }
   uint64_t mine = 0ull;
   for (int j = 0; j < k; ++j) {

@@ -24,6 +24,17 @@ constexpr int kMaxTopK = 32;
 // Up to this many assignments (T*k) the routing, grouping and activation
 // quantisation run as one fused launch (one block does the grouping).
 constexpr int kSmallA = 2048;
+// Hidden channels per part of the router projection's fixed summation order.
+constexpr int kRouterPart = 512;
+
+// Router logits as the routing kernels read them: the logit of (t, e) is
+// the sum, in order s = 0..nparts-1, of p[s * stride + t * E + e] (one plane
+// when the caller gives the logits, one per part of the router projection).
+struct LogitPlanes {
+  const float *p;  // NULL: pre-routed
+  int nparts;
+  int64_t stride;
+};
 
 // ------------------------------------------------------------ device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
@@ -90,7 +101,7 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // a 16-row boundary, so P <= A + 15*min(E, A) rows for A = T*k assignments.
 struct FwdLayout {
   size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, a1,
-      rs, h, amax, qh, sh, y, total;
+      rs, h, amax, qh, sh, y, rpart, total;
   int64_t nblk;  // routing blocks
   int64_t P;     // padded permuted rows (upper bound)
 };
@@ -104,16 +115,21 @@ size_t calib_ws_bytes(int H);
 // starts, poffsets the padded ones; qh (and a1) are fragment-tiled.
 // Fused small-batch prologue: route (or copy pre-routed ids), group, clear
 // the per-row max and sorted[] over P rows, and quantise the activations.
-hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
+hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                                  int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
                                  int32_t *counts, int32_t *offsets, int32_t *poffsets,
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
                                  const uint16_t *x, const float *inv_s, int H, int8_t *qx,
                                  float *sx, uint32_t *amax, hipStream_t st, Timing tm);
-hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
+hipError_t launch_route_hist(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
                              int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
                              hipStream_t st, Timing tm);
+int router_parts(int H);
+hipError_t launch_router_proj(const uint16_t *x, const uint16_t *w_router, int64_t T, int E,
+                              int H, float *part, hipStream_t st, Timing tm);
+hipError_t launch_router_sum(const float *part, int nparts, int64_t T, int E, float *logits,
+                             hipStream_t st);
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
                        int32_t *offsets, int32_t *poffsets, int32_t *mtile_off, hipStream_t st,
                        Timing tm);

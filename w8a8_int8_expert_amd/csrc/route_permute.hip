@@ -120,7 +120,7 @@ constexpr int kSmallQuantTokens = 4;  // tokens quantised per block (blocks 1..)
 
 template <int NV>
 __global__ __launch_bounds__(1024) void prologue_small_kernel(
-    const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
+    const LogitPlanes logits, const int32_t *__restrict__ ids_in,
     const float *__restrict__ w_in, int T, int E, int k, int64_t capacity,
     int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ poffsets,
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
   for (int t = wave; t < T; t += 16) {
     int e;
     float w;
-    if (logits) {
-      e = route_token_wave<NV>(logits + (int64_t)t * E, E, k, &w, wave_keys[wave]);
+    if (logits.p) {
+      e = route_token_wave<NV>(logits, t, E, k, &w, wave_keys[wave]);
     } else {
       e = lane < k ? ids_in[t * k + lane] : -1;
       w = lane < k ? w_in[t * k + lane] : 0.0f;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
 // ------------------------------------------------------------- large A path
 template <int NV>
 __global__ __launch_bounds__(1024) void route_hist_kernel(
-    const float *__restrict__ logits, const int32_t *__restrict__ ids_in,
+    const LogitPlanes logits, const int32_t *__restrict__ ids_in,
     const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax,
     int32_t *__restrict__ sorted, int64_t P) {
@@ -223,8 +223,8 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     if (t >= T) break;
     int e;
     float w;
-    if (logits) {
-      e = route_token_wave<NV>(logits + t * E, E, k, &w, wave_keys[wave]);
+    if (logits.p) {
+      e = route_token_wave<NV>(logits, t, E, k, &w, wave_keys[wave]);
     } else {
       e = lane < k ? ids_in[t * k + lane] : -1;
       w = lane < k ? w_in[t * k + lane] : 0.0f;
@@ -340,7 +340,7 @@ int route_nv(int E) {
 
 }  // namespace
 
-hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, const float *w_in,
+hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                                  int T, int E, int k, int64_t capacity, int32_t *ids, float *wts,
                                  int32_t *counts, int32_t *offsets, int32_t *poffsets,
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
@@ -361,7 +361,7 @@ hipError_t launch_prologue_small(const float *logits, const int32_t *ids_in, con
 #undef MOE_PROLOGUE
 }
 
-hipError_t launch_route_hist(const float *logits, const int32_t *ids_in, const float *w_in,
+hipError_t launch_route_hist(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
                              int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
                              hipStream_t st, Timing tm) {
