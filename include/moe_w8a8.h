@@ -14,7 +14,10 @@
  *               capacity dropping the overflow (same page, §二.2);
  *   3. quantise each token to INT8 per token after dividing by the
  *               SmoothQuant scales ("MiniMax-M3 W8A8 inference on K100AI",
- *               mhpq.cn/news/1068415, §3.2 and §6.4);
+ *               mhpq.cn/news/1068415, §3.2 and §6.4), at the token's absolute
+ *               maximum or, when a clip is set, at the smaller of that and
+ *               the clip thresholds (values beyond saturate at +-127: K100AI
+ *               page §6.4; "一晚上完成MoE模型推理优化…" §3.2);
  *   4. GEMM1    per expert, INT8 x INT8 -> INT32 gate and up projections,
  *               dequantised per token and per output channel, h = silu(g)*u,
  *               requantised to INT8 per (token, expert) row (K100AI page
@@ -89,6 +92,14 @@ typedef struct {
  *               Not quantised ("MiniMax-M3 W8A8 inference on K100AI" §6.1:
  *               the layers at the routing stay in 16-bit floating point) and
  *               not written by moe_w8a8_calibrate.
+ *   act_clip  : fp32 [1]      static activation clipping threshold c written by
+ *               moe_w8a8_calibrate_clip, or NULL (no static clip). A value
+ *               <= 0 also means no clip.
+ *   act_sat_percentile  (a value, not a buffer) dynamic saturation of the
+ *               activations: 0 = off, else p in (0, 100]: each token is
+ *               quantised at most at the nearest-rank p-th percentile of its
+ *               own |x_j / s_j| (the m-th largest, m = H - ceil(p/100*H) + 1,
+ *               m <= 16 supported).
  * Code of W'[n][k] is q with W' ~= q * scale[n]; codes lie in [-127, 127]. */
 typedef struct {
   int8_t *w_gate_up;
@@ -98,6 +109,8 @@ typedef struct {
   float *smooth;
   float *inv_smooth;
   uint16_t *w_router;
+  float *act_clip;
+  float act_sat_percentile;
 } moe_w8a8_weights;
 
 /* Optional per-stage outputs of moe_w8a8_forward for checking; every pointer
@@ -178,6 +191,19 @@ int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
                        const moe_w8a8_weights *out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Static activation clipping threshold ("一晚上完成MoE模型推理优化…" §3.2:
+ * the calibration clips activations beyond the 99.9th percentile of their
+ * range). Writes act_clip[0] = the nearest-rank percentile `percentile` of
+ * |fl32(calib_x[n][j] * inv_smooth[j])| over all n_calib * H entries: the
+ * value of rank ceil(percentile/100 * N) (evaluated in fp64, clamped to
+ * [1, N]) in ascending order; 0 when n_calib = 0.
+ *   percentile in (0, 100]; calib_x bf16 [n_calib][H]; inv_smooth fp32 [H]
+ *   (from moe_w8a8_calibrate); act_clip fp32 [1]. All device memory.
+ * Errors: MOE_W8A8_ERR_INVALID, MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_HIP. */
+int moe_w8a8_calibrate_clip(const moe_w8a8_dims *dims, float percentile,
+                            const uint16_t *calib_x, int64_t n_calib,
+                            const float *inv_smooth, float *act_clip, void *stream);
+
 /* Forward pass of the layer for T tokens (steps 1-6 above).
  *   x           bf16 [T][H] input tokens.
  *   Routing input, one of three modes:
@@ -202,8 +228,9 @@ int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
  *   debug       NULL, or a host struct of optional device outputs (above).
  * T == 0 is a successful no-op whatever the other pointers are (empty
  * tensors may carry NULL addresses). Errors: MOE_W8A8_ERR_INVALID (NULL required
- * pointer, T < 0, T*k >= 2^31, routing inputs as above),
- * MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
+ * pointer, T < 0, T*k >= 2^31, routing inputs as above, act_sat_percentile
+ * outside {0} and (0, 100]), MOE_W8A8_ERR_UNSUPPORTED (also a saturation
+ * rank m > 16), MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
 int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
                      const uint16_t *x, int64_t T,
                      const float *router_logits,

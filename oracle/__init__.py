@@ -56,11 +56,14 @@ def _load():
         "oracle_capacity": (_I64, [_F32, _I64, _I32, _I32]),
         "oracle_permute": (_I64, [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P]),
         "oracle_act_quant": (None, [_I64, _I32, _P, _P, _P, _P]),
+        "oracle_act_quant_clip": (None, [_I64, _I32, _P, _P, _F32, _F32, _P, _P]),
+        "oracle_clip_threshold": (_F32, [_I64, _I32, _P, _P, _F32]),
+        "oracle_percentile_rank": (_I64, [ctypes.c_double, _I64]),
         "oracle_expert_rows": (None, [_I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _P, _P, _P, _P, _P]),
         "oracle_combine": (None, [_I64, _P, _I32, _I32, _P, _P, _P, _P, _P]),
         "oracle_forward": (_I64, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32,
-                                  _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _F32, _F32,
                                   _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "oracle_num_threads": (ctypes.c_int, []),
     }
@@ -169,15 +172,36 @@ def permute(ids, E: int, cap: int):
                 row_of=row_of[:A].reshape(T, k), kept=int(kept))
 
 
-def act_quant(x_bf16, inv_s):
-    """Per-token smoothed INT8 quantisation; x uint16 [T][H] -> qx int8, sx f32 [T]."""
+def act_quant(x_bf16, inv_s, clip: float = 0.0, sat_percentile: float = 0.0):
+    """Per-token smoothed INT8 quantisation; x uint16 [T][H] -> qx int8, sx f32 [T].
+    clip > 0: static clipping threshold; sat_percentile in (0, 100]: dynamic
+    per-token saturation at that percentile of |x * inv_s|."""
     x = _c(x_bf16, np.uint16)
     inv_s = _c(inv_s, np.float32)
     T, H = x.shape
     qx = np.empty((T, H), np.int8)
     sx = np.empty(T, np.float32)
-    _load().oracle_act_quant(T, H, _ptr(x), _ptr(inv_s), _ptr(qx), _ptr(sx))
+    if clip == 0.0 and sat_percentile == 0.0:
+        _load().oracle_act_quant(T, H, _ptr(x), _ptr(inv_s), _ptr(qx), _ptr(sx))
+    else:
+        _load().oracle_act_quant_clip(T, H, _ptr(x), _ptr(inv_s), float(clip),
+                                      float(sat_percentile), _ptr(qx), _ptr(sx))
     return qx, sx
+
+
+def clip_threshold(calib_x_bf16, inv_s, percentile: float) -> np.float32:
+    """Static clipping threshold: nearest-rank percentile of |x * inv_s| over
+    every calibration entry."""
+    x = _c(calib_x_bf16, np.uint16)
+    inv_s = _c(inv_s, np.float32)
+    n, H = x.shape
+    return np.float32(_load().oracle_clip_threshold(n, H, _ptr(x), _ptr(inv_s),
+                                                    float(np.float32(percentile))))
+
+
+def percentile_rank(p: float, N: int) -> int:
+    """1-based rank of the nearest-rank percentile p (float32 p, as the ABI)."""
+    return int(_load().oracle_percentile_rank(float(np.float32(p)), int(N)))
 
 
 def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h: bool = True):
@@ -219,7 +243,8 @@ def combine(tokens, w, row_of, y, y_row_index=None):
 
 
 def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor: float = 0.0,
-            want_acc1: bool = True, want_h: bool = True):
+            want_acc1: bool = True, want_h: bool = True, clip: float = 0.0,
+            sat_percentile: float = 0.0):
     """The whole layer on the CPU. Returns a dict of every stage's output."""
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
@@ -244,8 +269,8 @@ def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor:
              y=np.empty((max(A, 1), H), np.float64), out=np.empty((T, H), np.uint16))
     kept = _load().oracle_forward(
         T, H, F, E, k, _ptr(x), _ptr(lg), _ptr(ids_in), _ptr(w_in), float(capacity_factor),
-        _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), _ptr(inv_s),
-        _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]),
+        _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), _ptr(inv_s), float(clip),
+        float(np.float32(sat_percentile)), _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]),
         _ptr(o["row_of"]), _ptr(o["qx"]), _ptr(o["sx"]), _ptr(o["acc1"]), _ptr(o["h"]),
         _ptr(o["qh"]), _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]))
     kept = int(kept)

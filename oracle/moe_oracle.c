@@ -74,12 +74,9 @@ uint16_t oracle_f64_to_bf16(double v) {
  * unused); rounding is half to even; the code is rint(v * (127/amax)) with both
  * the reciprocal and the product rounded to fp32; the stored scale is
  * amax/127; an all-zero row gets scale 0 and codes 0. */
-static void quant_row(const float *v, int64_t n, int8_t *q, float *scale) {
-  float amax = 0.0f;
-  for (int64_t i = 0; i < n; ++i) {
-    float a = fabsf(v[i]);
-    if (a > amax) amax = a;
-  }
+/* The quantiser at a given level (the row's range): codes for |v| above the
+ * level saturate at +-127. quant_row below uses level = max |v|. */
+static void quant_row_at(const float *v, int64_t n, float amax, int8_t *q, float *scale) {
   if (amax == 0.0f) {
     memset(q, 0, (size_t)n);
     *scale = 0.0f;
@@ -94,6 +91,19 @@ static void quant_row(const float *v, int64_t n, int8_t *q, float *scale) {
     q[i] = (int8_t)c;
   }
   *scale = amax / 127.0f;
+}
+
+static float row_absmax(const float *v, int64_t n) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(v[i]);
+    if (a > amax) amax = a;
+  }
+  return amax;
+}
+
+static void quant_row(const float *v, int64_t n, int8_t *q, float *scale) {
+  quant_row_at(v, n, row_absmax(v, n), q, scale);
 }
 
 /* Exported form of the quantiser, one row after another (used by the pins). */
@@ -281,24 +291,88 @@ int64_t oracle_permute(int64_t T, int32_t E, int32_t k, const int32_t *ids, int6
   return kept;
 }
 
+/* ------------------------------------------------------ activation clips */
+
+/* Nearest-rank percentile. [Opus-K3 §3.2]: the calibration truncates
+ * activation values beyond the 99.9th percentile of their range (a range set
+ * by the extremes stretches the step and costs the small values precision).
+ * Reading: for N values sorted ascending, the p-th percentile is the value
+ * of rank r = ceil(p / 100 * N) (1-based, evaluated in fp64, clamped to
+ * [1, N]); no interpolation, so the threshold is one of the data values. */
+static int cmp_float(const void *a, const void *b) {
+  const float x = *(const float *)a, y = *(const float *)b;
+  return (x > y) - (x < y);
+}
+
+int64_t oracle_percentile_rank(double p, int64_t N) {
+  int64_t r = (int64_t)ceil(p / 100.0 * (double)N);
+  if (r < 1) r = 1;
+  if (r > N) r = N;
+  return r;
+}
+
+/* Static clipping threshold over the calibration tokens, taken on the
+ * smoothed activations the forward quantises: c = percentile p of
+ * |fl32(x[n][j] * inv_s[j])| over all n_calib * H entries. 0 when there are no
+ * entries. */
+float oracle_clip_threshold(int64_t n_calib, int32_t H, const uint16_t *x, const float *inv_s,
+                            float p) {
+  const int64_t N = n_calib * (int64_t)H;
+  if (N <= 0) return 0.0f;
+  float *a = (float *)malloc(sizeof(float) * (size_t)N);
+  for (int64_t n = 0; n < n_calib; ++n)
+    for (int32_t j = 0; j < H; ++j) a[n * H + j] = fabsf(bf16_bits_to_f32(x[n * H + j]) * inv_s[j]);
+  qsort(a, (size_t)N, sizeof(float), cmp_float);
+  const float c = a[oracle_percentile_rank((double)p, N) - 1];
+  free(a);
+  return c;
+}
+
+/* Level at which a smoothed token row is quantised. [K100AI §6.4]: besides
+ * per-token scales and SmoothQuant, activations may be saturated at a
+ * threshold instead of stretching the scale to the row's maximum.
+ *   clip > 0      static threshold (from the calibration above);
+ *   sat_p in (0, 100]: dynamic threshold, the row's own nearest-rank
+ *                 percentile sat_p of |v| (sorted copy of the row);
+ * the level is the smallest of max |v| and the enabled thresholds that are
+ * > 0 (a zero threshold, e.g. a mostly-zero row, leaves the level alone). */
+static float clip_level(const float *v, int32_t n, float clip, float sat_p, float *tmp) {
+  float level = row_absmax(v, n);
+  if (clip > 0.0f && clip < level) level = clip;
+  if (sat_p > 0.0f) {
+    for (int32_t j = 0; j < n; ++j) tmp[j] = fabsf(v[j]);
+    qsort(tmp, (size_t)n, sizeof(float), cmp_float);
+    const float t = tmp[oracle_percentile_rank((double)sat_p, n) - 1];
+    if (t > 0.0f && t < level) level = t;
+  }
+  return level;
+}
+
 /* ------------------------------------------------------------- act quant */
 
 /* Per-token activation quantisation with the smoothing folded in.
  * [K100AI §3.2, §6.4]: activations are quantised per token (one outlier token
  * must not set the range of others) after SmoothQuant's rescaling.
  * xs_j = x_j * inv_s_j in fp32, then the quantiser above over the row. */
-void oracle_act_quant(int64_t T, int32_t H, const uint16_t *x, const float *inv_s,
-                      int8_t *qx, float *sx) {
+void oracle_act_quant_clip(int64_t T, int32_t H, const uint16_t *x, const float *inv_s,
+                           float clip, float sat_p, int8_t *qx, float *sx) {
   #pragma omp parallel
   {
     float *row = (float *)malloc(sizeof(float) * (size_t)H);
+    float *tmp = (float *)malloc(sizeof(float) * (size_t)H);
     #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
       for (int32_t j = 0; j < H; ++j) row[j] = bf16_bits_to_f32(x[t * H + j]) * inv_s[j];
-      quant_row(row, H, qx + t * H, sx + t);
+      quant_row_at(row, H, clip_level(row, H, clip, sat_p, tmp), qx + t * H, sx + t);
     }
     free(row);
+    free(tmp);
   }
+}
+
+void oracle_act_quant(int64_t T, int32_t H, const uint16_t *x, const float *inv_s,
+                      int8_t *qx, float *sx) {
+  oracle_act_quant_clip(T, H, x, inv_s, 0.0f, 0.0f, qx, sx);
 }
 
 /* ------------------------------------------------------------ expert row */
@@ -410,6 +484,7 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                        const int32_t *ids_in, const float *w_in, float capacity_factor,
                        const int8_t *q_gu, const float *sw_gu,
                        const int8_t *q_d, const float *sw_d, const float *inv_s,
+                       float clip, float sat_p,
                        int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
                        int32_t *sorted, int32_t *row_of, int8_t *qx, float *sx,
                        int32_t *acc1, float *h, int8_t *qh, float *sh, double *y,
@@ -422,7 +497,7 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
   }
   int64_t cap = oracle_capacity(capacity_factor, T, k, E);
   int64_t kept = oracle_permute(T, E, k, ids, cap, counts, offsets, sorted, row_of);
-  oracle_act_quant(T, H, x, inv_s, qx, sx);
+  oracle_act_quant_clip(T, H, x, inv_s, clip, sat_p, qx, sx);
   int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(kept > 0 ? kept : 1));
   for (int64_t i = 0; i < kept; ++i) rows[i] = (int32_t)i;
   oracle_expert_rows(kept, rows, H, F, k, ids, sorted, qx, sx, q_gu, sw_gu, q_d, sw_d,

@@ -203,6 +203,86 @@ def test_router_logits_integer_closed_form():
     assert np.array_equal(got, want)
 
 
+# ------------------------------------------------------- activation clips
+
+def test_percentile_rank_closed_forms():
+    """Nearest rank ceil(p/100 * N), clamped to [1, N]."""
+    assert oracle.percentile_rank(75.0, 1000) == 750
+    # p is taken as its float32 value: 99.9f = 99.900001526 > 99.9, so the
+    # rank among 1000 values is ceil(999.0000153) = 1000
+    assert oracle.percentile_rank(99.9, 1000) == 1000
+    assert oracle.percentile_rank(100.0, 4096) == 4096
+    assert oracle.percentile_rank(50.0, 4) == 2
+    assert oracle.percentile_rank(1e-6, 5) == 1
+    # 99.9 as float32 is 99.90000152...: 0.999000015 * 4096 = 4091.90 -> 4092
+    assert oracle.percentile_rank(99.9, 4096) == 4092
+
+
+def test_clip_threshold_bruteforce():
+    """The static threshold is the ranked value of the sorted |x * inv_s|."""
+    rng = np.random.default_rng(21)
+    n, H = 37, 64
+    x = f32_to_bf16_bits(rng.standard_normal((n, H), dtype=np.float32) * np.float32(3.0))
+    inv_s = rng.uniform(0.2, 2.0, H).astype(np.float32)
+    a = np.sort(np.abs(bf16_bits_to_f32(x) * inv_s).ravel())
+    for p in (99.9, 99.0, 90.0, 50.0, 100.0, 0.01):
+        r = math.ceil(np.float64(np.float32(p)) / 100.0 * a.size)
+        want = a[min(max(r, 1), a.size) - 1]
+        assert oracle.clip_threshold(x, inv_s, p) == want
+    assert oracle.clip_threshold(x, inv_s, 100.0) == a[-1]
+    assert oracle.clip_threshold(x[:0], inv_s, 99.9) == 0.0
+
+
+def _levels_quant(v, level):
+    """Quantiser of the pages at a given level, in float32 arithmetic."""
+    rr = np.float32(127.0) / np.float32(level)
+    q = np.clip(np.rint((v * rr).astype(np.float32)), -127, 127).astype(np.int8)
+    return q, np.float32(level) / np.float32(127.0)
+
+
+def test_dynamic_saturation_hand_row():
+    """A row 1..256 (inv_s = 1) plus three outliers: at p with m = 4 the level
+    is the 4th largest |v|; the three outliers saturate at +-127."""
+    H = 256
+    vals = np.arange(1, H + 1, dtype=np.float32)
+    vals[[10, 20, 30]] = [5000.0, -4000.0, 3000.0]
+    x = f32_to_bf16_bits(vals[None, :])
+    v = bf16_bits_to_f32(x)[0]
+    inv_s = np.ones(H, np.float32)
+    p = 98.5                         # ceil(0.985 * 256) = 253 -> m = 256 - 253 + 1 = 4
+    assert oracle.percentile_rank(p, H) == 253
+    level = np.sort(np.abs(v))[-4]
+    assert level == 256.0
+    qx, sx = oracle.act_quant(x, inv_s, sat_percentile=p)
+    q, sc = _levels_quant(v, level)
+    assert np.array_equal(qx[0], q) and sx[0] == sc
+    assert qx[0, 10] == 127 and qx[0, 20] == -127 and qx[0, 30] == 127
+    # p = 100 keeps the plain per-token maximum
+    q0, s0 = oracle.act_quant(x, inv_s)
+    q1, s1 = oracle.act_quant(x, inv_s, sat_percentile=100.0)
+    assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
+
+
+def test_static_clip_level_and_off_values():
+    """Static clip: level = min(max |v|, c); c above the maximum or <= 0 leaves
+    the plain quantiser; values past c saturate."""
+    rng = np.random.default_rng(22)
+    T, H = 9, 256
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    inv_s = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    v = bf16_bits_to_f32(x) * inv_s
+    amax = np.abs(v).max(axis=1)
+    c = np.float32(np.median(amax))
+    qx, sx = oracle.act_quant(x, inv_s, clip=c)
+    for t in range(T):
+        q, sc = _levels_quant(v[t], min(amax[t], c))
+        assert np.array_equal(qx[t], q) and sx[t] == sc
+    q0, s0 = oracle.act_quant(x, inv_s)
+    for off in (np.float32(1e9), np.float32(-1.0)):
+        q1, s1 = oracle.act_quant(x, inv_s, clip=off)
+        assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
+
+
 def test_permute_golden(golden_dir):
     g = _load(golden_dir, "permute_capacity.json")
     ids = np.array(g["ids"], np.int32)

@@ -33,7 +33,8 @@ class moe_w8a8_dims(ctypes.Structure):
 
 class moe_w8a8_weights(ctypes.Structure):
     _fields_ = [("w_gate_up", _P), ("w_down", _P), ("s_gate_up", _P), ("s_down", _P),
-                ("smooth", _P), ("inv_smooth", _P), ("w_router", _P)]
+                ("smooth", _P), ("inv_smooth", _P), ("w_router", _P), ("act_clip", _P),
+                ("act_sat_percentile", ctypes.c_float)]
 
 
 class moe_w8a8_debug(ctypes.Structure):
@@ -46,8 +47,8 @@ STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", 
           "router")
 
 
-EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_forward",
-           "moe_w8a8_router_logits", "moe_w8a8_strerror")
+EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_calibrate_clip",
+           "moe_w8a8_forward", "moe_w8a8_router_logits", "moe_w8a8_strerror")
 
 _lib = None
 
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_w8a8_forward.restype = ctypes.c_int
     lib.moe_w8a8_forward.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_float, _P,
                                      _P, ctypes.c_size_t, G, _P]
+    lib.moe_w8a8_calibrate_clip.restype = ctypes.c_int
+    lib.moe_w8a8_calibrate_clip.argtypes = [D, ctypes.c_float, _P, ctypes.c_int64, _P, _P, _P]
     lib.moe_w8a8_router_logits.restype = ctypes.c_int
     lib.moe_w8a8_router_logits.argtypes = [D, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t,
                                            _P]
@@ -127,6 +130,13 @@ def moe_w8a8_forward(d, weights: moe_w8a8_weights, x, T, router_logits, topk_ids
         _stream(stream)))
 
 
+def moe_w8a8_calibrate_clip(d, percentile, calib_x, n_calib, inv_smooth, act_clip,
+                            stream=None) -> int:
+    return int(load_library().moe_w8a8_calibrate_clip(
+        ctypes.byref(d), float(percentile), _ptr(calib_x), int(n_calib), _ptr(inv_smooth),
+        _ptr(act_clip), _stream(stream)))
+
+
 def moe_w8a8_router_logits(d, x, T, w_router, logits, workspace, workspace_bytes,
                            stream=None) -> int:
     return int(load_library().moe_w8a8_router_logits(
@@ -161,9 +171,23 @@ class MoEW8A8:
         self.inv_smooth = torch.empty(H, dtype=torch.float32, **kw)
         self.weights = moe_w8a8_weights(*(t.data_ptr() for t in (
             self.w_gate_up, self.w_down, self.s_gate_up, self.s_down, self.smooth,
-            self.inv_smooth)), None)
+            self.inv_smooth)), None, None, 0.0)
         self.w_router = None
+        self.act_clip = torch.zeros(1, dtype=torch.float32, **kw)
         self._ws = None
+
+    def calibrate_clip(self, calib_x, percentile: float):
+        """Static activation clip at the percentile of the calibration tokens'
+        smoothed values (after calibrate); forward then uses it."""
+        _check(moe_w8a8_calibrate_clip(self.d, percentile, calib_x, calib_x.shape[0],
+                                       self.inv_smooth, self.act_clip), "moe_w8a8_calibrate_clip")
+        self.weights.act_clip = self.act_clip.data_ptr()
+
+    def set_clip(self, static: bool = False, sat_percentile: float = 0.0):
+        """Use (or not) the static clip, and the dynamic saturation percentile
+        (0 = off)."""
+        self.weights.act_clip = self.act_clip.data_ptr() if static else None
+        self.weights.act_sat_percentile = float(sat_percentile)
 
     def set_router(self, w_router):
         """bf16 [E][H] router matrix (kept on the device; copied), or None."""

@@ -57,6 +57,15 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   return L;
 }
 
+// 1-based rank of the nearest-rank percentile p of N values: ceil(p/100 * N)
+// in fp64, clamped to [1, N].
+int64_t percentile_rank(float p, int64_t N) {
+  int64_t r = (int64_t)ceil((double)p / 100.0 * (double)N);
+  if (r < 1) r = 1;
+  if (r > N) r = N;
+  return r;
+}
+
 size_t calib_ws_bytes(int H) { return align_up(sizeof(uint32_t) * H) * 2; }
 
 }  // namespace moe
@@ -110,6 +119,20 @@ extern "C" int moe_w8a8_router_logits(const moe_w8a8_dims *d, const uint16_t *x,
   return MOE_W8A8_OK;
 }
 
+extern "C" int moe_w8a8_calibrate_clip(const moe_w8a8_dims *d, float percentile,
+                                       const uint16_t *calib_x, int64_t n_calib,
+                                       const float *inv_smooth, float *act_clip, void *stream) {
+  if (!dims_valid(d) || !inv_smooth || !act_clip || n_calib < 0 || (n_calib > 0 && !calib_x) ||
+      !(percentile > 0.0f && percentile <= 100.0f))
+    return MOE_W8A8_ERR_INVALID;
+  if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
+  const int H = d->hidden;
+  const int64_t N = n_calib * (int64_t)H;
+  const int64_t m = N > 0 ? N - percentile_rank(percentile, N) + 1 : 1;
+  MOE_CHECK(launch_calib_clip(calib_x, n_calib, H, inv_smooth, m, act_clip, (hipStream_t)stream));
+  return MOE_W8A8_OK;
+}
+
 extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uint16_t *calib_x,
                                   int64_t n_calib, const float *w_gate, const float *w_up,
                                   const float *w_down, const moe_w8a8_weights *out,
@@ -151,9 +174,16 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
       !wt->inv_smooth)
     return MOE_W8A8_ERR_INVALID;
   if (isnan(capacity_factor)) return MOE_W8A8_ERR_INVALID;
+  const float sat_p = wt->act_sat_percentile;
+  if (!(sat_p == 0.0f || (sat_p > 0.0f && sat_p <= 100.0f))) return MOE_W8A8_ERR_INVALID;
   if (dbg && (dbg->gemm_path < 0 || dbg->gemm_path > 2)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts, k = d->top_k;
+  ActClip ac{wt->act_clip, 0};
+  if (sat_p > 0.0f) {
+    ac.sat_m = (int)(H - percentile_rank(sat_p, H) + 1);
+    if (ac.sat_m > kMaxSatM) return MOE_W8A8_ERR_UNSUPPORTED;
+  }
   const FwdLayout L = fwd_layout(T, H, F, E, k);
   if (!workspace || workspace_bytes < L.total) return MOE_W8A8_ERR_WORKSPACE;
 
@@ -216,7 +246,7 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   if (small) {
     MOE_CHECK(launch_prologue_small(lp, topk_ids, topk_w, (int)T, E, k, capacity, ids,
                                     wts, counts, offsets, poffsets, mtile_off, sorted, row_of,
-                                    (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, st,
+                                    (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, ac, st,
                                     tm(kRoute)));
   } else {
     MOE_CHECK(launch_route_hist(lp, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
@@ -227,7 +257,7 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
                              tm(kScatter)));
   }
   if (path == 1) {
-    if (!small) MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ)));
+    if (!small) MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, st, tm(kActQ)));
     MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, poffsets, offsets, wt->w_gate_up,
                                   wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
   } else {
@@ -236,7 +266,7 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
     // Writing the codes straight into the permuted tiles from the
     // quantisation kernel scatters 16-byte pieces and measured 2.5x slower.
     if (!small)
-      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, st, tm(kActQ, true, false)));
+      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, st, tm(kActQ, true, false)));
     MOE_CHECK(launch_gather_tiles(qx, sx, sorted, k, poffsets, E, L.P, H, a1, rs, st,
                                   tm(kActQ, small, true)));
     MOE_CHECK(launch_gemm1_tiled(a1, rs, counts, poffsets, offsets, mtile_off, A, wt->w_gate_up,

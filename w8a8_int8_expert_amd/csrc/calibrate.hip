@@ -140,6 +140,49 @@ hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const f
   return hipGetLastError();
 }
 
+// Static clipping threshold ("一晚上完成MoE模型推理优化…" §3.2: calibration
+// clips the activations at a percentile of their range): the m-th largest of
+// the N = n_calib * H values |fl32(x[n][j] * inv_s[j])|, m = N - r + 1 for the
+// percentile's rank r. One block decides the answer bit by bit from the top
+// (non-negative floats order as unsigned integers): a bit is kept when at
+// least m values are >= the answer with it set. N = 0 writes 0 (no clip).
+__global__ __launch_bounds__(1024) void clip_threshold_kernel(const uint16_t *__restrict__ x,
+                                                              int64_t n_calib, int H,
+                                                              const float *__restrict__ inv_s,
+                                                              int64_t m, float *__restrict__ out) {
+  __shared__ long long wcnt[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t N = n_calib * H;
+  uint32_t ans = 0u;
+  for (int bit = 30; bit >= 0 && N > 0; --bit) {
+    const uint32_t cand = ans | (1u << bit);
+    long long cnt = 0;
+    for (int j = tid; j < H; j += 1024) {
+      const float sj = inv_s[j];
+      for (int64_t n = 0; n < n_calib; ++n) {
+        const float v = __uint_as_float((uint32_t)x[n * H + j] << 16) * sj;
+        cnt += __float_as_uint(__builtin_fabsf(v)) >= cand ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    long long total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) total += wcnt[w];
+    __syncthreads();
+    if (total >= m) ans = cand;
+  }
+  if (tid == 0) *out = __uint_as_float(ans);
+}
+
+hipError_t launch_calib_clip(const uint16_t *calib_x, int64_t n_calib, int H, const float *inv_s,
+                             int64_t m, float *out, hipStream_t st) {
+  clip_threshold_kernel<<<dim3(1), dim3(1024), 0, st>>>(calib_x, n_calib, H, inv_s, m, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alpha, int H,
                                float *s, float *inv_s, hipStream_t st) {
   smooth_kernel<<<dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st>>>(ax, aw, alpha, H, s,

@@ -119,17 +119,48 @@ __device__ __forceinline__ int route_token_wave(const LogitPlanes &lp, int64_t t
 }
 
 // ------------------------------------------------------------ quantisation
+// Insert the bits of a non-negative float (which order as unsigned integers)
+// into a lane's list of its kMaxSatM largest, kept in descending order.
+__device__ __forceinline__ void top_insert(uint32_t (&l)[kMaxSatM], uint32_t v) {
+#pragma unroll
+  for (int s = kMaxSatM - 1; s > 0; --s) l[s] = v > l[s - 1] ? l[s - 1] : (v > l[s] ? v : l[s]);
+  l[0] = v > l[0] ? v : l[0];
+}
+
+// m-th largest (m <= kMaxSatM) of the values the wavefront holds, given each
+// lane's list of its kMaxSatM largest: the global m largest are all in the
+// lists, so counting list entries >= a candidate decides every bit of the
+// answer exactly. top = bits of the overall maximum.
+__device__ __forceinline__ uint32_t wave_mth_largest(const uint32_t (&l)[kMaxSatM], int m,
+                                                     uint32_t top) {
+  uint32_t ans = 0u;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = ans | (1u << bit);
+    if (cand > top) continue;  // nothing is >= cand
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxSatM; ++s) cnt += l[s] >= cand ? 1 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+    if (cnt >= m) ans = cand;
+  }
+  return ans;
+}
+
 // "MiniMax-M3 W8A8 inference on K100AI" §3.2/§6.4: per-token symmetric INT8
-// after the SmoothQuant rescaling. amax = max |x_j * inv_s_j|,
-// code = rint(fl32(v * fl32(127/amax))) clamped to [-127, 127], scale =
-// amax/127; an all-zero row gets scale 0 and codes 0.
+// after the SmoothQuant rescaling. v_j = x_j * inv_s_j, level = max |v_j|,
+// optionally lowered by a clip (§6.4: saturate instead of stretching the scale;
+// "一晚上完成MoE模型推理优化…" §3.2: clip at a percentile), code =
+// rint(fl32(v * fl32(127/level))) clamped to [-127, 127], scale = level/127;
+// a zero level gives scale 0 and codes 0.
 // One wavefront per row; the row (H bf16) is read once, 16 bytes per lane
 // per chunk, and kept in registers between the max and the code pass while
 // it fits (H <= 64 * 8 * MAXC), re-read otherwise.
 template <int MAXC>
 __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
                                                 const float *__restrict__ inv_s, int H,
-                                                int8_t *__restrict__ qr, float *__restrict__ sx) {
+                                                int8_t *__restrict__ qr, float *__restrict__ sx,
+                                                ActClip ac = ActClip{nullptr, 0}) {
   const int lane = threadIdx.x & 63;
   const int nchunk = H >> 3;
   const bool cached = nchunk <= 64 * MAXC;
@@ -172,8 +203,35 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
     }
   }
   amax = wave_max(amax);
-  if (lane == 0) *sx = amax / 127.0f;
-  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  float level = amax;
+  if (ac.clip) {
+    const float c = *ac.clip;
+    if (c > 0.0f && c < level) level = c;
+  }
+  if (ac.sat_m > 1) {
+    uint32_t top[kMaxSatM];
+#pragma unroll
+    for (int s = 0; s < kMaxSatM; ++s) top[s] = 0u;
+    auto add8 = [&](v4i r, int c) {
+      float v[8];
+      scale8(r, c, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) top_insert(top, __float_as_uint(__builtin_fabsf(v[j])));
+    };
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) add8(raw[i], c);
+      }
+    } else {
+      for (int c = lane; c < nchunk; c += 64) add8(*reinterpret_cast<const v4i *>(xr + c * 8), c);
+    }
+    const float t = __uint_as_float(wave_mth_largest(top, ac.sat_m, __float_as_uint(amax)));
+    if (t > 0.0f && t < level) level = t;
+  }
+  if (lane == 0) *sx = level / 127.0f;
+  const float rr = level > 0.0f ? 127.0f / level : 0.0f;
   auto emit = [&](v4i r, int c) {
     float v[8];
     scale8(r, c, v);

@@ -27,6 +27,16 @@ constexpr int kSmallA = 2048;
 // Hidden channels per part of the router projection's fixed summation order.
 constexpr int kRouterPart = 512;
 
+// Clip of the per-token activation quantiser: the row is quantised at a
+// level below its maximum when *clip is a positive static threshold, or when
+// sat_m > 1 (dynamic saturation: at most the row's sat_m-th largest |v|).
+// Zero thresholds leave the level alone.
+constexpr int kMaxSatM = 16;  // largest supported sat_m
+struct ActClip {
+  const float *clip;  // device fp32 [1], or NULL
+  int sat_m;          // 0 or 1: off
+};
+
 // Router logits as the routing kernels read them: the logit of (t, e) is
 // the sum, in order s = 0..nparts-1, of p[s * stride + t * E + e] (one plane
 // when the caller gives the logits, one per part of the router projection).
@@ -120,7 +130,8 @@ hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, cons
                                  int32_t *counts, int32_t *offsets, int32_t *poffsets,
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
                                  const uint16_t *x, const float *inv_s, int H, int8_t *qx,
-                                 float *sx, uint32_t *amax, hipStream_t st, Timing tm);
+                                 float *sx, uint32_t *amax, ActClip ac, hipStream_t st,
+                                 Timing tm);
 hipError_t launch_route_hist(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
                              int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
@@ -137,7 +148,7 @@ hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
                           int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
-                            float *sx, hipStream_t st, Timing tm);
+                            float *sx, ActClip ac, hipStream_t st, Timing tm);
 hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
                                float *rs, hipStream_t st, Timing tm);
@@ -174,6 +185,8 @@ hipError_t launch_debug_row_of(const int32_t *row_of_p, const int32_t *ids, cons
 hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const float *w_gate,
                                const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,
                                hipStream_t st);
+hipError_t launch_calib_clip(const uint16_t *calib_x, int64_t n_calib, int H, const float *inv_s,
+                             int64_t m, float *out, hipStream_t st);
 hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alpha, int H,
                                float *s, float *inv_s, hipStream_t st);
 hipError_t launch_calib_quant(const float *w_gate, const float *w_up, const float *w_down,

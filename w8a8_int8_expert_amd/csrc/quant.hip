@@ -18,10 +18,10 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
                                                         const float *__restrict__ inv_s,
                                                         int64_t T, int H,
                                                         int8_t *__restrict__ qx,
-                                                        float *__restrict__ sx) {
+                                                        float *__restrict__ sx, ActClip ac) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t);
+  quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac);
 }
 
 // h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
@@ -87,9 +87,9 @@ __global__ __launch_bounds__(256) void gather_tiles_kernel(const int8_t *__restr
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
-                            float *sx, hipStream_t st, Timing tm) {
+                            float *sx, ActClip ac, hipStream_t st, Timing tm) {
   return launch_kernel(act_quant_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, tm, x, inv_s,
-                       T, H, qx, sx);
+                       T, H, qx, sx, ac);
 }
 
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
