@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -199,6 +201,71 @@ def time_router(gl: GpuLayer, wl, inputs, w_router, steps, warmup):
             "logits_TFLOPs": round(flops / lg_s / 1e12, 2)}
 
 
+def fp64_layer(layer, x_f32, ids, w):
+    """The unquantised layer in fp64 from the fp32 weights (the reference the
+    quantisation error is measured against): out[t] = sum_j w[t][j] *
+    W_down[e] (silu(W_gate[e] x) * (W_up[e] x)), e = ids[t][j]."""
+    T, k = ids.shape
+    out = np.zeros((T, layer.w_down.shape[1]))
+    x64 = x_f32.astype(np.float64)
+    for e in np.unique(ids):
+        t, j = np.nonzero(ids == e)
+        xe = x64[t]
+        g = xe @ layer.w_gate[e].astype(np.float64).T
+        u = xe @ layer.w_up[e].astype(np.float64).T
+        h = g / (1.0 + np.exp(-g)) * u
+        y = h @ layer.w_down[e].astype(np.float64).T
+        np.add.at(out, t, w[t, j][:, None].astype(np.float64) * y)
+    return out
+
+
+def alpha_sweep(gl: GpuLayer, layer, T, alphas, percentile):
+    """Quantisation error of the whole layer against fp64_layer for each
+    SmoothQuant alpha, without clipping, with the static percentile clip of
+    the calibration and with dynamic per-token saturation at the same
+    percentile: relative RMS error over T tokens of the decode layer."""
+    import synth
+    import w8a8_int8_expert_amd as m
+    torch = gl.torch
+    dev = torch.device("cuda")
+    wl = synth.workload("decode", T=T)
+    inputs = synth.make_inputs(wl, layer)
+    x = torch.from_numpy(inputs.x.view("int16")).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(inputs.logits).to(dev)
+    ids_t = torch.empty(T * wl.k, dtype=torch.int32, device=dev)
+    w_t = torch.empty(T * wl.k, dtype=torch.float32, device=dev)
+    dbg = m.moe_w8a8_debug()
+    dbg.topk_ids, dbg.topk_w = ids_t.data_ptr(), w_t.data_ptr()
+    cx = torch.from_numpy(layer.calib_x.view("int16")).to(dev).view(torch.bfloat16)
+    wg = torch.from_numpy(layer.w_gate).to(dev)
+    wu = torch.from_numpy(layer.w_up).to(dev)
+    wd = torch.from_numpy(layer.w_down).to(dev)
+    ref = None
+    rows = []
+    for a in alphas:
+        gl.g.calibrate(cx, wg, wu, wd, a)
+        gl.g.calibrate_clip(cx, percentile)
+        for name, static, sat in (("none", False, 0.0),
+                                  ("static_p%g" % percentile, True, 0.0),
+                                  ("dynamic_p%g" % percentile, False, percentile)):
+            gl.g.set_clip(static=static, sat_percentile=sat)
+            out = gl.g.forward(x, logits, None, None, 0.0, debug=dbg)
+            torch.cuda.synchronize()
+            if ref is None:
+                ids = ids_t.cpu().numpy().reshape(T, wl.k)
+                w = w_t.cpu().numpy().reshape(T, wl.k)
+                ref = fp64_layer(layer, synth.bf16_bits_to_f32(inputs.x), ids, w)
+                rms = float(np.sqrt(np.mean(ref ** 2)))
+            o = out.float().cpu().numpy().astype(np.float64)
+            rows.append({"alpha": a, "clip": name,
+                         "rel_rms_err": round(float(np.sqrt(np.mean((o - ref) ** 2))) / rms, 6)})
+    gl.g.set_clip()
+    del wg, wu, wd
+    torch.cuda.empty_cache()
+    return {"workload": "decode layer, %d tokens, logits routing" % T, "tokens": T,
+            "percentile": percentile, "reference": "unquantised layer in fp64", "rows": rows}
+
+
 def launched_stages(wl):
     """Stages that have a launch of their own (and so a timing pair): up to
     2048 assignments route, grouping and activation quantisation are one
@@ -259,6 +326,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--alpha-sweep", action="store_true",
+                    help="only the quantisation-error sweep over alpha and the clip variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -283,6 +352,11 @@ def main():
     log("generating %s layer (H=%d F=%d E=%d)" % (layer_wl.name, wl.H, wl.F, wl.E))
     layer = synth.make_layer(layer_wl)
     gl = GpuLayer(layer_wl, layer, torch)
+    if args.alpha_sweep:
+        log("alpha sweep")
+        print(json.dumps({"alpha_sweep": alpha_sweep(
+            gl, layer, 128, [0.5, 0.55, 0.6, 0.65, 0.7], 99.9)}), flush=True)
+        return
     inputs = synth.make_inputs(wl, layer)
     gl.wl = wl
     log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
