@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W8A8 MoE layer tokens/s; HBM GB/s (decode) & INT8 MFMA % of peak (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # Steps between two steps that carry stage events (decode; prefill steps all do).
 EVENT_STRIDE = 10
 STAGE_INDEX = {s: i for i, s in enumerate(
@@ -101,11 +102,11 @@ def stored_traffic(kernel: str, workload: str):
 
 
 class GpuLayer:
-    def __init__(self, wl, layer, torch):
+    def __init__(self, wl, layer, torch, fp8=False):
         import w8a8_int8_expert_amd as m
         self.m, self.torch, self.wl = m, torch, wl
         dev = torch.device("cuda")
-        self.g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
+        self.g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k, fp8=fp8)
         cx = torch.from_numpy(layer.calib_x.view("int16")).to(dev).view(torch.bfloat16)
         wg = torch.from_numpy(layer.w_gate).to(dev)
         wu = torch.from_numpy(layer.w_up).to(dev)
@@ -326,6 +327,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--alpha-sweep", action="store_true",
                     help="only the quantisation-error sweep over alpha and the clip variants")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -425,6 +427,40 @@ def main():
             "stage_us": {k: round(v * 1e3, 1) for k, v in pr["stage_ms"].items()},
         }
         del pr
+    if wl.name == "decode" and not args.no_fp8:
+        log("FP8 (e4m3) expert path: calibrating and timing decode")
+        gf = GpuLayer(layer_wl, layer, torch, fp8=True)
+        fr = time_workload(gf, wl, inputs, args.steps, args.warmup, hip, launched_stages(wl),
+                           EVENT_STRIDE)
+        fsec = fr["seconds"]
+        g1b = gemm1_bytes(wl, touched)
+        fp8 = {"decode": {
+            "tokens_per_s": round(T * args.steps / fsec, 1),
+            "ms_per_step": round(fsec * 1e3 / args.steps, 5),
+            "gemm1_hbm_frac": round(g1b / (fr["stage_ms"]["gemm1"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_hbm_frac": round(lb / fsec * args.steps / 1e9 / HBM_PEAK_GBS, 4),
+            "stage_us": {k: round(v * 1e3, 2) for k, v in fr["stage_ms"].items()}}}
+        if not args.no_prefill:
+            log("FP8 prefill: 3 warmup + %d steps" % args.prefill_steps)
+            pwl = synth.workload("prefill")
+            gf.wl = pwl
+            pin = synth.make_inputs(pwl, layer)
+            pr = time_workload(gf, pwl, pin, args.prefill_steps, 3, hip, launched_stages(pwl), 1)
+            pA = int(pr["counts"].sum())
+            ops = 6.0 * pA * pwl.H * pwl.F
+            fp8["prefill"] = {
+                "tokens_per_s": round(pwl.T * args.prefill_steps / pr["seconds"], 1),
+                "ms_per_step": round(pr["seconds"] * 1e3 / args.prefill_steps, 4),
+                "layer_frac_fp8_peak": round(ops * args.prefill_steps / pr["seconds"] / 1e12 /
+                                             FP8_PEAK_TFLOPS, 4),
+                "gemm1_frac_fp8_peak": round(4.0 * pA * pwl.H * pwl.F /
+                                             (pr["stage_ms"]["gemm1"] * 1e-3) / 1e12 /
+                                             FP8_PEAK_TFLOPS, 4),
+                "stage_us": {k: round(v * 1e3, 1) for k, v in pr["stage_ms"].items()}}
+            del pr
+        res["fp8"] = fp8
+        del gf, fr
+        torch.cuda.empty_cache()
     if wl.name == "decode" and not args.no_router:
         log("timing router-projection mode")
         w_router = synth.make_router(layer_wl)

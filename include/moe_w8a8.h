@@ -70,6 +70,18 @@ typedef struct {
   int32_t top_k;       /* k, assignments per token */
 } moe_w8a8_dims;
 
+/* Code format of the expert path ("超大规模模型推理的Day0适配实践" §二.1: expert
+ * layers in INT8 or FP8; §四: the activations take the weights' format).
+ *   INT8: symmetric codes in [-127, 127], scale = range/127, integer
+ *         accumulation.
+ *   FP8:  OCP e4m3 codes (bias 7, 3 mantissa bits, subnormals, largest
+ *         finite 448, NaN 0x7f/0xff), scale = range/448; a value is coded as
+ *         the nearest e4m3 (ties to even, sign of zero kept) of
+ *         clamp(fl32(v * fl32(448/range)), -448, 448); fp32 accumulation of
+ *         the exact code products. */
+#define MOE_W8A8_FORMAT_INT8 0
+#define MOE_W8A8_FORMAT_FP8 1
+
 /* Quantised layer weights (device memory, written by moe_w8a8_calibrate).
  *
  * Fragment-tiled INT8 layout. A weight matrix W[N][K] (N output channels,
@@ -100,7 +112,11 @@ typedef struct {
  *               quantised at most at the nearest-rank p-th percentile of its
  *               own |x_j / s_j| (the m-th largest, m = H - ceil(p/100*H) + 1,
  *               m <= 16 supported).
- * Code of W'[n][k] is q with W' ~= q * scale[n]; codes lie in [-127, 127]. */
+ *   format    : MOE_W8A8_FORMAT_INT8 or _FP8, set by the caller before
+ *               moe_w8a8_calibrate (which codes the weights in it); forward
+ *               codes the activations and runs the GEMMs in the same format.
+ * Code of W'[n][k] is q with W' ~= q * scale[n] (INT8: codes lie in
+ * [-127, 127]; FP8: W' ~= e4m3 value of q * scale[n]). */
 typedef struct {
   int8_t *w_gate_up;
   int8_t *w_down;
@@ -111,6 +127,7 @@ typedef struct {
   uint16_t *w_router;
   float *act_clip;
   float act_sat_percentile;
+  int32_t format;
 } moe_w8a8_weights;
 
 /* Optional per-stage outputs of moe_w8a8_forward for checking; every pointer
@@ -121,8 +138,10 @@ typedef struct {
  *   expert_counts int32 [E] kept rows per expert; expert_offsets int32 [E+1]
  *   sorted_assign int32 [A] assignment t*k+j of each permuted row
  *   row_of int32 [A] permuted row of assignment t*k+j, -1 if dropped
- *   qx int8 [T][H], sx fp32 [T]   per-token codes and scales
- *   acc1 int32 [A][2F]            GEMM1 accumulators (gate then up)
+ *   qx int8 [T][H], sx fp32 [T]   per-token codes (e4m3 bytes in FP8 format)
+ *                                 and scales
+ *   acc1 int32 [A][2F]            GEMM1 accumulators (gate then up; the
+ *                                 bits of the fp32 sums in FP8 format)
  *   h fp32 [A][F]                 SwiGLU output before requantisation
  *   qh int8 [A][F], sh fp32 [A]   requantised hidden rows and their scales
  *   y fp32 [A][H]                 dequantised down-projection rows */

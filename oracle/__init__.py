@@ -49,22 +49,25 @@ def _load():
     sig = {
         "oracle_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
         "oracle_quant_rows": (None, [_I64, _I64, _P, _P, _P]),
+        "oracle_quant_rows_fmt": (None, [_I64, _I64, _P, _I32, _P, _P]),
+        "oracle_e4m3_value": (ctypes.c_double, [ctypes.c_uint8]),
+        "oracle_e4m3_code": (ctypes.c_uint8, [_F32]),
         "oracle_calibrate": (ctypes.c_int, [_I32, _I32, _I32, _F32, _P, _I64, _P, _P, _P,
-                                            _P, _P, _P, _P, _P, _P, _P]),
+                                            _P, _P, _P, _P, _P, _P, _P, _I32]),
         "oracle_route": (None, [_I64, _I32, _I32, _P, _P, _P]),
         "oracle_router_logits": (None, [_I64, _I32, _I32, _P, _P, _P]),
         "oracle_capacity": (_I64, [_F32, _I64, _I32, _I32]),
         "oracle_permute": (_I64, [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P]),
         "oracle_act_quant": (None, [_I64, _I32, _P, _P, _P, _P]),
-        "oracle_act_quant_clip": (None, [_I64, _I32, _P, _P, _F32, _F32, _P, _P]),
+        "oracle_act_quant_clip": (None, [_I64, _I32, _P, _P, _F32, _F32, _I32, _P, _P]),
         "oracle_clip_threshold": (_F32, [_I64, _I32, _P, _P, _F32]),
         "oracle_percentile_rank": (_I64, [ctypes.c_double, _I64]),
         "oracle_expert_rows": (None, [_I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                      _P, _P, _P, _P, _P, _P, _P]),
+                                      _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
         "oracle_combine": (None, [_I64, _P, _I32, _I32, _P, _P, _P, _P, _P]),
         "oracle_forward": (_I64, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32,
-                                  _P, _P, _P, _P, _P, _F32, _F32,
-                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+                                  _P, _P, _P, _P, _P, _F32, _F32, _I32,
+                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "oracle_num_threads": (ctypes.c_int, []),
     }
     for name, (res, args) in sig.items():
@@ -105,8 +108,32 @@ def quant_rows(v: np.ndarray):
     return q, s
 
 
-def calibrate(calib_x_bf16, w_gate, w_up, w_down, alpha: float, want_smoothed: bool = False):
-    """SmoothQuant calibration + per-output-channel INT8 weight quantisation.
+FMT_INT8, FMT_FP8 = 0, 1
+
+
+def quant_rows_fmt(v: np.ndarray, fmt: int):
+    """Row quantiser of either format; v float32 [rows][n]."""
+    v = _c(v, np.float32)
+    rows, n = v.shape
+    q = np.empty((rows, n), np.int8)
+    s = np.empty(rows, np.float32)
+    _load().oracle_quant_rows_fmt(rows, n, _ptr(v), int(fmt), _ptr(q), _ptr(s))
+    return q, s
+
+
+def e4m3_value(code: int) -> float:
+    return float(_load().oracle_e4m3_value(int(code) & 0xFF))
+
+
+def e4m3_code(t: float) -> int:
+    """Code of a value already inside [-448, 448]."""
+    return int(_load().oracle_e4m3_code(float(np.float32(t))))
+
+
+def calibrate(calib_x_bf16, w_gate, w_up, w_down, alpha: float, want_smoothed: bool = False,
+              fmt: int = FMT_INT8):
+    """SmoothQuant calibration + per-output-channel weight quantisation
+    (INT8 codes, or FP8 e4m3 codes with fmt = FMT_FP8).
 
     calib_x_bf16: uint16 [Nc][H]; w_gate, w_up: float32 [E][F][H];
     w_down: float32 [E][H][F]. Returns a dict with s, inv_s [H], q_gu int8
@@ -124,7 +151,7 @@ def calibrate(calib_x_bf16, w_gate, w_up, w_down, alpha: float, want_smoothed: b
     rc = _load().oracle_calibrate(H, F, E, float(alpha), _ptr(cx), cx.shape[0],
                                   _ptr(wg), _ptr(wu), _ptr(wd), _ptr(out["s"]), _ptr(out["inv_s"]),
                                   _ptr(out["q_gu"]), _ptr(out["sw_gu"]), _ptr(out["q_d"]),
-                                  _ptr(out["sw_d"]), _ptr(out.get("ws_gu")))
+                                  _ptr(out["sw_d"]), _ptr(out.get("ws_gu")), int(fmt))
     if rc != 0:
         raise ValueError("oracle_calibrate failed: %d" % rc)
     return out
@@ -172,7 +199,8 @@ def permute(ids, E: int, cap: int):
                 row_of=row_of[:A].reshape(T, k), kept=int(kept))
 
 
-def act_quant(x_bf16, inv_s, clip: float = 0.0, sat_percentile: float = 0.0):
+def act_quant(x_bf16, inv_s, clip: float = 0.0, sat_percentile: float = 0.0,
+              fmt: int = FMT_INT8):
     """Per-token smoothed INT8 quantisation; x uint16 [T][H] -> qx int8, sx f32 [T].
     clip > 0: static clipping threshold; sat_percentile in (0, 100]: dynamic
     per-token saturation at that percentile of |x * inv_s|."""
@@ -181,11 +209,8 @@ def act_quant(x_bf16, inv_s, clip: float = 0.0, sat_percentile: float = 0.0):
     T, H = x.shape
     qx = np.empty((T, H), np.int8)
     sx = np.empty(T, np.float32)
-    if clip == 0.0 and sat_percentile == 0.0:
-        _load().oracle_act_quant(T, H, _ptr(x), _ptr(inv_s), _ptr(qx), _ptr(sx))
-    else:
-        _load().oracle_act_quant_clip(T, H, _ptr(x), _ptr(inv_s), float(clip),
-                                      float(sat_percentile), _ptr(qx), _ptr(sx))
+    _load().oracle_act_quant_clip(T, H, _ptr(x), _ptr(inv_s), float(clip),
+                                  float(np.float32(sat_percentile)), int(fmt), _ptr(qx), _ptr(sx))
     return qx, sx
 
 
@@ -204,8 +229,10 @@ def percentile_rank(p: float, N: int) -> int:
     return int(_load().oracle_percentile_rank(float(np.float32(p)), int(N)))
 
 
-def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h: bool = True):
-    """Expert FFN for the permuted rows listed in `rows` (sorted positions)."""
+def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h: bool = True,
+                fmt: int = FMT_INT8):
+    """Expert FFN for the permuted rows listed in `rows` (sorted positions).
+    acc1 is int32 for INT8 codes and the exact fp64 sums for FP8 codes."""
     rows = _c(rows, np.int32)
     ids = _c(ids, np.int32)
     T, k = ids.shape
@@ -216,15 +243,16 @@ def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h:
     E, F2, H = q_gu.shape
     F = F2 // 2
     n = rows.shape[0]
-    acc1 = np.empty((n, 2 * F), np.int32) if want_acc1 else None
+    acc1 = np.empty((n, 2 * F), np.int32) if want_acc1 and fmt == FMT_INT8 else None
+    acc1f = np.empty((n, 2 * F), np.float64) if want_acc1 and fmt == FMT_FP8 else None
     h = np.empty((n, F), np.float32) if want_h else None
     qh = np.empty((n, F), np.int8)
     sh = np.empty(n, np.float32)
     y = np.empty((n, H), np.float64)
     _load().oracle_expert_rows(n, _ptr(rows), H, F, k, _ptr(ids), _ptr(sorted_), _ptr(qx), _ptr(sx),
-                               _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d),
-                               _ptr(acc1), _ptr(h), _ptr(qh), _ptr(sh), _ptr(y))
-    return dict(acc1=acc1, h=h, qh=qh, sh=sh, y=y)
+                               _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), int(fmt),
+                               _ptr(acc1), _ptr(acc1f), _ptr(h), _ptr(qh), _ptr(sh), _ptr(y))
+    return dict(acc1=acc1 if fmt == FMT_INT8 else acc1f, h=h, qh=qh, sh=sh, y=y)
 
 
 def combine(tokens, w, row_of, y, y_row_index=None):
@@ -244,7 +272,7 @@ def combine(tokens, w, row_of, y, y_row_index=None):
 
 def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor: float = 0.0,
             want_acc1: bool = True, want_h: bool = True, clip: float = 0.0,
-            sat_percentile: float = 0.0):
+            sat_percentile: float = 0.0, fmt: int = FMT_INT8):
     """The whole layer on the CPU. Returns a dict of every stage's output."""
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
@@ -263,20 +291,26 @@ def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor:
              counts=np.empty(E, np.int32), offsets=np.empty(E + 1, np.int32),
              sorted=np.full(max(A, 1), -1, np.int32), row_of=np.empty((T, k), np.int32),
              qx=np.empty((T, H), np.int8), sx=np.empty(T, np.float32),
-             acc1=np.empty((A, 2 * F), np.int32) if want_acc1 else None,
+             acc1=np.empty((A, 2 * F), np.int32) if want_acc1 and fmt == FMT_INT8 else None,
+             acc1f=np.empty((A, 2 * F), np.float64) if want_acc1 and fmt == FMT_FP8 else None,
              h=np.empty((A, F), np.float32) if want_h else None,
              qh=np.empty((max(A, 1), F), np.int8), sh=np.empty(max(A, 1), np.float32),
              y=np.empty((max(A, 1), H), np.float64), out=np.empty((T, H), np.uint16))
     kept = _load().oracle_forward(
         T, H, F, E, k, _ptr(x), _ptr(lg), _ptr(ids_in), _ptr(w_in), float(capacity_factor),
         _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), _ptr(inv_s), float(clip),
-        float(np.float32(sat_percentile)), _ptr(o["ids"]), _ptr(o["w"]), _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]),
-        _ptr(o["row_of"]), _ptr(o["qx"]), _ptr(o["sx"]), _ptr(o["acc1"]), _ptr(o["h"]),
-        _ptr(o["qh"]), _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]))
+        float(np.float32(sat_percentile)), int(fmt), _ptr(o["ids"]), _ptr(o["w"]),
+        _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]), _ptr(o["row_of"]), _ptr(o["qx"]),
+        _ptr(o["sx"]), _ptr(o["acc1"]), _ptr(o["acc1f"]), _ptr(o["h"]), _ptr(o["qh"]),
+        _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]))
     kept = int(kept)
     o["kept"] = kept
     o["sorted"] = o["sorted"][:kept]
     o["qh"], o["sh"], o["y"] = o["qh"][:kept], o["sh"][:kept], o["y"][:kept]
+    if fmt == FMT_FP8:
+        o["acc1"] = o.pop("acc1f")
+    else:
+        o.pop("acc1f")
     if o["acc1"] is not None:
         o["acc1"] = o["acc1"][:kept]
     if o["h"] is not None:

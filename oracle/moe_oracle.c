@@ -106,6 +106,72 @@ static void quant_row(const float *v, int64_t n, int8_t *q, float *scale) {
   quant_row_at(v, n, row_absmax(v, n), q, scale);
 }
 
+/* ---------------------------------------------------------------- FP8 */
+
+/* OCP FP8 e4m3 ("fn"). [Day0 §二.1]: expert layers are stored in FP8 or INT8;
+ * [Day0 §四]: activations follow the weights' format. Reading: the OCP e4m3
+ * encoding (the one the gfx950 matrix instructions take): sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6);
+ * the code 0x7f (and 0xff) is NaN, there is no infinity, the largest finite
+ * value is 1.75 * 2^8 = 448. The code of a value is its nearest e4m3 value,
+ * ties to the even code, with the sign bit of the value (so -0.0 -> 0x80);
+ * values are clamped to [-448, 448] before, so nothing rounds past 448. */
+double oracle_e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return s ? -v : v;
+}
+
+uint8_t oracle_e4m3_code(float t) {
+  const uint8_t sign = signbit(t) ? 0x80 : 0x00;
+  const double a = fabs((double)t);  /* <= 448 */
+  if (a < ldexp(1.0, -6)) {          /* subnormal binade: steps of 2^-9 */
+    const double q = rint(ldexp(a, 9));   /* 0..8; 8 is the smallest normal */
+    return sign | (uint8_t)q;
+  }
+  int ex;
+  frexp(a, &ex);                     /* a in [2^(ex-1), 2^ex) */
+  const int e = ex - 1;              /* unbiased exponent */
+  double q = rint(ldexp(a, 3 - e));  /* 8..16 steps of 2^(e-3) */
+  int eb = e + 7;
+  if (q == 16.0) { q = 8.0; ++eb; }
+  return sign | (uint8_t)((eb << 3) | ((int)q - 8));
+}
+
+/* The quantiser of either format at a given level. INT8: quant_row_at.
+ * FP8: rr = fl32(448/level), code = e4m3 of clamp(fl32(v*rr), -448, 448),
+ * scale = level/448; a zero level gives rr = 0 (codes of +-0) and scale 0. */
+static void quant_row_fmt_at(const float *v, int64_t n, float level, int32_t fmt, int8_t *q,
+                             float *scale) {
+  if (fmt == 0) {
+    quant_row_at(v, n, level, q, scale);
+    return;
+  }
+  const float rr = level > 0.0f ? 448.0f / level : 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float t = v[i] * rr;
+    t = fminf(fmaxf(t, -448.0f), 448.0f);
+    q[i] = (int8_t)oracle_e4m3_code(t);
+  }
+  *scale = level / 448.0f;
+}
+
+static void quant_row_fmt(const float *v, int64_t n, int32_t fmt, int8_t *q, float *scale) {
+  quant_row_fmt_at(v, n, row_absmax(v, n), fmt, q, scale);
+}
+
+/* Code value: INT8 codes as integers, FP8 codes decoded. */
+static double code_value(int8_t c, int32_t fmt) {
+  return fmt == 0 ? (double)c : oracle_e4m3_value((uint8_t)c);
+}
+
+/* Exported forms used by the pins: rows of either format. */
+void oracle_quant_rows_fmt(int64_t rows, int64_t n, const float *v, int32_t fmt, int8_t *q,
+                           float *scale) {
+  for (int64_t r = 0; r < rows; ++r) quant_row_fmt(v + r * n, n, fmt, q + r * n, scale + r);
+}
+
 /* Exported form of the quantiser, one row after another (used by the pins). */
 void oracle_quant_rows(int64_t rows, int64_t n, const float *v, int8_t *q, float *scale) {
   for (int64_t r = 0; r < rows; ++r) quant_row(v + r * n, n, q + r * n, scale + r);
@@ -137,7 +203,7 @@ int oracle_calibrate(int32_t H, int32_t F, int32_t E, float alpha,
                      const float *w_gate, const float *w_up, const float *w_down,
                      float *s, float *inv_s,
                      int8_t *q_gu, float *sw_gu, int8_t *q_d, float *sw_d,
-                     float *ws_gu) {
+                     float *ws_gu, int32_t fmt) {
   if (H <= 0 || F <= 0 || E <= 0 || n_calib < 0) return -1;
   double a = (double)alpha;
   #pragma omp parallel for schedule(static)
@@ -168,10 +234,11 @@ int oracle_calibrate(int32_t H, int32_t F, int32_t E, float alpha,
       const float *src = n < F ? w_gate + (e * F + n) * H : w_up + (e * F + (n - F)) * H;
       for (int32_t j = 0; j < H; ++j) row[j] = src[j] * s[j];
       if (ws_gu) memcpy(ws_gu + r * H, row, sizeof(float) * (size_t)H);
-      quant_row(row, H, q_gu + r * H, sw_gu + r);
+      quant_row_fmt(row, H, fmt, q_gu + r * H, sw_gu + r);
     }
     #pragma omp for schedule(static)
-    for (int64_t r = 0; r < (int64_t)E * H; ++r) quant_row(w_down + r * F, F, q_d + r * F, sw_d + r);
+    for (int64_t r = 0; r < (int64_t)E * H; ++r)
+      quant_row_fmt(w_down + r * F, F, fmt, q_d + r * F, sw_d + r);
     free(row);
   }
   return 0;
@@ -355,7 +422,7 @@ static float clip_level(const float *v, int32_t n, float clip, float sat_p, floa
  * must not set the range of others) after SmoothQuant's rescaling.
  * xs_j = x_j * inv_s_j in fp32, then the quantiser above over the row. */
 void oracle_act_quant_clip(int64_t T, int32_t H, const uint16_t *x, const float *inv_s,
-                           float clip, float sat_p, int8_t *qx, float *sx) {
+                           float clip, float sat_p, int32_t fmt, int8_t *qx, float *sx) {
   #pragma omp parallel
   {
     float *row = (float *)malloc(sizeof(float) * (size_t)H);
@@ -363,7 +430,7 @@ void oracle_act_quant_clip(int64_t T, int32_t H, const uint16_t *x, const float 
     #pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
       for (int32_t j = 0; j < H; ++j) row[j] = bf16_bits_to_f32(x[t * H + j]) * inv_s[j];
-      quant_row_at(row, H, clip_level(row, H, clip, sat_p, tmp), qx + t * H, sx + t);
+      quant_row_fmt_at(row, H, clip_level(row, H, clip, sat_p, tmp), fmt, qx + t * H, sx + t);
     }
     free(row);
     free(tmp);
@@ -372,7 +439,7 @@ void oracle_act_quant_clip(int64_t T, int32_t H, const uint16_t *x, const float 
 
 void oracle_act_quant(int64_t T, int32_t H, const uint16_t *x, const float *inv_s,
                       int8_t *qx, float *sx) {
-  oracle_act_quant_clip(T, H, x, inv_s, 0.0f, 0.0f, qx, sx);
+  oracle_act_quant_clip(T, H, x, inv_s, 0.0f, 0.0f, 0, qx, sx);
 }
 
 /* ------------------------------------------------------------ expert row */
@@ -393,29 +460,46 @@ void oracle_act_quant(int64_t T, int32_t H, const uint16_t *x, const float *inv_
  * acc1 and h may be NULL. */
 void oracle_expert_row(int32_t H, int32_t F, const int8_t *qx_row, float sx,
                        const int8_t *q_gu_e, const float *sw_gu_e,
-                       const int8_t *q_d_e, const float *sw_d_e,
-                       int32_t *acc1, float *h, int8_t *qh, float *sh, double *y) {
-  int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(2 * F));
+                       const int8_t *q_d_e, const float *sw_d_e, int32_t fmt,
+                       int32_t *acc1, double *acc1f, float *h, int8_t *qh, float *sh, double *y) {
+  /* acc: exact integer sums for INT8 codes (int32, |sum| <= K * 127^2), exact
+   * fp64 sums of the decoded products for FP8 codes. */
+  double *acc = (double *)malloc(sizeof(double) * (size_t)(2 * F));
   float *hf = (float *)malloc(sizeof(float) * (size_t)F);
   for (int32_t n = 0; n < 2 * F; ++n) {
     const int8_t *wr = q_gu_e + (int64_t)n * H;
-    int32_t s = 0;
-    for (int32_t j = 0; j < H; ++j) s += (int32_t)qx_row[j] * (int32_t)wr[j];
-    acc[n] = s;
+    if (fmt == 0) {
+      int32_t s = 0;
+      for (int32_t j = 0; j < H; ++j) s += (int32_t)qx_row[j] * (int32_t)wr[j];
+      acc[n] = (double)s;
+    } else {
+      double s = 0.0;
+      for (int32_t j = 0; j < H; ++j) s += code_value(qx_row[j], fmt) * code_value(wr[j], fmt);
+      acc[n] = s;
+    }
   }
   for (int32_t f = 0; f < F; ++f) {
-    double g = (double)acc[f] * (double)sx * (double)sw_gu_e[f];
-    double u = (double)acc[F + f] * (double)sx * (double)sw_gu_e[F + f];
+    double g = acc[f] * (double)sx * (double)sw_gu_e[f];
+    double u = acc[F + f] * (double)sx * (double)sw_gu_e[F + f];
     hf[f] = (float)(g / (1.0 + exp(-g)) * u);
   }
-  quant_row(hf, F, qh, sh);
+  quant_row_fmt(hf, F, fmt, qh, sh);
   for (int32_t n = 0; n < H; ++n) {
     const int8_t *wr = q_d_e + (int64_t)n * F;
-    int32_t s = 0;
-    for (int32_t f = 0; f < F; ++f) s += (int32_t)qh[f] * (int32_t)wr[f];
-    y[n] = (double)s * (double)(*sh) * (double)sw_d_e[n];
+    double s = 0.0;
+    if (fmt == 0) {
+      int32_t si = 0;
+      for (int32_t f = 0; f < F; ++f) si += (int32_t)qh[f] * (int32_t)wr[f];
+      s = (double)si;
+    } else {
+      for (int32_t f = 0; f < F; ++f) s += code_value(qh[f], fmt) * code_value(wr[f], fmt);
+    }
+    y[n] = s * (double)(*sh) * (double)sw_d_e[n];
   }
-  if (acc1) memcpy(acc1, acc, sizeof(int32_t) * (size_t)(2 * F));
+  for (int32_t n = 0; n < 2 * F; ++n) {
+    if (acc1) acc1[n] = (int32_t)acc[n];
+    if (acc1f) acc1f[n] = acc[n];
+  }
   if (h) memcpy(h, hf, sizeof(float) * (size_t)F);
   free(acc);
   free(hf);
@@ -428,8 +512,9 @@ void oracle_expert_rows(int64_t nrows, const int32_t *rows, int32_t H, int32_t F
                         const int32_t *ids, const int32_t *sorted,
                         const int8_t *qx, const float *sx,
                         const int8_t *q_gu, const float *sw_gu,
-                        const int8_t *q_d, const float *sw_d,
-                        int32_t *acc1, float *h, int8_t *qh, float *sh, double *y) {
+                        const int8_t *q_d, const float *sw_d, int32_t fmt,
+                        int32_t *acc1, double *acc1f, float *h, int8_t *qh, float *sh,
+                        double *y) {
   #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t r = 0; r < nrows; ++r) {
     int32_t a = sorted[rows[r]];
@@ -437,9 +522,9 @@ void oracle_expert_rows(int64_t nrows, const int32_t *rows, int32_t H, int32_t F
     int64_t e = ids[a];
     oracle_expert_row(H, F, qx + t * H, sx[t],
                       q_gu + e * 2 * F * (int64_t)H, sw_gu + e * 2 * F,
-                      q_d + e * (int64_t)H * F, sw_d + e * H,
-                      acc1 ? acc1 + r * 2 * F : NULL, h ? h + r * F : NULL,
-                      qh + r * F, sh + r, y + r * H);
+                      q_d + e * (int64_t)H * F, sw_d + e * H, fmt,
+                      acc1 ? acc1 + r * 2 * F : NULL, acc1f ? acc1f + r * 2 * F : NULL,
+                      h ? h + r * F : NULL, qh + r * F, sh + r, y + r * H);
   }
 }
 
@@ -484,11 +569,11 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                        const int32_t *ids_in, const float *w_in, float capacity_factor,
                        const int8_t *q_gu, const float *sw_gu,
                        const int8_t *q_d, const float *sw_d, const float *inv_s,
-                       float clip, float sat_p,
+                       float clip, float sat_p, int32_t fmt,
                        int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
                        int32_t *sorted, int32_t *row_of, int8_t *qx, float *sx,
-                       int32_t *acc1, float *h, int8_t *qh, float *sh, double *y,
-                       uint16_t *out) {
+                       int32_t *acc1, double *acc1f, float *h, int8_t *qh, float *sh,
+                       double *y, uint16_t *out) {
   int64_t A = T * k;
   if (logits) oracle_route(T, E, k, logits, ids, w);
   else {
@@ -497,11 +582,11 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
   }
   int64_t cap = oracle_capacity(capacity_factor, T, k, E);
   int64_t kept = oracle_permute(T, E, k, ids, cap, counts, offsets, sorted, row_of);
-  oracle_act_quant_clip(T, H, x, inv_s, clip, sat_p, qx, sx);
+  oracle_act_quant_clip(T, H, x, inv_s, clip, sat_p, fmt, qx, sx);
   int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(kept > 0 ? kept : 1));
   for (int64_t i = 0; i < kept; ++i) rows[i] = (int32_t)i;
-  oracle_expert_rows(kept, rows, H, F, k, ids, sorted, qx, sx, q_gu, sw_gu, q_d, sw_d,
-                     acc1, h, qh, sh, y);
+  oracle_expert_rows(kept, rows, H, F, k, ids, sorted, qx, sx, q_gu, sw_gu, q_d, sw_d, fmt,
+                     acc1, acc1f, h, qh, sh, y);
   free(rows);
   oracle_combine(T, NULL, H, k, w, row_of, NULL, y, out);
   return kept;

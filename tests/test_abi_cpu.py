@@ -87,6 +87,15 @@ def test_forward_validation(lib):
     dbg = m.moe_w8a8_debug()
     dbg.gemm_path = 3
     assert _fwd(d, dbg=dbg) == m.MOE_W8A8_ERR_INVALID
+    badf = _weights()
+    badf.format = 2
+    assert _fwd(d, weights=badf) == m.MOE_W8A8_ERR_INVALID               # unknown format
+    bads = _weights()
+    for p in (-1.0, 100.5, float("nan")):
+        bads.act_sat_percentile = p
+        assert _fwd(d, weights=bads) == m.MOE_W8A8_ERR_INVALID
+    bads.act_sat_percentile = 90.0                                       # H 256: m = 26 > 16
+    assert _fwd(d, weights=bads) == m.MOE_W8A8_ERR_UNSUPPORTED
     assert _fwd(m.dims(320, 512, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED      # H % 256
     assert _fwd(m.dims(256, 500, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED      # F % 128
     assert _fwd(m.dims(256, 512, 64, 33)) == m.MOE_W8A8_ERR_UNSUPPORTED    # k > 32
@@ -128,6 +137,22 @@ def test_calibrate_validation(lib):
     assert cal(d=m.dims(256, 500, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED
     assert cal(ws_bytes=16) == m.MOE_W8A8_ERR_WORKSPACE
     assert cal(ws=None) == m.MOE_W8A8_ERR_WORKSPACE
+    badf = _weights()
+    badf.format = 7
+    assert cal(out=badf) == m.MOE_W8A8_ERR_INVALID
+
+
+def test_calibrate_clip_validation(lib):
+    d = m.dims(256, 512, 8, 2)
+    def cc(p=99.9, cx=FAKE, n=64, inv=FAKE, out=FAKE, d=d):
+        return m.moe_w8a8_calibrate_clip(d, p, cx, n, inv, out, stream=0)
+    for p in (0.0, -1.0, 100.1, float("nan")):
+        assert cc(p=p) == m.MOE_W8A8_ERR_INVALID
+    assert cc(cx=None) == m.MOE_W8A8_ERR_INVALID
+    assert cc(n=-1) == m.MOE_W8A8_ERR_INVALID
+    assert cc(inv=None) == m.MOE_W8A8_ERR_INVALID
+    assert cc(out=None) == m.MOE_W8A8_ERR_INVALID
+    assert cc(d=m.dims(320, 512, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

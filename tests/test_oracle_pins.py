@@ -283,6 +283,115 @@ def test_static_clip_level_and_off_values():
         assert np.array_equal(q0, q1) and np.array_equal(s0, s1)
 
 
+# --------------------------------------------------------------- FP8 e4m3
+
+def _e4m3_table():
+    """Values of the 256 e4m3 codes from the bit fields, as exact Fractions
+    (None for the two NaN codes)."""
+    tab = []
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            tab.append(None)
+            continue
+        v = Fraction(m, 8) * Fraction(1, 2 ** 6) if e == 0 else \
+            (1 + Fraction(m, 8)) * (Fraction(2) ** (e - 7))
+        tab.append(-v if s else v)
+    return tab
+
+
+def test_e4m3_decode_table():
+    tab = _e4m3_table()
+    for c in range(256):
+        got = oracle.e4m3_value(c)
+        if tab[c] is None:
+            assert math.isnan(got)
+        else:
+            assert got == float(tab[c]), hex(c)
+            if c == 0x80:
+                assert math.copysign(1.0, got) < 0
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6 and oracle.e4m3_value(0x38) == 1.0
+
+
+def _e4m3_nearest(t: float) -> int:
+    """Brute force: the finite code nearest to t (ties to the even code),
+    with t's sign bit."""
+    tab = _e4m3_table()
+    a = abs(Fraction(t))
+    best, bd = 0, None
+    for c in range(0x7F):
+        d = abs(tab[c] - a)
+        if bd is None or d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    return best | (0x80 if math.copysign(1.0, t) < 0 else 0)
+
+
+def test_e4m3_encode_bruteforce():
+    """Every code value, every midpoint (ties to even) and its fp32
+    neighbours, signed zeros and random values in [-448, 448]."""
+    tab = _e4m3_table()
+    vals = [0.0, -0.0, 448.0, -448.0, 2.0 ** -10, 3 * 2.0 ** -10, 1e-30, -1e-30]
+    for c in range(0x7F):
+        vals.append(float(tab[c]))
+        if c < 0x7E:
+            mid = np.float32((tab[c] + tab[c + 1]) / 2)
+            vals += [float(mid), float(np.nextafter(mid, np.float32(0))),
+                     float(np.nextafter(mid, np.float32(1e9))), -float(mid)]
+    rng = np.random.default_rng(31)
+    vals += [float(v) for v in rng.uniform(-448, 448, 3000).astype(np.float32)]
+    vals += [float(v) for v in (rng.standard_normal(500) * 1e-2).astype(np.float32)]
+    for t in vals:
+        assert oracle.e4m3_code(t) == _e4m3_nearest(float(np.float32(t))), t
+
+
+def test_fp8_quantiser_roundtrip_and_max():
+    """Row maximum codes to +-448; each value lands within half an e4m3
+    step of v * 448 / max (fp32 rounding slack aside); zero row: scale 0."""
+    rng = np.random.default_rng(32)
+    v = (rng.standard_normal((20, 300)) * rng.lognormal(0, 2, (20, 1))).astype(np.float32)
+    q, sc = oracle.quant_rows_fmt(v, oracle.FMT_FP8)
+    for r in range(v.shape[0]):
+        amax = np.max(np.abs(v[r]))
+        assert sc[r] == np.float32(amax / np.float32(448.0))
+        i = int(np.argmax(np.abs(v[r])))
+        assert int(q[r].view(np.uint8)[i]) in (0x7E, 0xFE)
+        rr = np.float32(448.0) / np.float32(amax)
+        t = np.clip((v[r] * rr).astype(np.float32), -448, 448).astype(np.float64)
+        dec = np.array([oracle.e4m3_value(c) for c in q[r]])
+        step = np.where(np.abs(t) < 2.0 ** -6, 2.0 ** -9,
+                        2.0 ** (np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -6))) - 3))
+        assert np.all(np.abs(t - dec) <= step / 2 * (1 + 1e-6))
+    q0, s0 = oracle.quant_rows_fmt(np.zeros((1, 8), np.float32), oracle.FMT_FP8)
+    assert s0[0] == 0.0 and np.all(q0 == 0)
+
+
+def test_fp8_expert_row_exact_sums():
+    """FP8 GEMM sums equal the fp64 dot products of the decoded codes, and
+    GEMM2's y recovers them through sh and the weight scale."""
+    rng = np.random.default_rng(33)
+    H, F, E, T, k = 128, 64, 2, 5, 1
+    lut = np.array([oracle.e4m3_value(c) for c in range(256)])
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    cal = dict(q_gu=rng.choice(finite, (E, 2 * F, H)).astype(np.uint8).view(np.int8),
+               sw_gu=rng.uniform(1e-3, 1e-2, (E, 2 * F)).astype(np.float32),
+               q_d=rng.choice(finite, (E, H, F)).astype(np.uint8).view(np.int8),
+               sw_d=rng.uniform(1e-3, 1e-2, (E, H)).astype(np.float32))
+    qx = rng.choice(finite, (T, H)).astype(np.uint8).view(np.int8)
+    sx = rng.uniform(1e-3, 1e-2, T).astype(np.float32)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    sorted_ = np.arange(T, dtype=np.int32)
+    r = oracle.expert_rows(np.arange(T, dtype=np.int32), ids, sorted_, qx, sx, cal,
+                           fmt=oracle.FMT_FP8)
+    for t in range(T):
+        e = ids[t, 0]
+        want = lut[cal["q_gu"][e].view(np.uint8)] @ lut[qx[t].view(np.uint8)]
+        np.testing.assert_allclose(r["acc1"][t], want, rtol=1e-13, atol=1e-300)
+        acc2 = lut[cal["q_d"][e].view(np.uint8)] @ lut[r["qh"][t].view(np.uint8)]
+        np.testing.assert_allclose(r["y"][t], acc2 * np.float64(r["sh"][t]) * cal["sw_d"][e],
+                                   rtol=1e-12)
+
+
 def test_permute_golden(golden_dir):
     g = _load(golden_dir, "permute_capacity.json")
     ids = np.array(g["ids"], np.int32)
@@ -505,6 +614,28 @@ def _fp64_layer(x_f32, wg, wu, wd, ids, w, row_of):
             h = g / (1 + np.exp(-g)) * u
             out[t] += float(w[t, j]) * (wd[e].astype(np.float64) @ h)
     return out
+
+
+@pytest.mark.parametrize("case", ["dense", "tiny", "tiny_outliers"])
+def test_fp8_layer_close_to_unquantised(case):
+    """The FP8 (e4m3) layer is within FP8 quantisation error of the fp64
+    unquantised layer (3 mantissa bits: a few 1e-2 relative RMS), and
+    swapping gate and up is far outside it."""
+    over = dict(dense=dict(E=1, k=1, T=24), tiny=dict(),
+                tiny_outliers=dict(outlier_frac=0.02, outlier_mult=50.0))[case]
+    wl = synth.workload("tiny", **over)
+    L = synth.make_layer(wl)
+    I = synth.make_inputs(wl, L)
+    cal = oracle.calibrate(L.calib_x, L.w_gate, L.w_up, L.w_down, wl.alpha, fmt=oracle.FMT_FP8)
+    o = oracle.forward(I.x, cal, wl.k, logits=I.logits, fmt=oracle.FMT_FP8)
+    x64 = bf16_bits_to_f32(I.x).astype(np.float64)
+    ref = _fp64_layer(x64, L.w_gate, L.w_up, L.w_down, o["ids"], o["w"], o["row_of"])
+    got = bf16_bits_to_f32(o["out"]).astype(np.float64)
+    rel = np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))
+    assert rel < 8e-2, rel
+    swapped = _fp64_layer(x64, L.w_up, L.w_gate, L.w_down, o["ids"], o["w"], o["row_of"])
+    rel_sw = np.sqrt(np.mean((got - swapped) ** 2)) / np.sqrt(np.mean(swapped ** 2))
+    assert rel_sw > 0.3, rel_sw
 
 
 @pytest.mark.parametrize("case", ["dense", "tiny", "tiny_drop", "tiny_outliers"])

@@ -22,6 +22,8 @@ MOE_W8A8_ERR_INVALID = -1
 MOE_W8A8_ERR_UNSUPPORTED = -2
 MOE_W8A8_ERR_WORKSPACE = -3
 MOE_W8A8_ERR_HIP = -4
+MOE_W8A8_FORMAT_INT8 = 0
+MOE_W8A8_FORMAT_FP8 = 1
 
 _P = ctypes.c_void_p
 
@@ -34,7 +36,7 @@ class moe_w8a8_dims(ctypes.Structure):
 class moe_w8a8_weights(ctypes.Structure):
     _fields_ = [("w_gate_up", _P), ("w_down", _P), ("s_gate_up", _P), ("s_down", _P),
                 ("smooth", _P), ("inv_smooth", _P), ("w_router", _P), ("act_clip", _P),
-                ("act_sat_percentile", ctypes.c_float)]
+                ("act_sat_percentile", ctypes.c_float), ("format", ctypes.c_int32)]
 
 
 class moe_w8a8_debug(ctypes.Structure):
@@ -156,7 +158,8 @@ def _check(rc: int, what: str):
 class MoEW8A8:
     """Quantised layer on one device (torch tensors for memory and streams)."""
 
-    def __init__(self, hidden: int, ffn: int, num_experts: int, top_k: int, device="cuda"):
+    def __init__(self, hidden: int, ffn: int, num_experts: int, top_k: int, device="cuda",
+                 fp8: bool = False):
         import torch
         load_library()
         self.d = dims(hidden, ffn, num_experts, top_k)
@@ -171,7 +174,8 @@ class MoEW8A8:
         self.inv_smooth = torch.empty(H, dtype=torch.float32, **kw)
         self.weights = moe_w8a8_weights(*(t.data_ptr() for t in (
             self.w_gate_up, self.w_down, self.s_gate_up, self.s_down, self.smooth,
-            self.inv_smooth)), None, None, 0.0)
+            self.inv_smooth)), None, None, 0.0,
+            MOE_W8A8_FORMAT_FP8 if fp8 else MOE_W8A8_FORMAT_INT8)
         self.w_router = None
         self.act_clip = torch.zeros(1, dtype=torch.float32, **kw)
         self._ws = None

@@ -143,6 +143,8 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
   if (!out->w_gate_up || !out->w_down || !out->s_gate_up || !out->s_down || !out->smooth ||
       !out->inv_smooth)
     return MOE_W8A8_ERR_INVALID;
+  if (out->format != MOE_W8A8_FORMAT_INT8 && out->format != MOE_W8A8_FORMAT_FP8)
+    return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts;
   if (!workspace || workspace_bytes < calib_ws_bytes(H)) return MOE_W8A8_ERR_WORKSPACE;
@@ -152,7 +154,8 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
   MOE_CHECK(launch_calib_colmax(calib_x, n_calib, w_gate, w_up, H, F, E, ax, aw, st));
   MOE_CHECK(launch_calib_smooth(ax, aw, alpha, H, out->smooth, out->inv_smooth, st));
   MOE_CHECK(launch_calib_quant(w_gate, w_up, w_down, out->smooth, H, F, E, out->w_gate_up,
-                               out->s_gate_up, out->w_down, out->s_down, st));
+                               out->s_gate_up, out->w_down, out->s_down,
+                               out->format == MOE_W8A8_FORMAT_FP8, st));
   return MOE_W8A8_OK;
 }
 
@@ -176,6 +179,9 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   if (isnan(capacity_factor)) return MOE_W8A8_ERR_INVALID;
   const float sat_p = wt->act_sat_percentile;
   if (!(sat_p == 0.0f || (sat_p > 0.0f && sat_p <= 100.0f))) return MOE_W8A8_ERR_INVALID;
+  if (wt->format != MOE_W8A8_FORMAT_INT8 && wt->format != MOE_W8A8_FORMAT_FP8)
+    return MOE_W8A8_ERR_INVALID;
+  const bool fp8 = wt->format == MOE_W8A8_FORMAT_FP8;
   if (dbg && (dbg->gemm_path < 0 || dbg->gemm_path > 2)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts, k = d->top_k;
@@ -246,7 +252,7 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   if (small) {
     MOE_CHECK(launch_prologue_small(lp, topk_ids, topk_w, (int)T, E, k, capacity, ids,
                                     wts, counts, offsets, poffsets, mtile_off, sorted, row_of,
-                                    (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, ac, st,
+                                    (int)L.P, x, wt->inv_smooth, H, qx, sx, amax, ac, fp8, st,
                                     tm(kRoute)));
   } else {
     MOE_CHECK(launch_route_hist(lp, topk_ids, topk_w, T, E, k, ids, wts, blk_hist,
@@ -257,28 +263,30 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
                              tm(kScatter)));
   }
   if (path == 1) {
-    if (!small) MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, st, tm(kActQ)));
+    if (!small)
+      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st, tm(kActQ)));
     MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, poffsets, offsets, wt->w_gate_up,
-                                  wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
+                                  wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st, tm(kG1)));
   } else {
     // GEMM1's tiled operand is gathered from qx (stage "activation quant" is
     // timed from the start of the quantisation to the end of the gather).
     // Writing the codes straight into the permuted tiles from the
     // quantisation kernel scatters 16-byte pieces and measured 2.5x slower.
     if (!small)
-      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, st, tm(kActQ, true, false)));
+      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st,
+                                 tm(kActQ, true, false)));
     MOE_CHECK(launch_gather_tiles(qx, sx, sorted, k, poffsets, E, L.P, H, a1, rs, st,
                                   tm(kActQ, small, true)));
     MOE_CHECK(launch_gemm1_tiled(a1, rs, counts, poffsets, offsets, mtile_off, A, wt->w_gate_up,
-                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, st, tm(kG1)));
+                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st, tm(kG1)));
   }
-  MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, st, tm(kReq)));
+  MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, fp8, st, tm(kReq)));
   if (path == 1)
     MOE_CHECK(launch_gemm2_stream(qh, sh, counts, poffsets, wt->w_down, wt->s_down, H, F, E, y,
-                                  st, tm(kG2)));
+                                  fp8, st, tm(kG2)));
   else
     MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, poffsets, mtile_off, A, wt->w_down, wt->s_down,
-                                 H, F, E, y, st, tm(kG2)));
+                                 H, F, E, y, fp8, st, tm(kG2)));
   MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st, tm(kComb)));
 
   if (dbg) {

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void smooth_kernel(const uint32_t *__restrict_
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const float *__restrict__ wg, const float *__restrict__ wu, const float *__restrict__ wd,
     const float *__restrict__ s, int H, int F, int E, int8_t *__restrict__ w_gu,
-    float *__restrict__ s_gu, int8_t *__restrict__ w_d, float *__restrict__ s_d) {
+    float *__restrict__ s_gu, int8_t *__restrict__ w_d, float *__restrict__ s_d, bool fp8) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t n_gu = (int64_t)E * 2 * F;
@@ -107,16 +107,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     }
   }
   amax = wave_max(amax);
-  if (lane == 0) *scale = amax / 127.0f;
-  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float qmax = fp8 ? kFp8Max : 127.0f;
+  if (lane == 0) *scale = amax / qmax;
+  const float rr = amax > 0.0f ? qmax / amax : 0.0f;
   for (int c = lane; c < (K >> 4); c += 64) {
     const int kk = c * 16;
-    uint32_t p[4] = {0u, 0u, 0u, 0u};
+    uint32_t p[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = src[kk + i];
-      if (gu) v = v * s[kk + i];
-      p[i >> 2] |= (uint32_t)(q8(v, rr) & 0xff) << (8 * (i & 3));
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = src[kk + 4 * i + j];
+        if (gu) v[j] = v[j] * s[kk + 4 * i + j];
+      }
+      p[i] = codes4(v, rr, fp8);
     }
     int8_t *d = dst + frag_tile(n >> 4, kk >> 6, K) + ((((kk & 63) >> 4) << 4) + (n & 15)) * 16;
     *reinterpret_cast<v4i *>(d) = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
@@ -192,10 +197,10 @@ hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alp
 
 hipError_t launch_calib_quant(const float *w_gate, const float *w_up, const float *w_down,
                               const float *s, int H, int F, int E, int8_t *w_gu, float *s_gu,
-                              int8_t *w_d, float *s_d, hipStream_t st) {
+                              int8_t *w_d, float *s_d, bool fp8, hipStream_t st) {
   const int64_t rows = (int64_t)E * 2 * F + (int64_t)E * H;
   quant_rows_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st>>>(
-      w_gate, w_up, w_down, s, H, F, E, w_gu, s_gu, w_d, s_d);
+      w_gate, w_up, w_down, s, H, F, E, w_gu, s_gu, w_d, s_d, fp8);
   return hipGetLastError();
 }
 

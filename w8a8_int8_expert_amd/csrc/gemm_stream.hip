@@ -7,7 +7,8 @@
 // Every block streams one panel of one expert's fragment-tiled weights
 // exactly once, from HBM, as contiguous 1 KB wavefront loads, and multiplies
 // it with all rows routed to that expert (INT8 x INT8 -> INT32 on
-// v_mfma_i32_16x16x64_i8). The weight panel is the MFMA A operand (16 output
+// v_mfma_i32_16x16x64_i8; FP8 codes: -> fp32 on the 16x16x128 FP8
+// instruction, "超大规模模型推理的Day0适配实践" §二.1 and §四). The weight panel is the MFMA A operand (16 output
 // channels), the token rows the B operand (16 rows per tile), so the few
 // rows of a decode step cost no extra weight traffic.
 //
@@ -46,8 +47,14 @@ struct StreamArgs {
   int32_t *acc1_dbg;        // GEMM1 only, may be NULL; dense rows
 };
 
-template <bool kGateUp, int NPW, int KS, int U>
+// Accumulators: INT32 for INT8 codes, fp32 for FP8 codes.
+template <bool kF8> struct Acc16 { typedef v4i T; };
+template <> struct Acc16<true> { typedef v4f T; };
+
+template <bool kGateUp, int NPW, int KS, int U, bool kF8>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
+  typedef typename Acc16<kF8>::T Acc;
+  static_assert(!kF8 || U % 2 == 0, "FP8 pairs k-tiles");
   constexpr int NA = kGateUp ? 2 * NPW : NPW;  // weight panels per group
   constexpr int NG = 4 / KS;                   // panel groups per block
   const int e = blockIdx.y;
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
     const int nt = kGateUp ? (i < NPW ? u0 + i : (F >> 4) + u0 + i - NPW) : u0 + i;
     wp[i] = wexp + frag_tile(nt, 0, K) + lane * 16;
   }
-  __shared__ v4i red[KS > 1 ? 4 : 1][KS > 1 ? NA * kRT : 1][64];
+  __shared__ Acc red[KS > 1 ? 4 : 1][KS > 1 ? NA * kRT : 1][64];
 
   for (int base = 0; base < R; base += 16 * kRT) {
     const int8_t *bp[kRT];
@@ -86,11 +93,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
       }
     }
     const int astep = kGateUp ? 64 : 1024;  // bytes per k tile of the operand row
-    v4i acc[NA][kRT];
+    Acc acc[NA][kRT];
 #pragma unroll
     for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = v4i{0, 0, 0, 0};
+      for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = Acc{0, 0, 0, 0};
     // This wavefront's k-tiles, U at a time: all loads of a batch are issued
     // before its MFMAs, so U*NA weight tiles are in flight per wavefront.
     const int nk = (KT - ks + KS - 1) / KS;
@@ -104,11 +111,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
         bf[rt] = bv[rt] ? *reinterpret_cast<const v4i *>(bp[rt] + (size_t)kt * astep)
                         : v4i{0, 0, 0, 0};
     };
-    auto mma = [&](const v4i *af, const v4i *bf) {
+    // INT8: one k-tile per v_mfma_i32_16x16x64_i8. FP8: two k-tiles per
+    // v_mfma_scale_f32_16x16x128_f8f6f4 (a lone last tile is paired with zeros).
+    auto mma = [&](const v4i *af, const v4i *bf, const v4i *af2, const v4i *bf2) {
 #pragma unroll
       for (int i = 0; i < NA; ++i)
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) acc[i][rt] = mfma16(af[i], bf[rt], acc[i][rt]);
+        for (int rt = 0; rt < kRT; ++rt) {
+          if constexpr (kF8)
+            acc[i][rt] = mfma16f8(af[i], af2[i], bf[rt], bf2[rt], acc[i][rt]);
+          else
+            acc[i][rt] = mfma16(af[i], bf[rt], acc[i][rt]);
+        }
     };
     int it = 0;
     for (; it + U <= nk; it += U) {
@@ -116,12 +130,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) load(it + u, af[u], bf[u]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) mma(af[u], bf[u]);
+      for (int u = 0; u < U; u += kF8 ? 2 : 1) mma(af[u], bf[u], af[u + (kF8 ? 1 : 0)], bf[u + (kF8 ? 1 : 0)]);
     }
     for (; it < nk; ++it) {
-      v4i af[NA], bf[kRT];
+      v4i af[NA], bf[kRT], z[NA > kRT ? NA : kRT];
+#pragma unroll
+      for (int i = 0; i < (NA > kRT ? NA : kRT); ++i) z[i] = v4i{0, 0, 0, 0};
       load(it, af, bf);
-      mma(af, bf);
+      mma(af, bf, z, z);
     }
     if (KS > 1) {
 #pragma unroll
@@ -141,16 +157,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
       const int r = base + rt * 16 + (lane & 15);
       const bool valid = r < R;
       const int row = row0 + r;
-      auto total = [&](int i) -> v4i {
+      auto total = [&](int i) -> Acc {
         if (KS == 1) return acc[i][rt];
-        v4i sum = red[grp * KS][i * kRT + rt][lane];
+        Acc sum = red[grp * KS][i * kRT + rt][lane];
 #pragma unroll
         for (int w = 1; w < KS; ++w) sum += red[grp * KS + w][i * kRT + rt][lane];
         return sum;
       };
       if (kGateUp) {
         float hmax = 0.0f;
-        const v4i g = total(q), u = total(NPW + q);
+        const Acc g = total(q), u = total(NPW + q);
         if (valid) {
           const float sxv = a.act_scale[a.sorted[row] / a.k];
           const int f0 = (u0 + q) * 16 + ch0;
@@ -167,15 +183,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const StreamArgs a) {
           *reinterpret_cast<v4f *>(a.out + (size_t)row * F + f0) = hv;
           if (a.acc1_dbg) {
             const size_t drow = (size_t)(a.dense_off[e] + r);
-            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + f0) = g;
-            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + F + f0) = u;
+            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + f0) = __builtin_bit_cast(v4i, g);
+            *reinterpret_cast<v4i *>(a.acc1_dbg + drow * 2 * F + F + f0) =
+                __builtin_bit_cast(v4i, u);
           }
         }
         hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, 16, 64));
         hmax = __builtin_fmaxf(hmax, __shfl_xor(hmax, 32, 64));
         if (valid && lane < 16) atomicMax(a.amax + row, __float_as_uint(hmax));
       } else {
-        const v4i sacc = total(q);
+        const Acc sacc = total(q);
         if (valid) {
           const float shv = a.act_scale[row];
           const int n0 = (u0 + q) * 16 + ch0;
@@ -203,24 +220,31 @@ hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t 
                                const int32_t *counts, const int32_t *offsets,
                                const int32_t *dense_off, const int8_t *w_gu, const float *s_gu,
                                int H, int F, int E, float *h, uint32_t *amax, int32_t *acc1_dbg,
-                               hipStream_t st, Timing tm) {
+                               bool fp8, hipStream_t st, Timing tm) {
   StreamArgs a{};
   a.act = qx; a.act_scale = sx; a.sorted = sorted; a.k = k; a.counts = counts;
   a.offsets = offsets; a.dense_off = dense_off; a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H;
   a.out = h; a.amax = amax; a.acc1_dbg = acc1_dbg;
   const dim3 grid((unsigned)(F / (16 * (4 / kKsGateUp) * kNpwGateUp)), (unsigned)E);
-  return launch_kernel(gemm_stream_kernel<true, kNpwGateUp, kKsGateUp, kUGateUp>, grid, dim3(256), st, tm,
-                       a);
+  if (fp8)
+    return launch_kernel(gemm_stream_kernel<true, kNpwGateUp, kKsGateUp, kUGateUp, true>, grid,
+                         dim3(256), st, tm, a);
+  return launch_kernel(gemm_stream_kernel<true, kNpwGateUp, kKsGateUp, kUGateUp, false>, grid,
+                       dim3(256), st, tm, a);
 }
 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *offsets, const int8_t *w_d, const float *s_d, int H,
-                               int F, int E, float *y, hipStream_t st, Timing tm) {
+                               int F, int E, float *y, bool fp8, hipStream_t st, Timing tm) {
   StreamArgs a{};
   a.act = qh; a.act_scale = sh; a.k = 1; a.counts = counts; a.offsets = offsets; a.w = w_d;
   a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
   const dim3 grid((unsigned)(H / (16 * (4 / kKsDown) * kNpwDown)), (unsigned)E);
-  return launch_kernel(gemm_stream_kernel<false, kNpwDown, kKsDown, kUDown>, grid, dim3(256), st, tm, a);
+  if (fp8)
+    return launch_kernel(gemm_stream_kernel<false, kNpwDown, kKsDown, kUDown, true>, grid,
+                         dim3(256), st, tm, a);
+  return launch_kernel(gemm_stream_kernel<false, kNpwDown, kKsDown, kUDown, false>, grid,
+                       dim3(256), st, tm, a);
 }
 
 }  // namespace moe

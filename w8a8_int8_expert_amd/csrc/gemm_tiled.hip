@@ -5,6 +5,9 @@
 // rather than many small ones; §1.2: INT8 x INT8 with integer accumulation,
 // dequantised afterwards; "一晚上完成MoE模型推理优化…" §4.1: the activation
 // that follows a linear layer is fused into it (SwiGLU in GEMM1's epilogue).
+// FP8 codes ("超大规模模型推理的Day0适配实践" §二.1, §四) use the same tiles and
+// pipeline: the two 32-byte k halves of a stage feed one
+// v_mfma_scale_f32_32x32x64_f8f6f4 with fp32 accumulators.
 //
 // One block (8 wavefronts, two per SIMD) computes a 256-row x 256-column
 // tile of one expert:
@@ -104,8 +107,13 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-template <bool kGateUp>
+// Accumulators: INT32 for INT8 codes, fp32 for FP8 codes.
+template <bool kF8> struct Acc32 { typedef v16i T; };
+template <> struct Acc32<true> { typedef v16f T; };
+
+template <bool kGateUp, bool kF8>
 __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
+  typedef typename Acc32<kF8>::T Acc;
   // All 160 KB: the stage ring, then (after the K loop) the epilogue staging
   // and the row scales.
   __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
       dma16(src[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + dst[t])));
   };
 
-  v16i acc[4][2];
+  Acc acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -200,19 +208,38 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
     else wait_barrier<0>();
     if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
     const int8_t *st = lds + (kt % kStages) * kStageBytes;
+    if constexpr (kF8) {
+      // Both k halves of the stage feed one 32x32x64 FP8 instruction.
+      v4i af[2][4], bf[2][2];
 #pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      v4i af[4], bf[2];
+      for (int hk = 0; hk < 2; ++hk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[hk][i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bf[hk][j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma32f8(af[0][i], af[1][i], bf[0][j], bf[1][j], acc[i][j]);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int hk = 0; hk < 2; ++hk) {
+        v4i af[4], bf[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bf[j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+      }
     }
   }
   // Every wavefront is done with the stage buffers before they are reused.
@@ -245,8 +272,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
         slice[r * kEpiPitch1 + (lane & 31)] = hv;
         if (a.acc1_dbg && m0 + mw + 32 * i + r < R) {
           const size_t row = (size_t)(a.dense_off[e] + m0 + mw + 32 * i + r);
-          a.acc1_dbg[row * 2 * F + f0 + (lane & 31)] = acc[i][0][v];
-          a.acc1_dbg[row * 2 * F + F + f0 + (lane & 31)] = acc[i][1][v];
+          // The element is copied out before its bits are taken: a bit cast
+          // applied to a vector element directly reads element 0.
+          const auto gv = acc[i][0][v], uv = acc[i][1][v];
+          a.acc1_dbg[row * 2 * F + f0 + (lane & 31)] = __builtin_bit_cast(int32_t, gv);
+          a.acc1_dbg[row * 2 * F + F + f0 + (lane & 31)] = __builtin_bit_cast(int32_t, uv);
         }
       }
       // 32 rows x 32 columns: 8 lanes per row, 4 floats each.
@@ -310,7 +340,7 @@ hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *
                               const int32_t *offsets, const int32_t *dense_off,
                               const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st, Timing tm) {
+                              int32_t *acc1_dbg, bool fp8, hipStream_t st, Timing tm) {
   TiledArgs a{};
   a.act = a1; a.row_scale = rs; a.counts = counts;
   a.offsets = offsets; a.dense_off = dense_off; a.mtile_off = mtile_off; a.E = E;
@@ -319,13 +349,14 @@ hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *
   a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H; a.out = h; a.amax = amax;
   a.acc1_dbg = acc1_dbg;
   const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
-  return launch_kernel(gemm_tiled_kernel<true>, grid, dim3(512), st, tm, a);
+  if (fp8) return launch_kernel(gemm_tiled_kernel<true, true>, grid, dim3(512), st, tm, a);
+  return launch_kernel(gemm_tiled_kernel<true, false>, grid, dim3(512), st, tm, a);
 }
 
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E,
-                              float *y, hipStream_t st, Timing tm) {
+                              float *y, bool fp8, hipStream_t st, Timing tm) {
   TiledArgs a{};
   a.act = qh; a.row_scale = sh; a.counts = counts; a.offsets = offsets;
   a.mtile_off = mtile_off; a.E = E;
@@ -333,7 +364,8 @@ hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *
   a.nt = H / 256; a.gn = group_n(a.nt);
   a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
   const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
-  return launch_kernel(gemm_tiled_kernel<false>, grid, dim3(512), st, tm, a);
+  if (fp8) return launch_kernel(gemm_tiled_kernel<false, true>, grid, dim3(512), st, tm, a);
+  return launch_kernel(gemm_tiled_kernel<false, false>, grid, dim3(512), st, tm, a);
 }
 
 }  // namespace moe

@@ -152,7 +152,8 @@ __device__ __forceinline__ uint32_t wave_mth_largest(const uint32_t (&l)[kMaxSat
 // optionally lowered by a clip (§6.4: saturate instead of stretching the scale;
 // "一晚上完成MoE模型推理优化…" §3.2: clip at a percentile), code =
 // rint(fl32(v * fl32(127/level))) clamped to [-127, 127], scale = level/127;
-// a zero level gives scale 0 and codes 0.
+// a zero level gives scale 0 and codes 0. FP8 (e4m3) codes: the same with
+// 448 for 127 and f8x4 for the rounding.
 // One wavefront per row; the row (H bf16) is read once, 16 bytes per lane
 // per chunk, and kept in registers between the max and the code pass while
 // it fits (H <= 64 * 8 * MAXC), re-read otherwise.
@@ -160,7 +161,7 @@ template <int MAXC>
 __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
                                                 const float *__restrict__ inv_s, int H,
                                                 int8_t *__restrict__ qr, float *__restrict__ sx,
-                                                ActClip ac = ActClip{nullptr, 0}) {
+                                                ActClip ac, bool fp8) {
   const int lane = threadIdx.x & 63;
   const int nchunk = H >> 3;
   const bool cached = nchunk <= 64 * MAXC;
@@ -230,18 +231,13 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
     const float t = __uint_as_float(wave_mth_largest(top, ac.sat_m, __float_as_uint(amax)));
     if (t > 0.0f && t < level) level = t;
   }
-  if (lane == 0) *sx = level / 127.0f;
-  const float rr = level > 0.0f ? 127.0f / level : 0.0f;
+  const float qmax = fp8 ? kFp8Max : 127.0f;
+  if (lane == 0) *sx = level / qmax;
+  const float rr = level > 0.0f ? qmax / level : 0.0f;
   auto emit = [&](v4i r, int c) {
     float v[8];
     scale8(r, c, v);
-    uint32_t p0 = 0u, p1 = 0u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p0 |= (uint32_t)(q8(v[j], rr) & 0xff) << (8 * j);
-      p1 |= (uint32_t)(q8(v[4 + j], rr) & 0xff) << (8 * j);
-    }
-    *reinterpret_cast<uint2 *>(qr + c * 8) = make_uint2(p0, p1);
+    *reinterpret_cast<uint2 *>(qr + c * 8) = make_uint2(codes4(v, rr, fp8), codes4(v + 4, rr, fp8));
   };
   if (cached) {
 #pragma unroll

@@ -13,6 +13,8 @@ namespace moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Tokens routed (and histogrammed) per block of the routing kernel.
 constexpr int kRouteTokens = 64;
@@ -65,6 +67,26 @@ __device__ __forceinline__ int q8(float v, float rr) {
   c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
   return (int)c;
 }
+// Code format of the expert path ("超大规模模型推理的Day0适配实践" §二.1:
+// expert layers in INT8 or FP8; §四: activations follow the weights' format).
+// kFp8Max is the largest finite OCP e4m3 value, the level a range maps to.
+constexpr float kFp8Max = 448.0f;
+// Four FP8 (OCP e4m3) codes of fl32(v*rr), packed little-endian: each
+// product is clamped to [-448, 448] first (the conversion itself does not
+// saturate), then rounded to nearest, ties to even, by the hardware
+// conversion (the sign of zero is kept).
+__device__ __forceinline__ uint32_t f8x4(float a, float b, float c, float d, float rr) {
+  auto cl = [&](float v) { return __builtin_fminf(__builtin_fmaxf(v * rr, -kFp8Max), kFp8Max); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return (uint32_t)w;
+}
+// Four codes of v*rr in the given format (INT8: q8; FP8: f8x4).
+__device__ __forceinline__ uint32_t codes4(const float *v, float rr, bool fp8) {
+  if (fp8) return f8x4(v[0], v[1], v[2], v[3], rr);
+  return (uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
+         ((uint32_t)(q8(v[2], rr) & 0xff) << 16) | ((uint32_t)(q8(v[3], rr) & 0xff) << 24);
+}
 // Byte offset of the 1 KB fragment tile (n_tile, k_tile) of a fragment-tiled
 // [N][K] INT8 matrix.
 __device__ __forceinline__ size_t frag_tile(int n_tile, int k_tile, int K) {
@@ -75,16 +97,27 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 __device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ v16i mfma32(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+// FP8 (e4m3) x FP8 -> fp32 with unit block scales (E8M0 127 = 1.0). The
+// 32 bytes a lane gives per operand are two 16-byte k-chunks, a0|a1 and
+// b0|b1: the instruction pairs A and B bytes by the same lane position, so
+// chunks taken alike from both operands (the same INT8-layout k-chunks)
+// make the full dot product, whatever k order the hardware assigns.
+__device__ __forceinline__ v8i cat8(v4i x, v4i y) {
+  return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+__device__ __forceinline__ v4f mfma16f8(v4i a0, v4i a1, v4i b0, v4i b1, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat8(a0, a1), cat8(b0, b1), c, 0, 0, 0,
+                                                          127, 0, 127);
+}
+__device__ __forceinline__ v16f mfma32f8(v4i a0, v4i a1, v4i b0, v4i b1, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat8(a0, a1), cat8(b0, b1), c, 0, 0, 0,
+                                                         127, 0, 127);
 }
 #endif
 
@@ -130,8 +163,8 @@ hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, cons
                                  int32_t *counts, int32_t *offsets, int32_t *poffsets,
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
                                  const uint16_t *x, const float *inv_s, int H, int8_t *qx,
-                                 float *sx, uint32_t *amax, ActClip ac, hipStream_t st,
-                                 Timing tm);
+                                 float *sx, uint32_t *amax, ActClip ac, bool fp8,
+                                 hipStream_t st, Timing tm);
 hipError_t launch_route_hist(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
                              int64_t T, int E, int k, int32_t *ids, float *wts,
                              int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
@@ -148,29 +181,30 @@ hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
                           int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
-                            float *sx, ActClip ac, hipStream_t st, Timing tm);
+                            float *sx, ActClip ac, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
                                float *rs, hipStream_t st, Timing tm);
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
-                          int64_t P, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm);
+                          int64_t P, int F, int8_t *qh, float *sh, bool fp8, hipStream_t st,
+                          Timing tm);
 hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                                const int32_t *counts, const int32_t *poffsets,
                                const int32_t *dense_off, const int8_t *w_gu, const float *s_gu,
                                int H, int F, int E, float *h, uint32_t *amax, int32_t *acc1_dbg,
-                               hipStream_t st, Timing tm);
+                               bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
-                               int F, int E, float *y, hipStream_t st, Timing tm);
+                               int F, int E, float *y, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *counts,
                               const int32_t *offsets, const int32_t *dense_off,
                               const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
                               const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, hipStream_t st, Timing tm);
+                              int32_t *acc1_dbg, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
-                              hipStream_t st, Timing tm);
+                              bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm);
 // stage outputs in dense rows (debug only)
@@ -191,6 +225,6 @@ hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alp
                                float *s, float *inv_s, hipStream_t st);
 hipError_t launch_calib_quant(const float *w_gate, const float *w_up, const float *w_down,
                               const float *s, int H, int F, int E, int8_t *w_gu, float *s_gu,
-                              int8_t *w_d, float *s_d, hipStream_t st);
+                              int8_t *w_d, float *s_d, bool fp8, hipStream_t st);
 
 }  // namespace moe

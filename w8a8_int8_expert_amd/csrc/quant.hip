@@ -14,6 +14,7 @@ namespace moe {
 namespace {
 
 // x bf16 [T][H] -> qx int8 [T][H], sx fp32 [T]. One wavefront per token.
+template <bool kF8>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restrict__ x,
                                                         const float *__restrict__ inv_s,
                                                         int64_t T, int H,
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
                                                         float *__restrict__ sx, ActClip ac) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac);
+  quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, kF8);
 }
 
 // h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
 // exactly one 16-byte chunk of a tile. Rows past the padded row count are
 // left alone; padding rows (max 0) get codes 0 unless their h is undefined,
 // which only rows that are never stored downstream can be.
+template <bool kF8>
 __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ h,
                                                       const uint32_t *__restrict__ amax_bits,
                                                       const int32_t *__restrict__ poffsets, int E,
@@ -42,15 +44,16 @@ __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ 
   const int c0 = blockIdx.y * 256 + (threadIdx.x & 15) * 16;
   if (c0 >= F) return;
   const float amax = __uint_as_float(amax_bits[row]);
-  if (c0 == 0) sh[row] = amax / 127.0f;
-  const float rr = amax > 0.0f ? 127.0f / amax : 0.0f;
+  const float qmax = kF8 ? kFp8Max : 127.0f;
+  if (c0 == 0) sh[row] = amax / qmax;
+  const float rr = amax > 0.0f ? qmax / amax : 0.0f;
   const float *hr = h + (size_t)row * F + c0;
   v4i q;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const v4f v = *reinterpret_cast<const v4f *>(hr + 4 * w);
-    q[w] = (int)((uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
-                 ((uint32_t)(q8(v[2], rr) & 0xff) << 16) | ((uint32_t)(q8(v[3], rr) & 0xff) << 24));
+    const float vv[4] = {v[0], v[1], v[2], v[3]};
+    q[w] = (int)codes4(vv, rr, kF8);
   }
   const int kt = c0 >> 6, g = (c0 & 63) >> 4;
   *reinterpret_cast<v4i *>(qh + frag_tile(rt, kt, F) + ((g * 16 + (row & 15)) << 4)) = q;
@@ -87,15 +90,22 @@ __global__ __launch_bounds__(256) void gather_tiles_kernel(const int8_t *__restr
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
-                            float *sx, ActClip ac, hipStream_t st, Timing tm) {
-  return launch_kernel(act_quant_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, tm, x, inv_s,
-                       T, H, qx, sx, ac);
+                            float *sx, ActClip ac, bool fp8, hipStream_t st, Timing tm) {
+  const dim3 grid((unsigned)((T + 3) / 4));
+  if (fp8) return launch_kernel(act_quant_kernel<true>, grid, dim3(256), st, tm, x, inv_s, T, H, qx,
+                                sx, ac);
+  return launch_kernel(act_quant_kernel<false>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx, ac);
 }
 
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
-                          int64_t P, int F, int8_t *qh, float *sh, hipStream_t st, Timing tm) {
+                          int64_t P, int F, int8_t *qh, float *sh, bool fp8, hipStream_t st,
+                          Timing tm) {
   const dim3 grid((unsigned)((P + 15) / 16), (unsigned)((F + 255) / 256));
-  return launch_kernel(requant_kernel, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh, sh);
+  if (fp8)
+    return launch_kernel(requant_kernel<true>, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh,
+                         sh);
+  return launch_kernel(requant_kernel<false>, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh,
+                       sh);
 }
 
 hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,

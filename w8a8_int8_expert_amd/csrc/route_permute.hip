@@ -126,14 +126,15 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     int32_t *__restrict__ offsets, int32_t *__restrict__ poffsets,
     int32_t *__restrict__ mtile_off, int32_t *__restrict__ sorted, int32_t *__restrict__ row_of,
     int P, const uint16_t *__restrict__ x, const float *__restrict__ inv_s, int H,
-    int8_t *__restrict__ qx, float *__restrict__ sx, uint32_t *__restrict__ amax, ActClip ac) {
+    int8_t *__restrict__ qx, float *__restrict__ sx, uint32_t *__restrict__ amax, ActClip ac,
+    bool fp8) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (blockIdx.x > 0) {
     // Four tokens per block: the quantisation is spread over many compute
     // units instead of stacking 16 wavefronts' arithmetic on one.
     const int64_t t = (int64_t)(blockIdx.x - 1) * kSmallQuantTokens + wave;
     if (wave < kSmallQuantTokens && t < T)
-      quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac);
+      quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, fp8);
     return;
   }
   __shared__ uint64_t wave_keys[16][64];
@@ -345,13 +346,13 @@ hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, cons
                                  int32_t *counts, int32_t *offsets, int32_t *poffsets,
                                  int32_t *mtile_off, int32_t *sorted, int32_t *row_of, int P,
                                  const uint16_t *x, const float *inv_s, int H, int8_t *qx,
-                                 float *sx, uint32_t *amax, ActClip ac, hipStream_t st,
-                                 Timing tm) {
+                                 float *sx, uint32_t *amax, ActClip ac, bool fp8,
+                                 hipStream_t st, Timing tm) {
   const dim3 grid(1 + (unsigned)((T + kSmallQuantTokens - 1) / kSmallQuantTokens)), block(1024);
 #define MOE_PROLOGUE(NV)                                                                     \
   return launch_kernel(prologue_small_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, \
                        E, k, capacity, ids, wts, counts, offsets, poffsets, mtile_off, sorted,  \
-                       row_of, P, x, inv_s, H, qx, sx, amax, ac)
+                       row_of, P, x, inv_s, H, qx, sx, amax, ac, fp8)
   switch (route_nv(E)) {
     case 1: MOE_PROLOGUE(1);
     case 2: MOE_PROLOGUE(2);

@@ -27,7 +27,6 @@ namespace moe {
 namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v8bf as_bf16x8(v4i v) { return __builtin_bit_cast(v8bf, v); }
 
