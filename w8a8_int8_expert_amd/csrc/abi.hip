@@ -45,8 +45,6 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   L.row_of = take(sizeof(int32_t) * A);
   L.qx = take((size_t)T * H);
   L.sx = take(sizeof(float) * T);
-  L.a1 = take(P16 * H);
-  L.rs = take(sizeof(float) * (size_t)L.P);
   L.h = take(sizeof(float) * (size_t)L.P * F);
   L.amax = take(sizeof(uint32_t) * (size_t)L.P);
   L.qh = take(P16 * F);
@@ -215,8 +213,6 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
   int32_t *row_of = (int32_t *)(ws + L.row_of);
   int8_t *qx = (int8_t *)(ws + L.qx);
   float *sx = (float *)(ws + L.sx);
-  int8_t *a1 = (int8_t *)(ws + L.a1);
-  float *rs = (float *)(ws + L.rs);
   float *h = (float *)(ws + L.h);
   uint32_t *amax = (uint32_t *)(ws + L.amax);
   int8_t *qh = (int8_t *)(ws + L.qh);
@@ -268,17 +264,12 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
     MOE_CHECK(launch_gemm1_stream(qx, sx, sorted, k, counts, poffsets, offsets, wt->w_gate_up,
                                   wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st, tm(kG1)));
   } else {
-    // GEMM1's tiled operand is gathered from qx (stage "activation quant" is
-    // timed from the start of the quantisation to the end of the gather).
-    // Writing the codes straight into the permuted tiles from the
-    // quantisation kernel scatters 16-byte pieces and measured 2.5x slower.
+    // GEMM1 gathers its activation rows from qx as it loads them.
     if (!small)
-      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st,
-                                 tm(kActQ, true, false)));
-    MOE_CHECK(launch_gather_tiles(qx, sx, sorted, k, poffsets, E, L.P, H, a1, rs, st,
-                                  tm(kActQ, small, true)));
-    MOE_CHECK(launch_gemm1_tiled(a1, rs, counts, poffsets, offsets, mtile_off, A, wt->w_gate_up,
-                                 wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st, tm(kG1)));
+      MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st, tm(kActQ)));
+    MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, poffsets, offsets, mtile_off, A,
+                                 wt->w_gate_up, wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st,
+                                 tm(kG1)));
   }
   MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, fp8, st, tm(kReq)));
   if (path == 1)

@@ -9,30 +9,39 @@
 // pipeline: the two 32-byte k halves of a stage feed one
 // v_mfma_scale_f32_32x32x64_f8f6f4 with fp32 accumulators.
 //
-// One block (8 wavefronts, two per SIMD) computes a 256-row x 256-column
+// One block (8 wavefronts, two per SIMD) computes a 256-row x 384-column
 // tile of one expert:
 //   rows    = 256 consecutive permuted rows of the expert (the M tile);
-//   columns = GEMM1: 128 gate channels and the same 128 up channels of the
-//             expert's [2F][H] weights; GEMM2: 256 output channels.
-// Both operands are stored fragment-tiled (16 rows x 64 k per 1 KB, the lane
-// order of the INT8 matrix instructions): the weights by calibration, the
-// activations by the kernel that produces them (expert groups start on a
-// 16-row boundary). K advances 64 at a time through a 5-stage ring of 32 KB
-// LDS buffers (all 160 KB) filled by direct global->LDS loads
-// (global_load_lds_dwordx4: a wavefront moves one contiguous 1 KB tile per
-// instruction, lane l's 16 bytes landing at byte 16*l), issued four stages
-// ahead of use: about 128 KB per CU in flight, which the L2 latency under
-// load needs. Reading a 32x32x32 operand from such a tile is a conflict-free
-// ds_read_b128.
-// A 256x256 tile moves 2 bytes per 256 int8 operations, which is what keeps
-// the loads under the matrix time: the L2 -> LDS path sustains about 27
-// bytes per clock per CU, the INT8 matrix cores 8192 operations.
-// Wavefront (wm, wn) owns rows 128*wm.. and, for GEMM1, 32 gate + the
-// matching 32 up columns (so g and u of one h element meet in one lane); it
-// accumulates a 128x64 INT32 tile in 8 v_mfma_i32_32x32x32_i8 accumulators.
-// The epilogue goes through the wavefront's own slice of the (then free)
-// stage buffers so that every global store writes 16 bytes per lane along a
-// row.
+//   columns = GEMM1: 192 gate channels and the same 192 up channels of the
+//             expert's [2F][H] weights; GEMM2: 384 output channels. The last
+//             N tile of an expert may be partial (F a multiple of 32, H of
+//             256): its missing weight tiles repeat the last real one and
+//             their columns are not stored.
+// Both operands reach LDS fragment-tiled (16 rows x 64 k per 1 KB, the lane
+// order of the INT8 matrix instructions). The weights are stored so by
+// calibration and GEMM2's activations by the requantisation (expert groups
+// start on a 16-row boundary). GEMM1's activations are gathered by the loads
+// themselves from the token-major codes: the lane that fills row r of a tile
+// reads 16 bytes of the token that padded row r holds, so every token row is
+// read where it lies (T x H bytes, which stay cache-resident across the k
+// experts that use them) instead of from a permuted copy k times that size.
+// K advances 64 at a time through a 4-stage ring of 40 KB LDS buffers (all
+// 160 KB) filled by direct global->LDS loads (global_load_lds_dwordx4: one
+// instruction moves 1 KB, lane l's 16 bytes landing at byte 16*l), issued
+// three stages ahead of use. Reading a 32x32x32 operand from such a tile is
+// a conflict-free ds_read_b128.
+// What limits these kernels is the L2 -> LDS feed: a CU keeps only about 64
+// cache-line requests in flight, so its load rate is that many lines over
+// the L2 latency (~15 B per clock at prefill), far below the matrix rate.
+// The tile is therefore as large as the registers allow: 256 x 384 moves
+// 40 KB per 6.3 M multiply-adds, a fifth less per operation than 256 x 256.
+// Wavefront (wm, wn), wm < 4, wn < 2, owns rows 64*wm.. and six 32-column
+// fragments: for GEMM1 three gate and the three matching up fragments (so g
+// and u of one h element meet in one lane), for GEMM2 192 consecutive
+// outputs; it accumulates a 64x192 tile in 12 32x32 accumulators
+// (v_mfma_i32_32x32x32_i8). The epilogue goes through the wavefront's own
+// slice of the (then free) stage buffers so that every global store writes
+// 16 bytes per lane along a row.
 //
 // Tiles are numbered expert by expert, and within an expert (N group, M tile,
 // N tile in group), so that the blocks that run together on one XCD (one L2)
@@ -51,25 +60,29 @@ namespace moe {
 namespace {
 
 constexpr int BM = kTiledBM;  // 256 rows
-constexpr int BN = 256;       // output columns (GEMM1: 128 gate + 128 up)
+constexpr int BN = 384;       // output columns (GEMM1: 192 gate + 192 up)
 constexpr int BK = 64;        // k bytes per stage
-constexpr int kStages = 5;
+constexpr int kStages = 4;
 constexpr int kWaves = 8;
 constexpr int kATiles = BM / 16, kBTiles = BN / 16;      // 1 KB tiles per stage
-constexpr int kStageBytes = (kATiles + kBTiles) * 1024;  // 32 KB
-constexpr int kLoadsPerWave = (kATiles + kBTiles) / kWaves;
-// Epilogue staging: 32 rows per pass, row pitch padded by 8 floats so that
-// the two 32-lane halves of a wavefront (rows r and r+4) use disjoint banks.
-constexpr int kEpiPitch1 = 32 + 8;  // GEMM1: 32 h columns per wavefront
-constexpr int kEpiPitch2 = 64 + 8;  // GEMM2: 64 y columns per wavefront
-constexpr int kSlice = 16384;                 // per-wavefront epilogue staging
+constexpr int kStageBytes = (kATiles + kBTiles) * 1024;  // 40 KB
+constexpr int kALoads = kATiles / kWaves, kBLoads = kBTiles / kWaves;
+constexpr int kLoadsPerWave = kALoads + kBLoads;         // 2 + 3
+static_assert(kALoads * kWaves == kATiles && kBLoads * kWaves == kBTiles, "load split");
+// Epilogue staging: 32 rows x 96 columns per pass, row pitch padded by 8
+// floats so that the two 32-lane halves of a wavefront (rows r and r+4) use
+// disjoint banks.
+constexpr int kEpiPitch = 96 + 8;
+constexpr int kSlice = 32 * kEpiPitch * 4;    // per-wavefront epilogue staging
 constexpr int kRowScaleAt = kWaves * kSlice;  // then 256 row scales
-static_assert(32 * kEpiPitch2 * 4 <= kSlice, "epilogue slice");
-static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "row scales");
+static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "epilogue staging");
 
 struct TiledArgs {
-  const int8_t *act;        // fragment-tiled activations [rows/16][K/64] x 1 KB
-  const float *row_scale;   // per padded row: GEMM1 sx of the row's token; GEMM2 sh
+  const int8_t *act;        // GEMM1: token-major codes [T][K]; GEMM2: fragment-tiled
+                            // padded rows [rows/16][K/64] x 1 KB
+  const float *row_scale;   // GEMM1: per token (sx); GEMM2: per padded row (sh)
+  const int32_t *gather;    // GEMM1: assignment t*k+j of each padded row, -1 if padding
+  int topk;
   const int32_t *counts, *offsets, *mtile_off;  // offsets: 16-aligned group starts
   const int32_t *dense_off;                     // GEMM1: dense group starts (debug rows)
   int E;
@@ -145,100 +158,117 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   const int row0 = a.offsets[e];  // multiple of 16
   const int m0 = mtl * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, F = a.F, H = a.H;
   const int KT = K / BK;
 
   // This wavefront's share of each stage: activation tiles 2w, 2w+1 and
-  // weight tiles 2w, 2w+1. Activation tiles past the expert's last row tile
-  // are clamped to it (their rows are computed and never stored).
+  // weight tiles 3w .. 3w+2. Activation tiles past the expert's last row
+  // tile are clamped to it (their rows are computed and never stored);
+  // GEMM1's padding rows read token 0. Weight tiles past the last channel
+  // repeat it (their columns are never stored).
   const int8_t *src[kLoadsPerWave];
   int dst[kLoadsPerWave];
+  // bytes from one stage to the next: 64 k along a token row, 1 KB tile
+  const size_t astep = kGateUp ? BK : 1024;
   const int N = kGateUp ? 2 * F : H;
   const int8_t *wexp = a.w + (size_t)e * (size_t)N * (size_t)K;
   const int last_rt = (row0 + R - 1) >> 4;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int ti = 2 * wave + t;
+  for (int t = 0; t < kALoads; ++t) {
+    const int ti = kALoads * wave + t;
     int rt = ((row0 + m0) >> 4) + ti;
     rt = rt < last_rt ? rt : last_rt;
-    src[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
+    if (kGateUp) {
+      const int asg = a.gather[rt * 16 + (lane & 15)];
+      const int64_t tok = asg >= 0 ? asg / a.topk : 0;
+      src[t] = a.act + tok * K + (lane >> 4) * 16;
+    } else {
+      src[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
+    }
     dst[t] = ti * 1024;
+  }
+#pragma unroll
+  for (int t = 0; t < kBLoads; ++t) {
+    const int bi = kBLoads * wave + t;
     int wt;  // 16-channel weight tile
-    if (kGateUp) wt = ti < 8 ? ntile * 8 + ti : (F >> 4) + ntile * 8 + (ti - 8);
-    else wt = ntile * 16 + ti;
-    src[2 + t] = wexp + frag_tile(wt, 0, K) + lane * 16;
-    dst[2 + t] = (kATiles + ti) * 1024;
+    if (kGateUp) {
+      const int half = bi / 12, j = ntile * 12 + bi % 12;  // gate (0) or up (1)
+      wt = half * (F >> 4) + (j < (F >> 4) ? j : (F >> 4) - 1);
+    } else {
+      const int j = ntile * 24 + bi;
+      wt = j < (H >> 4) ? j : (H >> 4) - 1;
+    }
+    src[kALoads + t] = wexp + frag_tile(wt, 0, K) + lane * 16;
+    dst[kALoads + t] = (kATiles + bi) * 1024;
   }
   auto issue = [&](int kt) {
     int8_t *st = lds + (kt % kStages) * kStageBytes;
 #pragma unroll
     for (int t = 0; t < kLoadsPerWave; ++t)
-      dma16(src[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + dst[t])));
+      dma16(src[t] + (size_t)kt * (t < kALoads ? astep : 1024),
+            __builtin_amdgcn_readfirstlane(lds_addr(st + dst[t])));
   };
 
-  Acc acc[4][2];
+  Acc acc[2][6];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int c = 0; c < 6; ++c)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0;
 
   // Operand offsets inside a stage: 32x32x32 fragment of row (or column)
-  // block 32*blk, k half hk: tile 2*blk + (lane%32)/16, lane row lane%16,
-  // k group 2*hk + lane/32.
+  // block starting at 1 KB tile T, k half hk: tile T + (lane%32)/16, lane row
+  // lane%16, k group 2*hk + lane/32.
   const int frag = (((lane >> 5) * 16) + (lane & 15)) * 16 + ((lane & 31) >> 4) * 1024;
-  int boff[2];
+  int boff[6];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int t0 = kGateUp ? 8 * cb + 2 * wn : 4 * wn + 2 * cb;
-    boff[cb] = (kATiles + t0) * 1024 + frag;
+  for (int c = 0; c < 6; ++c) {
+    const int t0 = kGateUp ? (c < 3 ? 6 * wn + 2 * c : 12 + 6 * wn + 2 * (c - 3))
+                           : 12 * wn + 2 * c;
+    boff[c] = (kATiles + t0) * 1024 + frag;
   }
-  const int aoff = (8 * wm) * 1024 + frag;
+  const int aoff = (4 * wm) * 1024 + frag;
 
   const int pre = KT < kStages - 1 ? KT : kStages - 1;
   for (int s2 = 0; s2 < pre; ++s2) issue(s2);
   for (int kt = 0; kt < KT; ++kt) {
     const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
-    static_assert(kStages - 2 <= 3, "wait cases");
-    if (ahead >= 3) wait_barrier<3 * kLoadsPerWave>();
-    else if (ahead == 2) wait_barrier<2 * kLoadsPerWave>();
+    static_assert(kStages - 2 <= 2, "wait cases");
+    if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
     else if (ahead == 1) wait_barrier<kLoadsPerWave>();
     else wait_barrier<0>();
     if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
     const int8_t *st = lds + (kt % kStages) * kStageBytes;
     if constexpr (kF8) {
       // Both k halves of the stage feed one 32x32x64 FP8 instruction.
-      v4i af[2][4], bf[2][2];
+      v4i af[2][2];
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[hk][i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+        for (int hk = 0; hk < 2; ++hk)
+          af[i][hk] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bf[hk][j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+      for (int c = 0; c < 6; ++c) {
+        const v4i b0 = *reinterpret_cast<const v4i *>(st + boff[c]);
+        const v4i b1 = *reinterpret_cast<const v4i *>(st + boff[c] + 512);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][c] = mfma32f8(af[i][0], af[i][1], b0, b1, acc[i][c]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = mfma32f8(af[0][i], af[1][i], bf[0][j], bf[1][j], acc[i][j]);
     } else {
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
-        v4i af[4], bf[2];
+        v4i af[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
           af[i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bf[j] = *reinterpret_cast<const v4i *>(st + boff[j] + hk * 512);
+        for (int c = 0; c < 6; ++c) {
+          const v4i bf = *reinterpret_cast<const v4i *>(st + boff[c] + hk * 512);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+          for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i], bf, acc[i][c]);
+        }
       }
     }
   }
@@ -247,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   if (tid < BM) {
     const int r = m0 + tid;
     float sc = 0.0f;
-    if (r < R) sc = a.row_scale[row0 + r];
+    if (r < R) sc = kGateUp ? a.row_scale[a.gather[row0 + r] / a.topk] : a.row_scale[row0 + r];
     row_scale[tid] = sc;
   }
   __syncthreads();
@@ -256,71 +286,101 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   // slice. Lane holds column (lane & 31) of each 32x32 accumulator tile and
   // rows 8*(v/4) + 4*(lane/32) + v%4, v < 16.
   float *slice = reinterpret_cast<float *>(lds + wave * kSlice);
-  const int mw = 128 * wm;
+  const int mw = 64 * wm;
   const int rl = 4 * (lane >> 5);  // lane's row offset inside a group of 8
   if (kGateUp) {
-    const int f0 = ntile * 128 + 32 * wn;  // first h column of this wavefront
+    const int f0 = ntile * 192 + 96 * wn;  // first h column of this wavefront
     const float *sgu = a.wscale + (size_t)e * 2 * F;
-    const float sg = sgu[f0 + (lane & 31)], su = sgu[F + f0 + (lane & 31)];
+    // Columns past F (a partial last tile) get zero scales: their h is 0
+    // and leaves the row maxima alone.
+    float sg[3], su[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int c = 0; c < 3; ++c) {
+      const int f = f0 + 32 * c + (lane & 31);
+      sg[c] = f < F ? sgu[f] : 0.0f;
+      su[c] = f < F ? sgu[F + f] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + rl + (v & 3);
-        const float sxv = row_scale[mw + 32 * i + r];
-        const float hv = swiglu((float)acc[i][0][v] * sxv * sg, (float)acc[i][1][v] * sxv * su);
-        slice[r * kEpiPitch1 + (lane & 31)] = hv;
-        if (a.acc1_dbg && m0 + mw + 32 * i + r < R) {
-          const size_t row = (size_t)(a.dense_off[e] + m0 + mw + 32 * i + r);
-          // The element is copied out before its bits are taken: a bit cast
-          // applied to a vector element directly reads element 0.
-          const auto gv = acc[i][0][v], uv = acc[i][1][v];
-          a.acc1_dbg[row * 2 * F + f0 + (lane & 31)] = __builtin_bit_cast(int32_t, gv);
-          a.acc1_dbg[row * 2 * F + F + f0 + (lane & 31)] = __builtin_bit_cast(int32_t, uv);
+        const int m = mw + 32 * i + r;
+        const float sxv = row_scale[m];
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const float hv = swiglu((float)acc[i][c][v] * sxv * sg[c],
+                                  (float)acc[i][3 + c][v] * sxv * su[c]);
+          slice[r * kEpiPitch + 32 * c + (lane & 31)] = hv;
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(hv));
+        }
+        // row maximum over the wavefront's 96 columns: the 32 lanes of a half
+#pragma unroll
+        for (int s = 1; s < 32; s <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, s, 64));
+        if ((lane & 31) == 0 && m0 + m < R)
+          atomicMax(a.amax + row0 + m0 + m, __float_as_uint(mx));
+        if (a.acc1_dbg && m0 + m < R) {
+          const size_t row = (size_t)(a.dense_off[e] + m0 + m);
+#pragma unroll
+          for (int c = 0; c < 3; ++c) {
+            const int f = f0 + 32 * c + (lane & 31);
+            if (f < F) {
+              // The element is copied out before its bits are taken: a bit
+              // cast applied to a vector element directly reads element 0.
+              const auto gv = acc[i][c][v], uv = acc[i][3 + c][v];
+              a.acc1_dbg[row * 2 * F + f] = __builtin_bit_cast(int32_t, gv);
+              a.acc1_dbg[row * 2 * F + F + f] = __builtin_bit_cast(int32_t, uv);
+            }
+          }
         }
       }
-      // 32 rows x 32 columns: 8 lanes per row, 4 floats each.
+      // 32 rows x 96 columns: 24 lanes per row, 4 floats each.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 12; ++j) {
         const int c = j * 64 + lane;
-        const int r = c >> 3, c4 = (c & 7) * 4;
-        const v4f hv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch1 + c4);
-        float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(hv[0]), __builtin_fabsf(hv[1])),
-                                   __builtin_fmaxf(__builtin_fabsf(hv[2]), __builtin_fabsf(hv[3])));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2, 64));
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4, 64));
+        const int r = c / 24, c4 = (c % 24) * 4;
         const int m = mw + 32 * i + r;
-        if (m0 + m < R) {
-          const size_t row = (size_t)(row0 + m0 + m);
-          __builtin_nontemporal_store(hv, reinterpret_cast<v4f *>(a.out + row * F + f0 + c4));
-          if ((lane & 7) == 0) atomicMax(a.amax + row, __float_as_uint(mx));
+        if (m0 + m < R && f0 + c4 < F) {
+          const v4f hv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c4);
+          __builtin_nontemporal_store(
+              hv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * F + f0 + c4));
         }
       }
     }
   } else {
-    const int n0 = ntile * 256 + 64 * wn;  // first y column of this wavefront
-    const float sd0 = a.wscale[(size_t)e * H + n0 + (lane & 31)];
-    const float sd1 = a.wscale[(size_t)e * H + n0 + 32 + (lane & 31)];
+    const int n0 = ntile * 384 + 192 * wn;  // first y column of this wavefront
+    float sd[6];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int c = 0; c < 6; ++c) {
+      const int n = n0 + 32 * c + (lane & 31);
+      sd[c] = n < H ? a.wscale[(size_t)e * H + n] : 0.0f;
+    }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + rl + (v & 3);
-        const float shv = row_scale[mw + 32 * i + r];
-        slice[r * kEpiPitch2 + (lane & 31)] = (float)acc[i][0][v] * shv * sd0;
-        slice[r * kEpiPitch2 + 32 + (lane & 31)] = (float)acc[i][1][v] * shv * sd1;
-      }
-      // 32 rows x 64 columns: 16 lanes per row, 4 floats each.
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = j * 64 + lane;
-        const int r = c >> 4, c4 = (c & 15) * 4;
-        const int m = mw + 32 * i + r;
-        if (m0 + m < R) {
-          const v4f yv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch2 + c4);
-          __builtin_nontemporal_store(
-              yv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * H + n0 + c4));
+      for (int hc = 0; hc < 2; ++hc) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 8 * (v >> 2) + rl + (v & 3);
+          const float shv = row_scale[mw + 32 * i + r];
+#pragma unroll
+          for (int c = 0; c < 3; ++c)
+            slice[r * kEpiPitch + 32 * c + (lane & 31)] =
+                (float)acc[i][3 * hc + c][v] * shv * sd[3 * hc + c];
+        }
+        // 32 rows x 96 columns: 24 lanes per row, 4 floats each.
+        const int nc = n0 + 96 * hc;
+#pragma unroll
+        for (int j = 0; j < 12; ++j) {
+          const int c = j * 64 + lane;
+          const int r = c / 24, c4 = (c % 24) * 4;
+          const int m = mw + 32 * i + r;
+          if (m0 + m < R && nc + c4 < H) {
+            const v4f yv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c4);
+            __builtin_nontemporal_store(
+                yv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * H + nc + c4));
+          }
         }
       }
     }
@@ -336,16 +396,17 @@ int group_n(int nt) {
 
 }  // namespace
 
-hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *counts,
-                              const int32_t *offsets, const int32_t *dense_off,
-                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
-                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, bool fp8, hipStream_t st, Timing tm) {
+hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
+                              uint32_t *amax, int32_t *acc1_dbg, bool fp8, hipStream_t st,
+                              Timing tm) {
   TiledArgs a{};
-  a.act = a1; a.row_scale = rs; a.counts = counts;
+  a.act = qx; a.row_scale = sx; a.gather = sorted; a.topk = k; a.counts = counts;
   a.offsets = offsets; a.dense_off = dense_off; a.mtile_off = mtile_off; a.E = E;
   a.mt_max = (int)((A + BM - 1) / BM + E);
-  a.nt = F / 128; a.gn = group_n(a.nt);
+  a.nt = (F + 191) / 192; a.gn = group_n(a.nt);
   a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H; a.out = h; a.amax = amax;
   a.acc1_dbg = acc1_dbg;
   const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
@@ -361,7 +422,7 @@ hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *
   a.act = qh; a.row_scale = sh; a.counts = counts; a.offsets = offsets;
   a.mtile_off = mtile_off; a.E = E;
   a.mt_max = (int)((A + BM - 1) / BM + E);
-  a.nt = H / 256; a.gn = group_n(a.nt);
+  a.nt = (H + BN - 1) / BN; a.gn = group_n(a.nt);
   a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
   const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
   if (fp8) return launch_kernel(gemm_tiled_kernel<false, true>, grid, dim3(512), st, tm, a);

@@ -143,8 +143,8 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // Permuted rows inside the layer are "padded": every expert's group starts on
 // a 16-row boundary, so P <= A + 15*min(E, A) rows for A = T*k assignments.
 struct FwdLayout {
-  size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, a1,
-      rs, h, amax, qh, sh, y, rpart, total;
+  size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, h,
+      amax, qh, sh, y, rpart, total;
   int64_t nblk;  // routing blocks
   int64_t P;     // padded permuted rows (upper bound)
 };
@@ -155,7 +155,7 @@ size_t calib_ws_bytes(int H);
 // ----------------------------------------------------------------- launchers
 // Each returns hipGetLastError() after enqueueing on `st` (timed by `tm`).
 // Rows of sorted/h/amax/qh/sh/y are padded rows; offsets are dense group
-// starts, poffsets the padded ones; qh (and a1) are fragment-tiled.
+// starts, poffsets the padded ones; qh is fragment-tiled.
 // Fused small-batch prologue: route (or copy pre-routed ids), group, clear
 // the per-row max and sorted[] over P rows, and quantise the activations.
 hipError_t launch_prologue_small(LogitPlanes logits, const int32_t *ids_in, const float *w_in,
@@ -182,9 +182,6 @@ hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int
                           int32_t *row_of, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
                             float *sx, ActClip ac, bool fp8, hipStream_t st, Timing tm);
-hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
-                               const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
-                               float *rs, hipStream_t st, Timing tm);
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
                           int64_t P, int F, int8_t *qh, float *sh, bool fp8, hipStream_t st,
                           Timing tm);
@@ -196,11 +193,12 @@ hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
                                int F, int E, float *y, bool fp8, hipStream_t st, Timing tm);
-hipError_t launch_gemm1_tiled(const int8_t *a1, const float *rs, const int32_t *counts,
-                              const int32_t *offsets, const int32_t *dense_off,
-                              const int32_t *mtile_off, int64_t A, const int8_t *w_gu,
-                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
-                              int32_t *acc1_dbg, bool fp8, hipStream_t st, Timing tm);
+hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
+                              const int32_t *counts, const int32_t *offsets,
+                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
+                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
+                              uint32_t *amax, int32_t *acc1_dbg, bool fp8, hipStream_t st,
+                              Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,

@@ -1,7 +1,6 @@
 // quant.hip -- per-token activation quantisation (a launch of its own for a
 // large batch; a small batch quantises inside the fused prologue), per-row
-// requantisation of the SwiGLU output into GEMM2's tiled operand, and the
-// gather that lays out GEMM1's tiled operand for the tiled path.
+// requantisation of the SwiGLU output into GEMM2's tiled operand.
 //
 // "MiniMax-M3 W8A8 inference on K100AI" (mhpq.cn/news/1068415) §3.2 and §6.4:
 // activations are quantised per token (one outlier token must not set the
@@ -59,34 +58,6 @@ __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ 
   *reinterpret_cast<v4i *>(qh + frag_tile(rt, kt, F) + ((g * 16 + (row & 15)) << 4)) = q;
 }
 
-// GEMM1's activation operand for the tiled path: the quantised token rows in
-// permuted (padded) row order, fragment-tiled, so that the GEMM streams
-// contiguous 1 KB tiles instead of gathering 64-byte row pieces. Block = one
-// 16-row tile; wavefront w builds k tiles w, w+4, ...: lane l copies row
-// l%16, k bytes 16*(l/16).. of the tile. Padding rows are zero. rs gets the
-// scale of each row's token (0 for padding rows), GEMM1's row dequant scale.
-__global__ __launch_bounds__(256) void gather_tiles_kernel(const int8_t *__restrict__ qx,
-                                                           const float *__restrict__ sx,
-                                                           const int32_t *__restrict__ sorted,
-                                                           int k,
-                                                           const int32_t *__restrict__ poffsets,
-                                                           int E, int H, int8_t *__restrict__ a1,
-                                                           float *__restrict__ rs) {
-  const int rt = blockIdx.x;
-  if (rt * 16 >= poffsets[E]) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int asg = sorted[rt * 16 + (lane & 15)];
-  if (threadIdx.x < 16) rs[rt * 16 + lane] = asg >= 0 ? sx[asg / k] : 0.0f;
-  const int8_t *src = qx + (size_t)(asg >= 0 ? asg / k : 0) * H + (lane >> 4) * 16;
-  int8_t *dst = a1 + frag_tile(rt, 0, H) + lane * 16;
-  const int KT = H >> 6;
-#pragma unroll 4
-  for (int kt = wave; kt < KT; kt += 4) {
-    const v4i v = asg >= 0 ? *reinterpret_cast<const v4i *>(src + kt * 64) : v4i{0, 0, 0, 0};
-    *reinterpret_cast<v4i *>(dst + ((size_t)kt << 10)) = v;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
@@ -106,13 +77,6 @@ hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *p
                          sh);
   return launch_kernel(requant_kernel<false>, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh,
                        sh);
-}
-
-hipError_t launch_gather_tiles(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
-                               const int32_t *poffsets, int E, int64_t P, int H, int8_t *a1,
-                               float *rs, hipStream_t st, Timing tm) {
-  return launch_kernel(gather_tiles_kernel, dim3((unsigned)((P + 15) / 16)), dim3(256), st, tm, qx,
-                       sx, sorted, k, poffsets, E, H, a1, rs);
 }
 
 }  // namespace moe
