@@ -249,27 +249,66 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
 #pragma unroll
         for (int hk = 0; hk < 2; ++hk)
           af[i][hk] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+      // The next column fragment's halves are read while the current
+      // one's instructions run.
+      v4i b0 = *reinterpret_cast<const v4i *>(st + boff[0]);
+      v4i b1 = *reinterpret_cast<const v4i *>(st + boff[0] + 512);
 #pragma unroll
       for (int c = 0; c < 6; ++c) {
-        const v4i b0 = *reinterpret_cast<const v4i *>(st + boff[c]);
-        const v4i b1 = *reinterpret_cast<const v4i *>(st + boff[c] + 512);
+        v4i n0 = b0, n1 = b1;
+        if (c < 5) {
+          n0 = *reinterpret_cast<const v4i *>(st + boff[c + 1]);
+          n1 = *reinterpret_cast<const v4i *>(st + boff[c + 1] + 512);
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) acc[i][c] = mfma32f8(af[i][0], af[i][1], b0, b1, acc[i][c]);
+        b0 = n0; b1 = n1;
       }
+      // Issue order: the A halves and two column fragments, then per
+      // fragment its 2 instructions followed by the reads of the fragment
+      // two ahead, so one fragment's reads are always in flight.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     } else {
+      // As for FP8: both k halves of the A fragments first, then per column
+      // fragment its two halves and four instructions, so that each wait
+      // for an operand read is followed by 128 cycles of matrix work.
+      v4i af[2][2];
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        v4i af[2];
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+        for (int hk = 0; hk < 2; ++hk)
+          af[i][hk] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
+      v4i b0 = *reinterpret_cast<const v4i *>(st + boff[0]);
+      v4i b1 = *reinterpret_cast<const v4i *>(st + boff[0] + 512);
 #pragma unroll
-        for (int c = 0; c < 6; ++c) {
-          const v4i bf = *reinterpret_cast<const v4i *>(st + boff[c] + hk * 512);
-#pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i], bf, acc[i][c]);
+      for (int c = 0; c < 6; ++c) {
+        v4i n0 = b0, n1 = b1;
+        if (c < 5) {  // next column fragment, read under this one's instructions
+          n0 = *reinterpret_cast<const v4i *>(st + boff[c + 1]);
+          n1 = *reinterpret_cast<const v4i *>(st + boff[c + 1] + 512);
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i][0], b0, acc[i][c]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i][1], b1, acc[i][c]);
+        b0 = n0; b1 = n1;
       }
+      // Issue order: the A halves and two column fragments, then per
+      // fragment its 4 instructions followed by the reads of the fragment
+      // two ahead, so one fragment's reads are always in flight.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
   }
   // Every wavefront is done with the stage buffers before they are reused.
