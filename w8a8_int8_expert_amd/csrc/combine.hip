@@ -1,10 +1,12 @@
 // combine.hip -- gate-weighted un-permute and sum of the expert outputs.
 //
 // "超大规模模型推理的Day0适配实践" §四: after the grouped GEMMs the MoE operator
-// un-sorts the rows and takes the weighted sum per token (combine8 in
+// un-sorts the rows and takes the weighted sum per token (combine_2x4 in
 // layer_device.h: fp32 in slot order, bfloat16 with ties to even).
-// Grid (T, H/2048), 256 threads per block; each thread owns 8 consecutive
-// outputs (two 16-byte loads of fp32 y per kept slot, one 16-byte store).
+// Grid (T, H/2048), 256 threads per block covering 2048 outputs of one
+// token: thread i owns outputs 4i.. and 1024+4i.., so each wavefront load
+// reads 1 KB of one y row (two 16-byte loads per lane and kept slot, two
+// 8-byte stores).
 #include "layer_device.h"
 
 namespace moe {
@@ -15,8 +17,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const int32_t *__restrict__ row_of,
                                                       int64_t T, int H, int k,
                                                       uint16_t *__restrict__ out) {
-  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (n < H) combine8(y, wts, row_of, blockIdx.x, H, k, n, out);
+  const int n = blockIdx.y * 2048 + threadIdx.x * 4;
+  if (n < H) combine_2x4(y, wts, row_of, blockIdx.x, H, k, n, n + 1024, out);
 }
 
 }  // namespace

@@ -251,18 +251,21 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
 }
 
 // ------------------------------------------------------------------ combine
-// "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum. Eight
-// consecutive outputs n0..n0+7 of token t:
+// "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum. Two
+// groups of four consecutive outputs of token t, at n0 and n1 (a group at
+// or past H is skipped; H is a multiple of 4):
 //   out[t][n] = bf16( sum over slots j < k with row_of[t*k+j] >= 0 of
 //                     w[t][j] * y[row][n] )
 // summed in fp32 in slot order (independent of scheduling), bf16 with ties
 // to even. y is fp32 [rows][H]: its only rounding is the final one to
 // bfloat16. Dropped slots add nothing; the remaining weights are not
-// renormalised.
-__device__ __forceinline__ void combine8(const float *__restrict__ y,
-                                         const float *__restrict__ wts,
-                                         const int32_t *__restrict__ row_of, int64_t t, int H,
-                                         int k, int n0, uint16_t *__restrict__ out) {
+// renormalised. Callers place the groups of a wavefront's 64 lanes so that
+// each load instruction reads 1 KB of one y row.
+__device__ __forceinline__ void combine_2x4(const float *__restrict__ y,
+                                            const float *__restrict__ wts,
+                                            const int32_t *__restrict__ row_of, int64_t t, int H,
+                                            int k, int n0, int n1, uint16_t *__restrict__ out) {
+  const bool g0 = n0 < H, g1 = n1 < H;
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   // Slots 8 at a time: all loads of a batch are issued before the sums,
   // which then run in slot order over the kept slots.
@@ -277,9 +280,9 @@ __device__ __forceinline__ void combine8(const float *__restrict__ y,
       kept[u] = r >= 0;
       w[u] = kept[u] ? wts[t * k + j] : 0.0f;
       if (kept[u]) {
-        const float *yr = y + (int64_t)r * H + n0;
-        v0[u] = *reinterpret_cast<const v4f *>(yr);
-        v1[u] = *reinterpret_cast<const v4f *>(yr + 4);
+        const float *yr = y + (int64_t)r * H;
+        if (g0) v0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(yr + n0));
+        if (g1) v1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(yr + n1));
       }
     }
 #pragma unroll
@@ -292,14 +295,14 @@ __device__ __forceinline__ void combine8(const float *__restrict__ y,
       }
     }
   }
-  v4i o;
+  v2i o0, o1;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    o[i] = (int)((uint32_t)f32_to_bf16(acc0[2 * i]) | ((uint32_t)f32_to_bf16(acc0[2 * i + 1]) << 16));
-    o[2 + i] =
-        (int)((uint32_t)f32_to_bf16(acc1[2 * i]) | ((uint32_t)f32_to_bf16(acc1[2 * i + 1]) << 16));
+    o0[i] = (int)((uint32_t)f32_to_bf16(acc0[2 * i]) | ((uint32_t)f32_to_bf16(acc0[2 * i + 1]) << 16));
+    o1[i] = (int)((uint32_t)f32_to_bf16(acc1[2 * i]) | ((uint32_t)f32_to_bf16(acc1[2 * i + 1]) << 16));
   }
-  *reinterpret_cast<v4i *>(out + t * H + n0) = o;
+  if (g0) *reinterpret_cast<v2i *>(out + t * H + n0) = o0;
+  if (g1) *reinterpret_cast<v2i *>(out + t * H + n1) = o1;
 }
 
 }  // namespace moe
