@@ -35,6 +35,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 # Steps between two steps that carry stage events (decode; prefill steps all do).
 EVENT_STRIDE = 10
+COLD_FLUSH_BYTES = 512 << 20  # overwritten between cold-cache forwards
 STAGE_INDEX = {s: i for i, s in enumerate(
     ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine", "router"))}
 # Sources of the kernels whose counter-measured traffic may be reused.
@@ -169,6 +170,37 @@ def time_workload(gl: GpuLayer, wl, inputs, steps, warmup, hip, timed_stages, st
             hip.destroy(a)
             hip.destroy(b)
     return dict(seconds=t1 - t0, stage_ms=stage_ms, counts=counts_h, out=out)
+
+
+def time_cold(gl: GpuLayer, wl, inputs, steps, warmup):
+    """Each forward timed alone by a pair of events on the layer's stream,
+    with a 512 MiB buffer overwritten between forwards (outside the events),
+    so that no weight is served from the 256 MB last-level cache: the case of
+    a layer whose weights were evicted by the rest of a model. Returns the
+    median and the minimum ms per forward."""
+    torch = gl.torch
+    dev = torch.device("cuda")
+    T = inputs.x.shape[0]
+    x = torch.from_numpy(inputs.x.view("int16")).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(inputs.logits).to(dev) if inputs.logits is not None else None
+    ids = torch.from_numpy(inputs.ids).to(dev) if inputs.ids is not None else None
+    w = torch.from_numpy(inputs.w).to(dev) if inputs.w is not None else None
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device=dev)
+    gl.g.workspace(T)
+    scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    pairs = []
+    for i in range(warmup + steps):
+        scratch.fill_(i & 0x7F)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        gl.g.forward(x, logits, ids, w, wl.capacity_factor, out=out)
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in pairs[warmup:])
+    del scratch
+    return ms[len(ms) // 2], ms[0]
 
 
 def time_router(gl: GpuLayer, wl, inputs, w_router, steps, warmup):
@@ -403,6 +435,11 @@ def main():
                       "frac": round(lb / sec * args.steps / 1e9 / HBM_PEAK_GBS, 4)},
         "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()},
     }
+    log("timing %d forwards with the last-level cache flushed before each" % args.steps)
+    cmed, cmin = time_cold(gl, wl, inputs, args.steps, args.warmup)
+    res["cold_cache"] = {"flush_bytes": COLD_FLUSH_BYTES, "ms_per_step_median": round(cmed, 5),
+                         "ms_per_step_min": round(cmin, 5),
+                         "tokens_per_s_median": round(T / (cmed * 1e-3), 1)}
     if wl.name == "decode" and not args.no_prefill:
         pwl = synth.workload("prefill")
         log("timing prefill: 3 warmup + %d steps" % args.prefill_steps)
