@@ -82,6 +82,8 @@ def test_fp8_calibrate_parity(torch_cuda, name):
 CASES = {
     "tiny": dict(T=40),
     "mid_tiled": dict(T=1000, E=4, k=2, H=512, F=384),
+    # partial last N tiles in both GEMMs, 5 N tiles each, capacity drops
+    "mid_odd_nt": dict(T=600, E=3, k=1, H=1792, F=896, capacity_factor=0.9),
     "decode": None,
 }
 

@@ -79,10 +79,12 @@ SMALL = {
     "pre_routed": dict(pre_routed=True, zipf_s=1.1, k=1, E=8, T=100),
     "pre_routed_k2": dict(pre_routed=True, zipf_s=0.0, k=2, E=8, T=17),
     "H512_F384": dict(H=512, F=384, T=48),
-    # several 256-row M tiles per expert with ragged tails; 3 N tiles (GEMM1), 2 (GEMM2)
+    # several 256-row M tiles per expert with ragged tails; 2 N tiles in each GEMM of the
+    # tiled path, GEMM2's second one partial (128 of 384 columns)
     "mid_tiled": dict(T=1000, E=4, k=2, H=512, F=384),
-    # 5 GEMM1 N tiles (no tile group larger than 1), capacity drops, K = 1024
-    "mid_odd_nt": dict(T=600, E=3, k=1, H=1024, F=640, capacity_factor=0.9),
+    # 5 N tiles in both GEMMs (no tile group larger than 1), both last tiles partial
+    # (128 of 192 h columns, 256 of 384 outputs), capacity drops
+    "mid_odd_nt": dict(T=600, E=3, k=1, H=1792, F=896, capacity_factor=0.9),
 }
 
 

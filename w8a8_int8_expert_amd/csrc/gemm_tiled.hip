@@ -17,19 +17,21 @@
 //             N tile of an expert may be partial (F a multiple of 32, H of
 //             256): its missing weight tiles repeat the last real one and
 //             their columns are not stored.
-// Both operands reach LDS fragment-tiled (16 rows x 64 k per 1 KB, the lane
-// order of the INT8 matrix instructions). The weights are stored so by
-// calibration and GEMM2's activations by the requantisation (expert groups
-// start on a 16-row boundary). GEMM1's activations are gathered by the loads
-// themselves from the token-major codes: the lane that fills row r of a tile
-// reads 16 bytes of the token that padded row r holds, so every token row is
-// read where it lies (T x H bytes, which stay cache-resident across the k
-// experts that use them) instead of from a permuted copy k times that size.
-// K advances 64 at a time through a 4-stage ring of 40 KB LDS buffers (all
-// 160 KB) filled by direct global->LDS loads (global_load_lds_dwordx4: one
-// instruction moves 1 KB, lane l's 16 bytes landing at byte 16*l), issued
-// three stages ahead of use. Reading a 32x32x32 operand from such a tile is
-// a conflict-free ds_read_b128.
+// Operands reach LDS through direct global->LDS loads (global_load_lds_dwordx4:
+// one instruction moves 1 KB, lane l's 16 bytes landing at byte 16*l), with
+// all 160 KB of LDS as rings of stages. The weights, and GEMM2's activations,
+// are stored fragment-tiled (16 rows x 64 k per 1 KB, the lane order of the
+// INT8 matrix instructions; by calibration and by the requantisation, expert
+// groups starting on a 16-row boundary) and move as whole tiles; reading a
+// 32x32x32 operand from such a tile is a conflict-free ds_read_b128. GEMM2
+// runs one ring of four 64-k stages of 40 KB, three ahead. GEMM1's
+// activations are gathered by the loads themselves from the token-major
+// codes, so every token row is read where it lies (T x H bytes, which stay
+// cache-resident across the k experts that use them) instead of from a
+// permuted copy k times that size: they come through their own ring of two
+// 128-k stages, each lane fetching one whole 128-byte line of a token row
+// into an XOR-swizzled row-major layout, beside a ring of four 64-k weight
+// stages.
 // What limits these kernels is the L2 -> LDS feed: a CU keeps only about 64
 // cache-line requests in flight, so its load rate is that many lines over
 // the L2 latency (~15 B per clock at prefill), far below the matrix rate.
@@ -162,32 +164,14 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   const int K = a.K, F = a.F, H = a.H;
   const int KT = K / BK;
 
-  // This wavefront's share of each stage: activation tiles 2w, 2w+1 and
-  // weight tiles 3w .. 3w+2. Activation tiles past the expert's last row
-  // tile are clamped to it (their rows are computed and never stored);
-  // GEMM1's padding rows read token 0. Weight tiles past the last channel
-  // repeat it (their columns are never stored).
-  const int8_t *src[kLoadsPerWave];
-  int dst[kLoadsPerWave];
-  // bytes from one stage to the next: 64 k along a token row, 1 KB tile
-  const size_t astep = kGateUp ? BK : 1024;
   const int N = kGateUp ? 2 * F : H;
   const int8_t *wexp = a.w + (size_t)e * (size_t)N * (size_t)K;
   const int last_rt = (row0 + R - 1) >> 4;
-#pragma unroll
-  for (int t = 0; t < kALoads; ++t) {
-    const int ti = kALoads * wave + t;
-    int rt = ((row0 + m0) >> 4) + ti;
-    rt = rt < last_rt ? rt : last_rt;
-    if (kGateUp) {
-      const int asg = a.gather[rt * 16 + (lane & 15)];
-      const int64_t tok = asg >= 0 ? asg / a.topk : 0;
-      src[t] = a.act + tok * K + (lane >> 4) * 16;
-    } else {
-      src[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
-    }
-    dst[t] = ti * 1024;
-  }
+
+  // Weight tiles 3w .. 3w+2 of each stage are this wavefront's loads. Tiles
+  // past the last channel repeat it (their columns are never stored).
+  const int8_t *bsrc[kBLoads];
+  int bdst[kBLoads];
 #pragma unroll
   for (int t = 0; t < kBLoads; ++t) {
     const int bi = kBLoads * wave + t;
@@ -199,16 +183,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
       const int j = ntile * 24 + bi;
       wt = j < (H >> 4) ? j : (H >> 4) - 1;
     }
-    src[kALoads + t] = wexp + frag_tile(wt, 0, K) + lane * 16;
-    dst[kALoads + t] = (kATiles + bi) * 1024;
+    bsrc[t] = wexp + frag_tile(wt, 0, K) + lane * 16;
+    bdst[t] = bi * 1024;
   }
-  auto issue = [&](int kt) {
-    int8_t *st = lds + (kt % kStages) * kStageBytes;
-#pragma unroll
-    for (int t = 0; t < kLoadsPerWave; ++t)
-      dma16(src[t] + (size_t)kt * (t < kALoads ? astep : 1024),
-            __builtin_amdgcn_readfirstlane(lds_addr(st + dst[t])));
-  };
 
   Acc acc[2][6];
 #pragma unroll
@@ -218,97 +195,174 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][c][v] = 0;
 
-  // Operand offsets inside a stage: 32x32x32 fragment of row (or column)
-  // block starting at 1 KB tile T, k half hk: tile T + (lane%32)/16, lane row
-  // lane%16, k group 2*hk + lane/32.
+  // Weight operand offsets inside a stage's weight tiles: the 32x32x32
+  // fragment of column block c, k half 0, starts in tile t0 + (lane%32)/16 at
+  // lane row lane%16, k group lane/32 (k half 1: + 512).
   const int frag = (((lane >> 5) * 16) + (lane & 15)) * 16 + ((lane & 31) >> 4) * 1024;
   int boff[6];
 #pragma unroll
   for (int c = 0; c < 6; ++c) {
     const int t0 = kGateUp ? (c < 3 ? 6 * wn + 2 * c : 12 + 6 * wn + 2 * (c - 3))
                            : 12 * wn + 2 * c;
-    boff[c] = (kATiles + t0) * 1024 + frag;
+    boff[c] = t0 * 1024 + frag;
   }
-  const int aoff = (4 * wm) * 1024 + frag;
 
-  const int pre = KT < kStages - 1 ? KT : kStages - 1;
-  for (int s2 = 0; s2 < pre; ++s2) issue(s2);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
-    static_assert(kStages - 2 <= 2, "wait cases");
-    if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
-    else if (ahead == 1) wait_barrier<kLoadsPerWave>();
-    else wait_barrier<0>();
-    if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
-    const int8_t *st = lds + (kt % kStages) * kStageBytes;
-    if constexpr (kF8) {
-      // Both k halves of the stage feed one 32x32x64 FP8 instruction.
-      v4i af[2][2];
+  // One 64-k step of matrix work: A fragment (row block i, k half hk) at
+  // ap[i][hk], the weight tiles of the stage at bst.
+  auto step = [&](const int8_t *const (&ap)[2][2], const int8_t *bst) {
+    v4i af[2][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
-          af[i][hk] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
-      // The next column fragment's halves are read while the current
-      // one's instructions run.
-      v4i b0 = *reinterpret_cast<const v4i *>(st + boff[0]);
-      v4i b1 = *reinterpret_cast<const v4i *>(st + boff[0] + 512);
+      for (int hk = 0; hk < 2; ++hk) af[i][hk] = *reinterpret_cast<const v4i *>(ap[i][hk]);
+    // The next column fragment's halves are read while the current one's
+    // instructions run.
+    v4i b0 = *reinterpret_cast<const v4i *>(bst + boff[0]);
+    v4i b1 = *reinterpret_cast<const v4i *>(bst + boff[0] + 512);
 #pragma unroll
-      for (int c = 0; c < 6; ++c) {
-        v4i n0 = b0, n1 = b1;
-        if (c < 5) {
-          n0 = *reinterpret_cast<const v4i *>(st + boff[c + 1]);
-          n1 = *reinterpret_cast<const v4i *>(st + boff[c + 1] + 512);
-        }
+    for (int c = 0; c < 6; ++c) {
+      v4i n0 = b0, n1 = b1;
+      if (c < 5) {
+        n0 = *reinterpret_cast<const v4i *>(bst + boff[c + 1]);
+        n1 = *reinterpret_cast<const v4i *>(bst + boff[c + 1] + 512);
+      }
+      if constexpr (kF8) {
+        // both k halves feed one 32x32x64 FP8 instruction
 #pragma unroll
         for (int i = 0; i < 2; ++i) acc[i][c] = mfma32f8(af[i][0], af[i][1], b0, b1, acc[i][c]);
-        b0 = n0; b1 = n1;
-      }
-      // Issue order: the A halves and two column fragments, then per
-      // fragment its 2 instructions followed by the reads of the fragment
-      // two ahead, so one fragment's reads are always in flight.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    } else {
-      // As for FP8: both k halves of the A fragments first, then per column
-      // fragment its two halves and four instructions, so that each wait
-      // for an operand read is followed by 128 cycles of matrix work.
-      v4i af[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int hk = 0; hk < 2; ++hk)
-          af[i][hk] = *reinterpret_cast<const v4i *>(st + aoff + i * 2048 + hk * 512);
-      v4i b0 = *reinterpret_cast<const v4i *>(st + boff[0]);
-      v4i b1 = *reinterpret_cast<const v4i *>(st + boff[0] + 512);
-#pragma unroll
-      for (int c = 0; c < 6; ++c) {
-        v4i n0 = b0, n1 = b1;
-        if (c < 5) {  // next column fragment, read under this one's instructions
-          n0 = *reinterpret_cast<const v4i *>(st + boff[c + 1]);
-          n1 = *reinterpret_cast<const v4i *>(st + boff[c + 1] + 512);
-        }
+      } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i][0], b0, acc[i][c]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) acc[i][c] = mfma32(af[i][1], b1, acc[i][c]);
-        b0 = n0; b1 = n1;
       }
-      // Issue order: the A halves and two column fragments, then per
-      // fragment its 4 instructions followed by the reads of the fragment
-      // two ahead, so one fragment's reads are always in flight.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      b0 = n0; b1 = n1;
+    }
+    // Issue order: the A halves and two column fragments, then per fragment
+    // its instructions followed by the reads of the fragment two ahead, so
+    // one fragment's reads are always in flight.
+    constexpr int kM = kF8 ? 2 : 4;  // instructions per column fragment
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int c = 0; c < 4; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kM, 0);
+  };
+
+  if constexpr (kGateUp) {
+    // GEMM1. The gathered activation rows come through a ring of two
+    // 128-k "double stages" (32 KB each: 256 rows x 128 bytes), so that every
+    // load lane fetches one whole 128-byte line of a token row; the weights
+    // through a ring of four 64-k stages (24 KB each). Instruction q of a
+    // double stage fills rows 8q..8q+7: lane l takes row 8q + l/8 and its
+    // 16-byte chunk (l%8) ^ (l/8), landing at byte 16*l. So chunk c of row r
+    // sits at r*128 + 16*(c ^ (r%8)), and the 16 rows one matrix operand
+    // read touches fall in distinct banks.
+    constexpr int kA2 = BM * 128;                 // one double stage
+    constexpr int kBStage = kBTiles * 1024;       // one weight stage
+    static_assert(2 * kA2 + 4 * kBStage <= kStages * kStageBytes, "GEMM1 rings");
+    const int8_t *asrc[4];
+    int adst[4];
+    const int last_p = last_rt * 16 + 15;  // last padded row of the expert
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int q = 4 * wave + t;
+      int p = row0 + m0 + 8 * q + (lane >> 3);
+      p = p < last_p ? p : last_p;  // rows past the expert: computed, never stored
+      const int asg = a.gather[p];
+      const int64_t tok = asg >= 0 ? asg / a.topk : 0;  // padding rows read token 0
+      asrc[t] = a.act + tok * K + (((lane & 7) ^ (lane >> 3)) << 4);
+      adst[t] = q * 1024;
+    }
+    auto issue_a = [&](int d) {
+      int8_t *st = lds + (d & 1) * kA2;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dma16(asrc[t] + (size_t)d * 128, __builtin_amdgcn_readfirstlane(lds_addr(st + adst[t])));
+    };
+    auto issue_b = [&](int kt) {
+      int8_t *st = lds + 2 * kA2 + (kt & 3) * kBStage;
+#pragma unroll
+      for (int t = 0; t < kBLoads; ++t)
+        dma16(bsrc[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + bdst[t])));
+    };
+    // A operand byte offsets: row 64*wm + 32*i + lane%32, chunk
+    // 4*(kt%2) + 2*hk + lane/32, swizzled by the row's low three bits
+    // (= lane%8).
+    int arow[2], axor[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) arow[i] = (64 * wm + 32 * i + (lane & 31)) * 128;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk)
+        axor[par][hk] = ((4 * par + 2 * hk + (lane >> 5)) ^ (lane & 7)) << 4;
+    // Issue order (K / 64 = KT steps, even): B(0); A(0), B(1); B(2); then at
+    // step kt, after the wait, A(kt/2 + 1) on even kt and B(kt + 3). Waiting
+    // at step kt for B(kt) (and on even kt for A(kt/2)) leaves 6 loads in
+    // flight on even kt and 10 on odd kt; the last three steps drain all.
+    issue_b(0);
+    issue_a(0);
+    issue_b(1);
+    issue_b(2);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 3 < KT) {
+        if (kt & 1) wait_barrier<2 * kBLoads + 4>();
+        else wait_barrier<2 * kBLoads>();
+      } else {
+        wait_barrier<0>();
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      if (!(kt & 1) && 2 * (kt / 2 + 1) < KT) issue_a(kt / 2 + 1);
+      if (kt + 3 < KT) issue_b(kt + 3);
+      const int8_t *as = lds + ((kt >> 1) & 1) * kA2;
+      const int par = kt & 1;
+      const int8_t *ap[2][2] = {{as + arow[0] + axor[par][0], as + arow[0] + axor[par][1]},
+                                {as + arow[1] + axor[par][0], as + arow[1] + axor[par][1]}};
+      step(ap, lds + 2 * kA2 + (kt & 3) * kBStage);
+    }
+  } else {
+    // GEMM2: both operands fragment-tiled, one ring of four 64-k stages of
+    // 40 KB (16 activation tiles, then 24 weight tiles); this wavefront loads
+    // activation tiles 2w, 2w+1 (clamped to the expert's last row tile:
+    // their rows are computed and never stored) and its weight tiles, three
+    // stages ahead.
+    const int8_t *asrc[kALoads];
+    int adst[kALoads];
+#pragma unroll
+    for (int t = 0; t < kALoads; ++t) {
+      const int ti = kALoads * wave + t;
+      int rt = ((row0 + m0) >> 4) + ti;
+      rt = rt < last_rt ? rt : last_rt;
+      asrc[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
+      adst[t] = ti * 1024;
+    }
+    auto issue = [&](int kt) {
+      int8_t *st = lds + (kt % kStages) * kStageBytes;
+#pragma unroll
+      for (int t = 0; t < kALoads; ++t)
+        dma16(asrc[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + adst[t])));
+#pragma unroll
+      for (int t = 0; t < kBLoads; ++t)
+        dma16(bsrc[t] + ((size_t)kt << 10),
+              __builtin_amdgcn_readfirstlane(lds_addr(st + kATiles * 1024 + bdst[t])));
+    };
+    // A operand: row block 32 of tile 4*wm + 2*i, as for the weights.
+    const int aoff = (4 * wm) * 1024 + frag;
+    const int pre = KT < kStages - 1 ? KT : kStages - 1;
+    for (int s2 = 0; s2 < pre; ++s2) issue(s2);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
+      static_assert(kStages - 2 <= 2, "wait cases");
+      if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
+      else if (ahead == 1) wait_barrier<kLoadsPerWave>();
+      else wait_barrier<0>();
+      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+      const int8_t *st = lds + (kt % kStages) * kStageBytes;
+      const int8_t *ap[2][2] = {{st + aoff, st + aoff + 512},
+                                {st + aoff + 2048, st + aoff + 2048 + 512}};
+      step(ap, st + kATiles * 1024);
     }
   }
   // Every wavefront is done with the stage buffers before they are reused.
