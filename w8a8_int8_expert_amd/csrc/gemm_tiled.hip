@@ -29,14 +29,15 @@
 // codes, so every token row is read where it lies (T x H bytes, which stay
 // cache-resident across the k experts that use them) instead of from a
 // permuted copy k times that size: they come through their own ring of two
-// 128-k stages, each lane fetching one whole 128-byte line of a token row
-// into an XOR-swizzled row-major layout, beside a ring of four 64-k weight
-// stages.
-// What limits these kernels is the L2 -> LDS feed: a CU keeps only about 64
-// cache-line requests in flight, so its load rate is that many lines over
-// the L2 latency (~15 B per clock at prefill), far below the matrix rate.
-// The tile is therefore as large as the registers allow: 256 x 384 moves
-// 40 KB per 6.3 M multiply-adds, a fifth less per operation than 256 x 256.
+// 128-k stages, each lane fetching 16 bytes so that one instruction reads
+// whole 128-byte lines of eight token rows, into an XOR-swizzled row-major
+// layout, beside a ring of four 64-k weight stages.
+// What limits these kernels is the operand feed, about 14 B per clock per CU
+// at prefill: a stage waits for its slowest line, and the 16-23 % of lines
+// that miss L2 come from the last-level cache or HBM. (One block per CU can
+// move ~49 B per clock into LDS when every line hits L2.) The tile is
+// therefore as large as the registers allow: 256 x 384 moves 40 KB per
+// 6.3 M multiply-adds, a fifth less per operation than 256 x 256.
 // Wavefront (wm, wn), wm < 4, wn < 2, owns rows 64*wm.. and six 32-column
 // fragments: for GEMM1 three gate and the three matching up fragments (so g
 // and u of one h element meet in one lane), for GEMM2 192 consecutive
@@ -255,11 +256,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
     // GEMM1. The gathered activation rows come through a ring of two
     // 128-k "double stages" (32 KB each: 256 rows x 128 bytes), so that every
     // load lane fetches one whole 128-byte line of a token row; the weights
-    // through a ring of four 64-k stages (24 KB each). Instruction q of a
-    // double stage fills rows 8q..8q+7: lane l takes row 8q + l/8 and its
-    // 16-byte chunk (l%8) ^ (l/8), landing at byte 16*l. So chunk c of row r
-    // sits at r*128 + 16*(c ^ (r%8)), and the 16 rows one matrix operand
-    // read touches fall in distinct banks.
+    // through a ring of four 64-k stages (24 KB each). Chunk c (16 bytes) of
+    // row r sits at r*128 + 16*(c ^ ((r/2)%8)): any 16 consecutive rows then
+    // put one chunk in 16 distinct 16-byte bank groups of a 256-byte line,
+    // so a matrix operand read is conflict-free. Instruction q of a double
+    // stage fills rows 8q..8q+7 (lane l: row 8q + l/8, slot l%8, byte 16*l).
     constexpr int kA2 = BM * 128;                 // one double stage
     constexpr int kBStage = kBTiles * 1024;       // one weight stage
     static_assert(2 * kA2 + 4 * kBStage <= kStages * kStageBytes, "GEMM1 rings");
@@ -273,7 +274,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
       p = p < last_p ? p : last_p;  // rows past the expert: computed, never stored
       const int asg = a.gather[p];
       const int64_t tok = asg >= 0 ? asg / a.topk : 0;  // padding rows read token 0
-      asrc[t] = a.act + tok * K + (((lane & 7) ^ (lane >> 3)) << 4);
+      // the chunk that belongs in slot l%8 of row 8q + l/8
+      asrc[t] = a.act + tok * K + (((lane & 7) ^ ((4 * (q & 1) + (lane >> 4)) & 7)) << 4);
       adst[t] = q * 1024;
     }
     auto issue_a = [&](int d) {
@@ -289,8 +291,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
         dma16(bsrc[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + bdst[t])));
     };
     // A operand byte offsets: row 64*wm + 32*i + lane%32, chunk
-    // 4*(kt%2) + 2*hk + lane/32, swizzled by the row's low three bits
-    // (= lane%8).
+    // 4*(kt%2) + 2*hk + lane/32, swizzled by (row/2)%8 = (lane/2)%8.
     int arow[2], axor[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) arow[i] = (64 * wm + 32 * i + (lane & 31)) * 128;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
     for (int par = 0; par < 2; ++par)
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk)
-        axor[par][hk] = ((4 * par + 2 * hk + (lane >> 5)) ^ (lane & 7)) << 4;
+        axor[par][hk] = ((4 * par + 2 * hk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
     // Issue order (K / 64 = KT steps, even): B(0); A(0), B(1); B(2); then at
     // step kt, after the wait, A(kt/2 + 1) on even kt and B(kt + 3). Waiting
     // at step kt for B(kt) (and on even kt for A(kt/2)) leaves 6 loads in
