@@ -433,6 +433,10 @@ def main():
         "layer_hbm": {"algorithmic_bytes": lb, "touched_experts": touched,
                       "achieved_GBps": round(lb / sec * args.steps / 1e9, 1),
                       "frac": round(lb / sec * args.steps / 1e9 / HBM_PEAK_GBS, 4)},
+        "layer_int8": {"algorithmic_ops": 6 * A * wl.H * wl.F,
+                       "achieved_TOPs": round(6.0 * A * wl.H * wl.F / sec * args.steps / 1e12, 1),
+                       "frac": round(6.0 * A * wl.H * wl.F / sec * args.steps / 1e12 /
+                                     INT8_PEAK_TOPS, 4)},
         "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()},
     }
     log("timing %d forwards with the last-level cache flushed before each" % args.steps)
