@@ -130,8 +130,9 @@ template <> struct Acc32<true> { typedef v16f T; };
 template <bool kGateUp, bool kF8>
 __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   typedef typename Acc32<kF8>::T Acc;
-  // All 160 KB: the stage ring, then (after the K loop) the epilogue staging
-  // and the row scales.
+  // All 160 KB: the operand rings (GEMM2: four 40 KB stages; GEMM1: two
+  // 32 KB activation stages and four 24 KB weight stages), then (after the
+  // K loop) the epilogue staging and the row scales.
   __shared__ __attribute__((aligned(1024))) int8_t lds[kStages * kStageBytes];
   float *row_scale = reinterpret_cast<float *>(lds + kRowScaleAt);
 
@@ -254,9 +255,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
 
   if constexpr (kGateUp) {
     // GEMM1. The gathered activation rows come through a ring of two
-    // 128-k "double stages" (32 KB each: 256 rows x 128 bytes), so that every
-    // load lane fetches one whole 128-byte line of a token row; the weights
-    // through a ring of four 64-k stages (24 KB each). Chunk c (16 bytes) of
+    // 128-k "double stages" (32 KB each: 256 rows x 128 bytes), so that each
+    // load instruction reads whole 128-byte lines of eight token rows; the
+    // weights through a ring of four 64-k stages (24 KB each). Chunk c (16 bytes) of
     // row r sits at r*128 + 16*(c ^ ((r/2)%8)): any 16 consecutive rows then
     // put one chunk in 16 distinct 16-byte bank groups of a 256-byte line,
     // so a matrix operand read is conflict-free. Instruction q of a double
