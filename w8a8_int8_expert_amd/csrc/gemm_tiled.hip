@@ -118,6 +118,21 @@ __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Maximum of a non-negative value over each 32-lane half of the wavefront,
+// by DPP moves (no LDS round trip): row_shr 1, 2, 4, 8 leave each 16-lane
+// row's maximum in its lane 15, and row_bcast15 into rows 1 and 3 adds the
+// row below. The results land in lanes 31 and 63. Non-negative floats order
+// as their bit patterns, so the maximum is taken on those.
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t m) {
+  auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
+  return m;
+}
+
 // silu(g) * u with the hardware exponential and reciprocal.
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
@@ -410,12 +425,16 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
           slice[r * kEpiPitch + 32 * c + (lane & 31)] = hv;
           mx = __builtin_fmaxf(mx, __builtin_fabsf(hv));
         }
-        // row maximum over the wavefront's 96 columns: the 32 lanes of a half
+        // row maximum over the wavefront's 96 columns (the 32 lanes of a
+        // half), taken by lanes 31 and 63
+        const uint32_t mb = half_wave_max(__float_as_uint(mx));
+        if ((lane & 31) == 31 && m0 + m < R) atomicMax(a.amax + row0 + m0 + m, mb);
+      }
+      if (a.acc1_dbg) {
 #pragma unroll
-        for (int s = 1; s < 32; s <<= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, s, 64));
-        if ((lane & 31) == 0 && m0 + m < R)
-          atomicMax(a.amax + row0 + m0 + m, __float_as_uint(mx));
-        if (a.acc1_dbg && m0 + m < R) {
+        for (int v = 0; v < 16; ++v) {
+          const int m = mw + 32 * i + 8 * (v >> 2) + rl + (v & 3);
+          if (m0 + m >= R) continue;
           const size_t row = (size_t)(a.dense_off[e] + m0 + m);
 #pragma unroll
           for (int c = 0; c < 3; ++c) {
