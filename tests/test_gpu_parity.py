@@ -85,6 +85,10 @@ SMALL = {
     # 5 N tiles in both GEMMs (no tile group larger than 1), both last tiles partial
     # (128 of 192 h columns, 256 of 384 outputs), capacity drops
     "mid_odd_nt": dict(T=600, E=3, k=1, H=1792, F=896, capacity_factor=0.9),
+    # the largest hidden and FFN sizes the library accepts (65536): 1024-stage K loops,
+    # 342 GEMM1 N tiles with a partial last one, uncached activation rows
+    "max_hidden": dict(H=65536, F=128, E=2, k=1, T=40),
+    "max_ffn": dict(H=256, F=65536, E=2, k=1, T=40),
 }
 
 
