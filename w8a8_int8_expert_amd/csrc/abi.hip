@@ -13,7 +13,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // Streaming kernels are used while experts get few rows on average; past
-// that the tiled kernels reuse each weight panel across 128-row tiles.
+// that the tiled kernels reuse each weight panel across 256-row tiles.
 constexpr int64_t kStreamMaxAvgRows = 32;
 
 bool dims_valid(const moe_w8a8_dims *d) {
