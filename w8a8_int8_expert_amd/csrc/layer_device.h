@@ -68,13 +68,13 @@ __device__ __forceinline__ float logit_of(const LogitPlanes &lp, const float *ro
   return v;
 }
 
-template <int NV>
-__device__ __forceinline__ int route_token_wave(const LogitPlanes &lp, int64_t t, int E, int k,
-                                                float *w_out, uint64_t *keys) {
+// Up to 64 experts, from the logit of expert `lane` already in hand (lanes
+// past E ignore theirs).
+__device__ __forceinline__ int route_logit_wave(float v, int E, int k, float *w_out,
+                                                uint64_t *keys) {
   const int lane = threadIdx.x & 63;
-  const float *row = lp.p + t * E;
-  if (NV == 1) {
-    const uint64_t key = lane < E ? route_key(logit_of(lp, row, lane), lane) : 0ull;
+  {
+    const uint64_t key = lane < E ? route_key(v, lane) : 0ull;
     keys[lane] = key;
     // A wavefront's LDS accesses complete in issue order; keep the compiler
     // from moving the reads above the write.
@@ -96,6 +96,14 @@ __device__ __forceinline__ int route_token_wave(const LogitPlanes &lp, int64_t t
     *w_out = topk_weight(mine, k);
     return lane < k ? key_expert(mine) : -1;
   }
+}
+
+template <int NV>
+__device__ __forceinline__ int route_token_wave(const LogitPlanes &lp, int64_t t, int E, int k,
+                                                float *w_out, uint64_t *keys) {
+  const int lane = threadIdx.x & 63;
+  const float *row = lp.p + t * E;
+  if (NV == 1) return route_logit_wave(lane < E ? logit_of(lp, row, lane) : 0.0f, E, k, w_out, keys);
   uint64_t key[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {

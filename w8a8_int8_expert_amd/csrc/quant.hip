@@ -29,8 +29,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
 // activation operand of GEMM2) and sh fp32 [rows]. Block = one 16-row tile x
 // 256 columns; thread = 16 consecutive values of one row, which quantise to
 // exactly one 16-byte chunk of a tile. Rows past the padded row count are
-// left alone; padding rows (max 0) get codes 0 unless their h is undefined,
-// which only rows that are never stored downstream can be.
+// left alone; padding rows (max 0, h never written) get codes 0.
 template <bool kF8>
 __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ h,
                                                       const uint32_t *__restrict__ amax_bits,
@@ -45,14 +44,18 @@ __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ 
   const float amax = __uint_as_float(amax_bits[row]);
   const float qmax = kF8 ? kFp8Max : 127.0f;
   if (c0 == 0) sh[row] = amax / qmax;
-  const float rr = amax > 0.0f ? qmax / amax : 0.0f;
-  const float *hr = h + (size_t)row * F + c0;
-  v4i q;
+  v4i q = {0, 0, 0, 0};
+  // A zero maximum (a padding row, or h all zero) gives codes 0 without
+  // reading h.
+  if (amax > 0.0f) {
+    const float rr = qmax / amax;
+    const float *hr = h + (size_t)row * F + c0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const v4f v = *reinterpret_cast<const v4f *>(hr + 4 * w);
-    const float vv[4] = {v[0], v[1], v[2], v[3]};
-    q[w] = (int)codes4(vv, rr, kF8);
+    for (int w = 0; w < 4; ++w) {
+      const v4f v = *reinterpret_cast<const v4f *>(hr + 4 * w);
+      const float vv[4] = {v[0], v[1], v[2], v[3]};
+      q[w] = (int)codes4(vv, rr, kF8);
+    }
   }
   const int kt = c0 >> 6, g = (c0 & 63) >> 4;
   *reinterpret_cast<v4i *>(qh + frag_tile(rt, kt, F) + ((g * 16 + (row & 15)) << 4)) = q;

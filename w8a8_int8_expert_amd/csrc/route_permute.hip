@@ -10,9 +10,11 @@
 //
 // Two ways through, chosen by the number of assignments A = T*k:
 //  small A (a decode step): ONE launch, prologue_small_kernel. Block 0 routes
-//      every token (one wavefront per token), histograms in LDS, scans, and
-//      scatters stably with one wavefront's ballots; blocks 1.. quantise the
-//      activations (one wavefront per token) at the same time.
+//      every token (one wavefront per token, the next token's logits loaded
+//      before the current one is ranked), histograms in LDS, scans the
+//      counts in one packed block scan, and scatters stably with four
+//      wavefronts' ballots; blocks 1.. quantise the activations (one
+//      wavefront per token) at the same time.
 //  large A (prefill): route_hist (one block per 64 tokens: route, per-block
 //      LDS histogram) -> scan (one block: per-expert scan over blocks,
 //      capacity, offsets, M-tile table) -> scatter (one block per 64 tokens:
@@ -115,6 +117,57 @@ __device__ __forceinline__ int finish_counts(int total, int E, int64_t capacity,
   return poff;
 }
 
+// finish_counts for at most kSmallA assignments, with one block scan: kept
+// count, padded count and M tiles of an expert packed into 21-bit fields of
+// one 64-bit value (each field's total stays below 2^21 for A <= kSmallA and
+// E <= kMaxExperts, so no field carries into the next).
+__device__ __forceinline__ int finish_counts_small(int total, int E, int64_t capacity,
+                                                   int32_t *__restrict__ counts,
+                                                   int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ poffsets,
+                                                   int32_t *__restrict__ mtile_off,
+                                                   uint64_t *wsum) {
+  static_assert(kSmallA + 15 * kMaxExperts < (1 << 21) && kSmallA / kTiledBM + kMaxExperts < (1 << 21),
+                "packed fields");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t v = 0;
+  if (tid < E) {
+    int kept = total;
+    if (capacity > 0 && (int64_t)kept > capacity) kept = (int)capacity;
+    counts[tid] = kept;
+    v = (uint64_t)kept | ((uint64_t)((kept + 15) & ~15) << 21) |
+        ((uint64_t)((kept + kTiledBM - 1) / kTiledBM) << 42);
+  }
+  uint64_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, o, 64);
+    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), o, 64);
+    if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint64_t base = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) base += wsum[w];
+    all += wsum[w];
+  }
+  const uint64_t ex = base + incl - v;
+  constexpr uint64_t kField = (1u << 21) - 1;
+  const int poff = (int)((ex >> 21) & kField);
+  if (tid < E) {
+    offsets[tid] = (int)(ex & kField);
+    poffsets[tid] = poff;
+    mtile_off[tid] = (int)(ex >> 42);
+  }
+  if (tid == 0) {
+    offsets[E] = (int)(all & kField);
+    poffsets[E] = (int)((all >> 21) & kField);
+    mtile_off[E] = (int)(all >> 42);
+  }
+  return poff;
+}
+
 // ------------------------------------------------------------- small A path
 constexpr int kSmallQuantTokens = 4;  // tokens quantised per block (blocks 1..)
 
@@ -142,16 +195,31 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
   __shared__ int32_t run[kMaxExperts];
   __shared__ int32_t lds_ids[kSmallA];
   __shared__ int32_t lds_off[kMaxExperts];
-  __shared__ int wsum[16];
+  __shared__ int32_t wcnt[4][kMaxExperts];
+  __shared__ uint64_t wsum[16];
   const int A = T * k;
-  for (int e = tid; e < E; e += 1024) { hist[e] = 0; run[e] = 0; }
+  for (int e = tid; e < E; e += 1024) {
+    hist[e] = 0;
+    run[e] = 0;
+    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
+  }
   block_fill(amax, P, 0u);
   block_fill(reinterpret_cast<uint32_t *>(sorted), P, 0xFFFFFFFFu);
   __syncthreads();
+  // Up to 64 experts the next token's logits are loaded before this one is
+  // routed, so their latency overlaps the routing.
+  float cur = 0.0f;
+  if (NV == 1 && logits.p && wave < T && lane < E)
+    cur = logit_of(logits, logits.p + (int64_t)wave * E, lane);
   for (int t = wave; t < T; t += 16) {
     int e;
     float w;
-    if (logits.p) {
+    if (NV == 1 && logits.p) {
+      float nxt = 0.0f;
+      if (t + 16 < T && lane < E) nxt = logit_of(logits, logits.p + (int64_t)(t + 16) * E, lane);
+      e = route_logit_wave(cur, E, k, &w, wave_keys[wave]);
+      cur = nxt;
+    } else if (logits.p) {
       e = route_token_wave<NV>(logits, t, E, k, &w, wave_keys[wave]);
     } else {
       e = lane < k ? ids_in[t * k + lane] : -1;
@@ -165,23 +233,30 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
     }
   }
   __syncthreads();
-  const int off = finish_counts(tid < E ? hist[tid] : 0, E, capacity, counts, offsets, poffsets,
-                                mtile_off, wsum);
+  const int off = finish_counts_small(tid < E ? hist[tid] : 0, E, capacity, counts, offsets,
+                                      poffsets, mtile_off, wsum);
   if (tid < E) lds_off[tid] = off;
   __syncthreads();
-  if (wave != 0) return;
+  // Stable scatter by waves 0..3, 256 assignments per round (wave order =
+  // assignment order): a lane's rank among equal experts of its wave from
+  // ballots, plus earlier waves of the round and earlier rounds through LDS
+  // counters. Every wave takes part in the barriers.
   const int nbits = id_bits(E);
-  for (int base = 0; base < A; base += 64) {
-    const int a = base + lane;
-    int e = a < A ? lds_ids[a] : -1;
+  for (int base = 0; base < A; base += 256) {
+    const int a = base + 64 * wave + lane;
+    int e = wave < 4 && a < A ? lds_ids[a] : -1;
     const bool valid = e >= 0 && e < E;
     if (!valid) e = -1;
-    int rank, cnt;
-    ballot_rank(e, valid, nbits, &rank, &cnt);
-    if (a < A) {
+    int rank = 0, cnt = 0;
+    if (wave < 4) ballot_rank(e, valid, nbits, &rank, &cnt);
+    const bool leader = valid && rank == cnt - 1;
+    if (leader) wcnt[wave][e] = cnt;
+    __syncthreads();
+    if (wave < 4 && a < A) {
       int32_t row = -1;
       if (valid) {
-        const int r = run[e] + rank;
+        int r = run[e] + rank;
+        for (int w = 0; w < wave; ++w) r += wcnt[w][e];
         if (capacity <= 0 || (int64_t)r < capacity) {
           row = lds_off[e] + r;
           sorted[row] = a;
@@ -189,9 +264,12 @@ __global__ __launch_bounds__(1024) void prologue_small_kernel(
       }
       row_of[a] = row;
     }
-    // Every lane has read run[] above before the group's last lane adds the
-    // group size: one wavefront's LDS accesses complete in issue order.
-    if (valid && rank == cnt - 1) run[e] += cnt;
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&run[e], cnt);
+      wcnt[wave][e] = 0;
+    }
+    __syncthreads();
   }
 }
 
