@@ -51,6 +51,8 @@
 // share a few weight panels and reuse each activation tile across the group;
 // each XCD takes one contiguous eighth of that order. The grid is sized by
 // an upper bound on the tile count; surplus blocks exit at once.
+#include <type_traits>
+
 #include "layer_device.h"
 
 // The direct-to-LDS loads are issued from inline assembly: the compiler's own
@@ -184,6 +186,12 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   const int N = kGateUp ? 2 * F : H;
   const int8_t *wexp = a.w + (size_t)e * (size_t)N * (size_t)K;
   const int last_rt = (row0 + R - 1) >> 4;
+  // In the last, partial M tile of a group, a wavefront whose 32 activation
+  // load rows (32w..32w+31) all lie past the group issues no activation loads,
+  // and one whose 64 compute rows (64wm..) all do skips its matrix work; the
+  // stale LDS rows they leave only meet rows that are never stored.
+  const bool skip_a = m0 + 32 * wave >= R;
+  const bool skip_mma = m0 + 64 * wm >= R;
 
   // Weight tiles 3w .. 3w+2 of each stage are this wavefront's loads. Tiles
   // past the last channel repeat it (their columns are never stored).
@@ -320,24 +328,26 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
     // step kt, after the wait, A(kt/2 + 1) on even kt and B(kt + 3). Waiting
     // at step kt for B(kt) (and on even kt for A(kt/2)) leaves 6 loads in
     // flight on even kt and 10 on odd kt; the last three steps drain all.
+    // A wavefront without activation loads waits for B(kt) alone: two B
+    // stages in flight on every step.
     issue_b(0);
-    issue_a(0);
+    if (!skip_a) issue_a(0);
     issue_b(1);
     issue_b(2);
     for (int kt = 0; kt < KT; ++kt) {
       if (kt + 3 < KT) {
-        if (kt & 1) wait_barrier<2 * kBLoads + 4>();
+        if ((kt & 1) && !skip_a) wait_barrier<2 * kBLoads + 4>();
         else wait_barrier<2 * kBLoads>();
       } else {
         wait_barrier<0>();
       }
-      if (!(kt & 1) && 2 * (kt / 2 + 1) < KT) issue_a(kt / 2 + 1);
+      if (!skip_a && !(kt & 1) && 2 * (kt / 2 + 1) < KT) issue_a(kt / 2 + 1);
       if (kt + 3 < KT) issue_b(kt + 3);
       const int8_t *as = lds + ((kt >> 1) & 1) * kA2;
       const int par = kt & 1;
       const int8_t *ap[2][2] = {{as + arow[0] + axor[par][0], as + arow[0] + axor[par][1]},
                                 {as + arow[1] + axor[par][0], as + arow[1] + axor[par][1]}};
-      step(ap, lds + 2 * kA2 + (kt & 3) * kBStage);
+      if (!skip_mma) step(ap, lds + 2 * kA2 + (kt & 3) * kBStage);
     }
   } else {
     // GEMM2: both operands fragment-tiled, one ring of four 64-k stages of
@@ -355,32 +365,41 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
       asrc[t] = a.act + frag_tile(rt, 0, K) + lane * 16;
       adst[t] = ti * 1024;
     }
-    auto issue = [&](int kt) {
-      int8_t *st = lds + (kt % kStages) * kStageBytes;
-#pragma unroll
-      for (int t = 0; t < kALoads; ++t)
-        dma16(asrc[t] + ((size_t)kt << 10), __builtin_amdgcn_readfirstlane(lds_addr(st + adst[t])));
-#pragma unroll
-      for (int t = 0; t < kBLoads; ++t)
-        dma16(bsrc[t] + ((size_t)kt << 10),
-              __builtin_amdgcn_readfirstlane(lds_addr(st + kATiles * 1024 + bdst[t])));
-    };
     // A operand: row block 32 of tile 4*wm + 2*i, as for the weights.
     const int aoff = (4 * wm) * 1024 + frag;
     const int pre = KT < kStages - 1 ? KT : kStages - 1;
-    for (int s2 = 0; s2 < pre; ++s2) issue(s2);
-    for (int kt = 0; kt < KT; ++kt) {
-      const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
-      static_assert(kStages - 2 <= 2, "wait cases");
-      if (ahead >= 2) wait_barrier<2 * kLoadsPerWave>();
-      else if (ahead == 1) wait_barrier<kLoadsPerWave>();
-      else wait_barrier<0>();
-      if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
-      const int8_t *st = lds + (kt % kStages) * kStageBytes;
-      const int8_t *ap[2][2] = {{st + aoff, st + aoff + 512},
-                                {st + aoff + 2048, st + aoff + 2048 + 512}};
-      step(ap, st + kATiles * 1024);
-    }
+    auto kloop = [&](auto skip) {
+      constexpr bool kSkipA = decltype(skip)::value;
+      constexpr int kLoads = kSkipA ? kBLoads : kLoadsPerWave;  // per stage and wavefront
+      auto issue = [&](int kt) {
+        int8_t *st = lds + (kt % kStages) * kStageBytes;
+        if (!kSkipA) {
+#pragma unroll
+          for (int t = 0; t < kALoads; ++t)
+            dma16(asrc[t] + ((size_t)kt << 10),
+                  __builtin_amdgcn_readfirstlane(lds_addr(st + adst[t])));
+        }
+#pragma unroll
+        for (int t = 0; t < kBLoads; ++t)
+          dma16(bsrc[t] + ((size_t)kt << 10),
+                __builtin_amdgcn_readfirstlane(lds_addr(st + kATiles * 1024 + bdst[t])));
+      };
+      for (int s2 = 0; s2 < pre; ++s2) issue(s2);
+      for (int kt = 0; kt < KT; ++kt) {
+        const int ahead = KT - 1 - kt < kStages - 2 ? KT - 1 - kt : kStages - 2;
+        static_assert(kStages - 2 <= 2, "wait cases");
+        if (ahead >= 2) wait_barrier<2 * kLoads>();
+        else if (ahead == 1) wait_barrier<kLoads>();
+        else wait_barrier<0>();
+        if (kt + kStages - 1 < KT) issue(kt + kStages - 1);
+        const int8_t *st = lds + (kt % kStages) * kStageBytes;
+        const int8_t *ap[2][2] = {{st + aoff, st + aoff + 512},
+                                  {st + aoff + 2048, st + aoff + 2048 + 512}};
+        if (!skip_mma) step(ap, st + kATiles * 1024);
+      }
+    };
+    if (skip_a) kloop(std::true_type{});
+    else kloop(std::false_type{});
   }
   // Every wavefront is done with the stage buffers before they are reused.
   wait_barrier<0>();
