@@ -29,7 +29,7 @@ bool dims_supported(const moe_w8a8_dims *d) {
 FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   FwdLayout L{};
   const int64_t A = T * k;
-  L.nblk = (T + kRouteTokens - 1) / kRouteTokens;
+  L.nblk = (T + route_tokens(T) - 1) / route_tokens(T);
   L.P = A + 15 * (A < E ? A : (int64_t)E);
   const size_t P16 = (size_t)((L.P + 15) / 16) * 16;  // rows of the tiled operands
   size_t o = 0;

@@ -17,8 +17,12 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Tokens routed (and histogrammed) per block of the routing kernel.
-constexpr int kRouteTokens = 64;
+// Tokens routed (and histogrammed) per block of the routing kernels for a
+// batch of T tokens: the fewest of 64, 32, 16 per block that still give at
+// most 256 blocks, so that a few thousand tokens spread over the whole chip
+// (one token per wavefront) while large batches keep the per-block
+// histograms that the scan reads few.
+inline int route_tokens(int64_t T) { return T <= 4096 ? 16 : (T <= 8192 ? 32 : 64); }
 // Rows per M tile of the tiled grouped GEMMs.
 constexpr int kTiledBM = 256;
 // Maximum experts (LDS histograms are sized for it).

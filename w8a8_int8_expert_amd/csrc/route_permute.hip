@@ -15,11 +15,11 @@
 //      counts in one packed block scan, and scatters stably with four
 //      wavefronts' ballots; blocks 1.. quantise the activations (one
 //      wavefront per token) at the same time.
-//  large A (prefill): route_hist (one block per 64 tokens: route, per-block
-//      LDS histogram) -> scan (one block: per-expert scan over blocks,
-//      capacity, offsets, M-tile table) -> scatter (one block per 64 tokens:
-//      stable ranks from wave ballots); activation quantisation is its own
-//      launch (quant.hip).
+//  large A (prefill): route_hist (one block per tpb = route_tokens(T)
+//      tokens, 16 to 64: route, per-block LDS histogram) -> scan (one block:
+//      per-expert scan over blocks, capacity, offsets, M-tile table) ->
+//      scatter (one block per tpb tokens: stable ranks from wave ballots);
+//      activation quantisation is its own launch (quant.hip).
 // Inside the layer every expert's group of permuted rows starts on a 16-row
 // boundary ("padded" rows: the activation operands of the grouped GEMMs are
 // stored as 16-row x 64-k tiles, and no tile may hold two experts' rows).
@@ -279,16 +279,16 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     const LogitPlanes logits, const int32_t *__restrict__ ids_in,
     const float *__restrict__ w_in, int64_t T, int E, int k, int32_t *__restrict__ ids,
     float *__restrict__ wts, int32_t *__restrict__ blk_hist, uint32_t *__restrict__ amax,
-    int32_t *__restrict__ sorted, int64_t P) {
+    int32_t *__restrict__ sorted, int64_t P, int tpb) {
   __shared__ uint64_t wave_keys[16][64];
   __shared__ int32_t hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) hist[e] = 0;
-  // This block's share of the padded rows: [b*64*k, (b+1)*64*k), and the
+  // This block's share of the padded rows: [b*tpb*k, (b+1)*tpb*k), and the
   // last block also takes the rows past T*k.
   {
-    const int64_t r0 = (int64_t)blockIdx.x * kRouteTokens * k;
-    int64_t r1 = r0 + (int64_t)kRouteTokens * k;
+    const int64_t r0 = (int64_t)blockIdx.x * tpb * k;
+    int64_t r1 = r0 + (int64_t)tpb * k;
     if (blockIdx.x == gridDim.x - 1 || r1 > P) r1 = P;
     for (int64_t r = r0 + tid; r < r1; r += 1024) {
       amax[r] = 0u;
@@ -296,8 +296,8 @@ __global__ __launch_bounds__(1024) void route_hist_kernel(
     }
   }
   __syncthreads();
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
-  for (int tt = wave; tt < kRouteTokens; tt += 16) {
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  for (int tt = wave; tt < tpb; tt += 16) {
     const int64_t t = t0 + tt;
     if (t >= T) break;
     int e;
@@ -333,21 +333,54 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t per_lane = (nblk + 63) / 64;
-  for (int e = wave; e < E; e += 16) {
-    int32_t *row = blk_hist + (int64_t)e * nblk;
-    const int64_t b0 = lane * per_lane;
-    const int64_t b1 = b0 + per_lane < nblk ? b0 + per_lane : nblk;
-    int s = 0;
-#pragma unroll 8
-    for (int64_t b = b0; b < b1; ++b) s += row[b];
-    const int incl = wave_incl_scan(s);
-    int r = incl - s;  // exclusive prefix of this lane's first block
-    for (int64_t b = b0; b < b1; ++b) {
-      const int c = row[b];
-      row[b] = r;
-      r += c;
+  const int64_t b0 = lane * per_lane;
+  const int64_t b1 = b0 + per_lane < nblk ? b0 + per_lane : nblk;
+  if (per_lane <= 4) {
+    // At most 256 blocks: four experts per wavefront at a time, every load
+    // of the four issued before the scans, so their latencies overlap.
+    constexpr int G = 4;
+    for (int e0 = wave; e0 < E; e0 += 16 * G) {
+      int c[G][4], s[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int e = e0 + 16 * g;
+        const int32_t *row = blk_hist + (int64_t)(e < E ? e : 0) * nblk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[g][j] = (e < E && b0 + j < b1) ? row[b0 + j] : 0;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int e = e0 + 16 * g;
+        s[g] = c[g][0] + c[g][1] + c[g][2] + c[g][3];
+        const int incl = wave_incl_scan(s[g]);
+        if (e < E) {
+          int32_t *row = blk_hist + (int64_t)e * nblk;
+          int r = incl - s[g];  // exclusive prefix of this lane's first block
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (b0 + j < b1) {
+              row[b0 + j] = r;
+              r += c[g][j];
+            }
+          if (lane == 63) total[e] = incl;
+        }
+      }
     }
-    if (lane == 63) total[e] = incl;
+  } else {
+    for (int e = wave; e < E; e += 16) {
+      int32_t *row = blk_hist + (int64_t)e * nblk;
+      int s = 0;
+#pragma unroll 8
+      for (int64_t b = b0; b < b1; ++b) s += row[b];
+      const int incl = wave_incl_scan(s);
+      int r = incl - s;  // exclusive prefix of this lane's first block
+      for (int64_t b = b0; b < b1; ++b) {
+        const int c = row[b];
+        row[b] = r;
+        r += c;
+      }
+      if (lane == 63) total[e] = incl;
+    }
   }
   __syncthreads();
   finish_counts(tid < E ? total[tid] : 0, E, capacity, counts, offsets, poffsets, mtile_off,
@@ -362,7 +395,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ blk_base,
     const int32_t *__restrict__ offsets, int64_t T, int E, int k, int64_t capacity,
-    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of) {
+    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, int tpb) {
   __shared__ int32_t running[kMaxExperts];
   __shared__ int32_t wcnt[4][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -372,8 +405,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   }
   __syncthreads();
   const int64_t A = T * (int64_t)k;
-  const int64_t a0 = (int64_t)blockIdx.x * kRouteTokens * k;
-  const int64_t a1 = a0 + (int64_t)kRouteTokens * k < A ? a0 + (int64_t)kRouteTokens * k : A;
+  const int64_t a0 = (int64_t)blockIdx.x * tpb * k;
+  const int64_t a1 = a0 + (int64_t)tpb * k < A ? a0 + (int64_t)tpb * k : A;
   const int nbits = id_bits(E);
   for (int64_t base = a0; base < a1; base += 256) {
     const int64_t a = base + tid;
@@ -445,10 +478,11 @@ hipError_t launch_route_hist(LogitPlanes logits, const int32_t *ids_in, const fl
                              int64_t T, int E, int k, int32_t *ids, float *wts,
                              int32_t *blk_hist, uint32_t *amax, int32_t *sorted, int64_t P,
                              hipStream_t st, Timing tm) {
-  const dim3 grid((unsigned)((T + kRouteTokens - 1) / kRouteTokens)), block(1024);
+  const int tpb = route_tokens(T);
+  const dim3 grid((unsigned)((T + tpb - 1) / tpb)), block(1024);
 #define MOE_ROUTE(NV)                                                                        \
   return launch_kernel(route_hist_kernel<NV>, grid, block, st, tm, logits, ids_in, w_in, T, E, \
-                       k, ids, wts, blk_hist, amax, sorted, P)
+                       k, ids, wts, blk_hist, amax, sorted, P, tpb)
   switch (route_nv(E)) {
     case 1: MOE_ROUTE(1);
     case 2: MOE_ROUTE(2);
@@ -469,9 +503,10 @@ hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity,
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
                           int32_t *row_of, hipStream_t st, Timing tm) {
-  const int64_t nblk = (T + kRouteTokens - 1) / kRouteTokens;
+  const int tpb = route_tokens(T);
+  const int64_t nblk = (T + tpb - 1) / tpb;
   return launch_kernel(scatter_kernel, dim3((unsigned)nblk), dim3(256), st, tm, ids, blk_hist,
-                       offsets, T, E, k, capacity, sorted, row_of);
+                       offsets, T, E, k, capacity, sorted, row_of, tpb);
 }
 
 }  // namespace moe
