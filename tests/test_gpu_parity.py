@@ -89,6 +89,14 @@ SMALL = {
     # 342 GEMM1 N tiles with a partial last one, uncached activation rows
     "max_hidden": dict(H=65536, F=128, E=2, k=1, T=40),
     "max_ffn": dict(H=256, F=65536, E=2, k=1, T=40),
+    # the batched routing path (T*k > 2048) at its block-size boundaries: 16 tokens per
+    # block up to 4096 tokens, 32 up to 8192, then 64 (last blocks partial), with expert
+    # counts that are not multiples of 16 (the scan's expert batches), two experts per
+    # router lane (E > 64) and capacity drops
+    "route_T4096_E40": dict(T=4096, E=40, k=2, H=256, F=128),
+    "route_T4097_E20": dict(T=4097, E=20, k=3, H=256, F=128),
+    "route_T8193_E72": dict(T=8193, E=72, k=2, H=256, F=128),
+    "route_T5000_cap": dict(T=5000, E=16, k=2, H=256, F=128, capacity_factor=0.8),
 }
 
 
