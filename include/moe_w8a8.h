@@ -182,8 +182,9 @@ typedef struct {
 
 /* Bytes of device workspace that moe_w8a8_forward needs for T tokens, and
  * that moe_w8a8_calibrate needs (T = 0 gives at least the calibrate size).
- * A pure function of the arguments; returns 0 for invalid or unsupported
- * dimensions or T < 0. */
+ * A pure function of the arguments, nondecreasing in T (a workspace sized for
+ * the largest batch serves every smaller one); returns 0 for invalid or
+ * unsupported dimensions or T < 0. */
 size_t moe_w8a8_workspace_size(const moe_w8a8_dims *dims, int64_t T);
 
 /* Calibrate and quantise the layer weights ("MiniMax-M3 W8A8 inference on

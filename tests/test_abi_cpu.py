@@ -44,6 +44,21 @@ def test_strerror(lib):
     assert m.moe_w8a8_strerror(-3) == "workspace missing or too small"
 
 
+def test_workspace_size_nondecreasing(lib):
+    """A workspace sized for the largest batch serves every smaller one, also across
+    the routing kernels' block-size steps (16/32/64 tokens at 4096 and 8192) and the
+    small-batch path's limit (T*k = 2048)."""
+    import w8a8_int8_expert_amd as m
+    Ts = sorted(set(list(range(0, 300)) + list(range(1000, 1030)) + list(range(2040, 2060)) +
+                    list(range(4085, 4110)) + list(range(8185, 8210)) + [16383, 16384, 16385]))
+    for d in (m.dims(256, 128, 1024, 1), m.dims(256, 128, 8, 2), m.dims(4096, 1536, 64, 8),
+              m.dims(8192, 2048, 32, 1)):
+        sizes = [m.moe_w8a8_workspace_size(d, T) for T in Ts]
+        assert all(s > 0 for s in sizes)
+        bad = [(Ts[i], Ts[i + 1]) for i in range(len(Ts) - 1) if sizes[i + 1] < sizes[i]]
+        assert not bad, "workspace shrinks between T=%s" % (bad[:3],)
+
+
 def test_workspace_size_pure(lib):
     d = m.dims(4096, 1536, 64, 8)
     a = m.moe_w8a8_workspace_size(d, 32)

@@ -36,7 +36,9 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
   L.ids = take(sizeof(int32_t) * A);
   L.wts = take(sizeof(float) * A);
-  L.blk_hist = take(sizeof(int32_t) * (size_t)L.nblk * E);
+  // sized for the finest routing block (16 tokens), so that the workspace
+  // never shrinks as T grows past a block-size step
+  L.blk_hist = take(sizeof(int32_t) * (size_t)((T + 15) / 16) * E);
   L.counts = take(sizeof(int32_t) * E);
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.poffsets = take(sizeof(int32_t) * (E + 1));
