@@ -54,3 +54,4 @@ def test_random_config_parity(torch_cuda, i):  # noqa: F811
     layer, cal = _layer_and_cal(wl)
     inputs = synth.make_inputs(wl, layer)
     _full_parity(wl, inputs, cal, path)
+
