@@ -55,3 +55,20 @@ def test_random_config_parity(torch_cuda, i):  # noqa: F811
     inputs = synth.make_inputs(wl, layer)
     _full_parity(wl, inputs, cal, path)
 
+
+
+# The FP8 (e4m3) expert path on twelve further draws, to its own bars (activation
+# codes and scales bit-exact; GEMM sums within the 64-block accumulation bound;
+# requantised codes within one e4m3 step; output equal to the exact pipeline on
+# the GPU's own codes within the accumulation bound and one bf16 step).
+N_FP8 = 12
+CASES_FP8 = [_draw(100 + i) for i in range(N_FP8)]
+
+
+@pytest.mark.parametrize("i", range(N_FP8))
+def test_random_config_fp8_parity(torch_cuda, i):  # noqa: F811
+    from test_gpu_fp8 import fp8_full_parity
+    over, path = CASES_FP8[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random fp8] case=%d path=%d %s" % (i, path, over))
+    fp8_full_parity(wl, path)
