@@ -72,3 +72,18 @@ def test_random_config_fp8_parity(torch_cuda, i):  # noqa: F811
     wl = synth.workload("tiny", **over)
     _say("[random fp8] case=%d path=%d %s" % (i, path, over))
     fp8_full_parity(wl, path)
+
+
+# Router-projection mode (logits = x . W_r^T on the GPU) on eight further draws.
+N_ROUTER = 8
+CASES_ROUTER = [_draw(200 + i) for i in range(N_ROUTER)]
+
+
+@pytest.mark.parametrize("i", range(N_ROUTER))
+def test_random_config_router_parity(torch_cuda, i):  # noqa: F811
+    from test_gpu_router import router_full_parity
+    over, path = CASES_ROUTER[i]
+    over = dict(over, pre_routed=False)
+    wl = synth.workload("tiny", **over)
+    _say("[random router] case=%d path=%d %s" % (i, path, over))
+    router_full_parity(torch_cuda, wl, path)

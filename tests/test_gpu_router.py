@@ -120,6 +120,13 @@ def test_forward_router_mode_parity(torch_cuda, case, gemm_path):
         synth.workload("tiny", **FORWARD_CASES[case])
     _say("[router] forward case=%s path=%d T=%d H=%d E=%d k=%d" % (case, gemm_path, wl.T, wl.H,
                                                                    wl.E, wl.k))
+    router_full_parity(torch, wl, gemm_path)
+
+
+def router_full_parity(torch, wl, gemm_path):
+    """The layer routed by its router projection: logits within the fp32 bound of the
+    exact ones, the routing decision bit-exact on the GPU's logits, every later stage
+    against the oracle routed from them."""
     import w8a8_int8_expert_amd as m
     layer = synth.make_layer(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
