@@ -63,11 +63,17 @@ CASES = {
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_forward_clip_parity(torch_cuda, case, gemm_path):
     import torch
-    import w8a8_int8_expert_amd as m
     over, static, sat_p = CASES[case]
     wl = synth.workload("decode") if over is None else synth.workload("tiny", **over)
     _say("[clip] forward case=%s path=%d T=%d H=%d static=%s sat=%g" % (
         case, gemm_path, wl.T, wl.H, static, sat_p))
+    clip_full_parity(torch, wl, gemm_path, static, sat_p)
+
+
+def clip_full_parity(torch, wl, gemm_path, static, sat_p):
+    """The layer with the static clip (at the calibration tokens' 99th percentile)
+    and/or dynamic saturation at percentile sat_p, every stage against the oracle."""
+    import w8a8_int8_expert_amd as m
     layer = synth.make_layer(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     inputs = synth.make_inputs(wl, layer)

@@ -87,3 +87,32 @@ def test_random_config_router_parity(torch_cuda, i):  # noqa: F811
     wl = synth.workload("tiny", **over)
     _say("[random router] case=%d path=%d %s" % (i, path, over))
     router_full_parity(torch_cuda, wl, path)
+
+
+# Activation clips on eight further draws: dynamic saturation at a percentile
+# that leaves 2-12 values of a token above the level, with or without the static
+# clip from the calibration tokens.
+N_CLIP = 8
+
+
+def _draw_clip(i):
+    import oracle
+    over, path = _draw(300 + i)
+    rng = np.random.default_rng(np.random.SeedSequence([2025, i]))
+    H = over["H"]
+    m = int(rng.integers(2, 13))
+    p = float(np.float32(100.0 * (H - m + 0.5) / H))
+    assert 2 <= H - oracle.percentile_rank(p, H) + 1 <= 16
+    return over, path, bool(rng.random() < 0.5), p
+
+
+CASES_CLIP = [_draw_clip(i) for i in range(N_CLIP)]
+
+
+@pytest.mark.parametrize("i", range(N_CLIP))
+def test_random_config_clip_parity(torch_cuda, i):  # noqa: F811
+    from test_gpu_clip import clip_full_parity
+    over, path, static, sat_p = CASES_CLIP[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random clip] case=%d path=%d static=%s sat=%.6g %s" % (i, path, static, sat_p, over))
+    clip_full_parity(torch_cuda, wl, path, static, sat_p)
