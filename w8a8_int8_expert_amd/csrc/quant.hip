@@ -27,19 +27,19 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
 // h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
 // fragment-tiled (16 rows x 64 k per 1 KB, the layout of the weights: the
 // activation operand of GEMM2) and sh fp32 [rows]. Block = one 16-row tile x
-// 256 columns; thread = 16 consecutive values of one row, which quantise to
-// exactly one 16-byte chunk of a tile. Rows past the padded row count are
+// 512 columns (two halves of 256); thread = 16 consecutive values of one row,
+// which quantise to exactly one 16-byte chunk of a tile. Rows past the padded row count are
 // left alone; padding rows (max 0, h never written) get codes 0.
 template <bool kF8>
-__global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ h,
+__global__ __launch_bounds__(512) void requant_kernel(const float *__restrict__ h,
                                                       const uint32_t *__restrict__ amax_bits,
                                                       const int32_t *__restrict__ poffsets, int E,
                                                       int F, int8_t *__restrict__ qh,
                                                       float *__restrict__ sh) {
   const int rt = blockIdx.x;
-  const int row = rt * 16 + (threadIdx.x >> 4);
+  const int row = rt * 16 + ((threadIdx.x >> 4) & 15);
   if (row >= poffsets[E]) return;
-  const int c0 = blockIdx.y * 256 + (threadIdx.x & 15) * 16;
+  const int c0 = blockIdx.y * 512 + (threadIdx.x >> 8) * 256 + (threadIdx.x & 15) * 16;
   if (c0 >= F) return;
   const float amax = __uint_as_float(amax_bits[row]);
   const float qmax = kF8 ? kFp8Max : 127.0f;
@@ -74,11 +74,11 @@ hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, in
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
                           int64_t P, int F, int8_t *qh, float *sh, bool fp8, hipStream_t st,
                           Timing tm) {
-  const dim3 grid((unsigned)((P + 15) / 16), (unsigned)((F + 255) / 256));
+  const dim3 grid((unsigned)((P + 15) / 16), (unsigned)((F + 511) / 512));
   if (fp8)
-    return launch_kernel(requant_kernel<true>, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh,
+    return launch_kernel(requant_kernel<true>, grid, dim3(512), st, tm, h, amax, poffsets, E, F, qh,
                          sh);
-  return launch_kernel(requant_kernel<false>, grid, dim3(256), st, tm, h, amax, poffsets, E, F, qh,
+  return launch_kernel(requant_kernel<false>, grid, dim3(512), st, tm, h, amax, poffsets, E, F, qh,
                        sh);
 }
 
