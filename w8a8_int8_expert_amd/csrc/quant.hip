@@ -12,8 +12,10 @@
 namespace moe {
 namespace {
 
-// x bf16 [T][H] -> qx int8 [T][H], sx fp32 [T]. One wavefront per token.
-template <bool kF8>
+// x bf16 [T][H] -> qx int8 [T][H], sx fp32 [T]. One wavefront per token;
+// the row stays in registers (MAXC chunks of 8 values per lane) between its
+// maximum and its codes.
+template <bool kF8, int MAXC>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restrict__ x,
                                                         const float *__restrict__ inv_s,
                                                         int64_t T, int H,
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restri
                                                         float *__restrict__ sx, ActClip ac) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  quant_token_row<16>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, kF8);
+  quant_token_row<MAXC>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, kF8);
 }
 
 // h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
@@ -66,9 +68,18 @@ __global__ __launch_bounds__(512) void requant_kernel(const float *__restrict__ 
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
                             float *sx, ActClip ac, bool fp8, hipStream_t st, Timing tm) {
   const dim3 grid((unsigned)((T + 3) / 4));
-  if (fp8) return launch_kernel(act_quant_kernel<true>, grid, dim3(256), st, tm, x, inv_s, T, H, qx,
-                                sx, ac);
-  return launch_kernel(act_quant_kernel<false>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx, ac);
+  // rows up to 4096 channels fit eight 16-byte chunks per lane: half the
+  // registers, twice the wavefronts in flight
+  if (H <= 4096) {
+    if (fp8) return launch_kernel(act_quant_kernel<true, 8>, grid, dim3(256), st, tm, x, inv_s, T, H,
+                                  qx, sx, ac);
+    return launch_kernel(act_quant_kernel<false, 8>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx,
+                         ac);
+  }
+  if (fp8) return launch_kernel(act_quant_kernel<true, 16>, grid, dim3(256), st, tm, x, inv_s, T, H,
+                                qx, sx, ac);
+  return launch_kernel(act_quant_kernel<false, 16>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx,
+                       ac);
 }
 
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
