@@ -64,10 +64,11 @@ def _load():
         "oracle_percentile_rank": (_I64, [ctypes.c_double, _I64]),
         "oracle_expert_rows": (None, [_I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
-        "oracle_combine": (None, [_I64, _P, _I32, _I32, _P, _P, _P, _P, _P]),
+        "oracle_combine": (None, [_I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P]),
         "oracle_forward": (_I64, [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _F32,
                                   _P, _P, _P, _P, _P, _F32, _F32, _I32,
-                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P]),
         "oracle_num_threads": (ctypes.c_int, []),
     }
     for name, (res, args) in sig.items():
@@ -255,8 +256,9 @@ def expert_rows(rows, ids, sorted_, qx, sx, cal, want_acc1: bool = True, want_h:
     return dict(acc1=acc1 if fmt == FMT_INT8 else acc1f, h=h, qh=qh, sh=sh, y=y)
 
 
-def combine(tokens, w, row_of, y, y_row_index=None):
-    """Gate-weighted sum for the listed tokens; returns bf16 bits [n][H]."""
+def combine(tokens, w, row_of, y, y_row_index=None, want_exact: bool = False):
+    """Gate-weighted sum for the listed tokens; returns bf16 bits [n][H], or
+    (bits, the fp64 sums before rounding) with want_exact."""
     w = _c(w, np.float32)
     T, k = w.shape
     row_of = _c(row_of, np.int32)
@@ -266,14 +268,17 @@ def combine(tokens, w, row_of, y, y_row_index=None):
     n = T if tok is None else tok.shape[0]
     yri = None if y_row_index is None else _c(y_row_index, np.int64)
     out = np.empty((n, H), np.uint16)
-    _load().oracle_combine(n, _ptr(tok), H, k, _ptr(w), _ptr(row_of), _ptr(yri), _ptr(y), _ptr(out))
-    return out
+    exact = np.empty((n, H), np.float64) if want_exact else None
+    _load().oracle_combine(n, _ptr(tok), H, k, _ptr(w), _ptr(row_of), _ptr(yri), _ptr(y), _ptr(out),
+                           _ptr(exact))
+    return (out, exact) if want_exact else out
 
 
 def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor: float = 0.0,
             want_acc1: bool = True, want_h: bool = True, clip: float = 0.0,
             sat_percentile: float = 0.0, fmt: int = FMT_INT8):
-    """The whole layer on the CPU. Returns a dict of every stage's output."""
+    """The whole layer on the CPU. Returns a dict of every stage's output
+    ("out_exact": the combine's fp64 sums before the rounding to bf16)."""
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
     q_gu, sw_gu = _c(cal["q_gu"], np.int8), _c(cal["sw_gu"], np.float32)
@@ -295,14 +300,15 @@ def forward(x_bf16, cal, k: int, logits=None, ids=None, w=None, capacity_factor:
              acc1f=np.empty((A, 2 * F), np.float64) if want_acc1 and fmt == FMT_FP8 else None,
              h=np.empty((A, F), np.float32) if want_h else None,
              qh=np.empty((max(A, 1), F), np.int8), sh=np.empty(max(A, 1), np.float32),
-             y=np.empty((max(A, 1), H), np.float64), out=np.empty((T, H), np.uint16))
+             y=np.empty((max(A, 1), H), np.float64), out=np.empty((T, H), np.uint16),
+             out_exact=np.empty((T, H), np.float64))
     kept = _load().oracle_forward(
         T, H, F, E, k, _ptr(x), _ptr(lg), _ptr(ids_in), _ptr(w_in), float(capacity_factor),
         _ptr(q_gu), _ptr(sw_gu), _ptr(q_d), _ptr(sw_d), _ptr(inv_s), float(clip),
         float(np.float32(sat_percentile)), int(fmt), _ptr(o["ids"]), _ptr(o["w"]),
         _ptr(o["counts"]), _ptr(o["offsets"]), _ptr(o["sorted"]), _ptr(o["row_of"]), _ptr(o["qx"]),
         _ptr(o["sx"]), _ptr(o["acc1"]), _ptr(o["acc1f"]), _ptr(o["h"]), _ptr(o["qh"]),
-        _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]))
+        _ptr(o["sh"]), _ptr(o["y"]), _ptr(o["out"]), _ptr(o["out_exact"]))
     kept = int(kept)
     o["kept"] = kept
     o["sorted"] = o["sorted"][:kept]

@@ -535,10 +535,11 @@ void oracle_expert_rows(int64_t nrows, const int32_t *rows, int32_t H, int32_t F
  *                   w[t][j] * y[row_of[t*k+j]][n] ), summed in fp64 in slot
  * order and rounded once to bfloat16. A dropped slot contributes nothing and
  * the remaining weights are not renormalised. y_row_index maps a permuted row
- * to its row in y (NULL: identity). */
+ * to its row in y (NULL: identity). exact (may be NULL) receives the fp64 sum
+ * itself, before the rounding to bfloat16. */
 void oracle_combine(int64_t ntok, const int64_t *tokens, int32_t H, int32_t k,
                     const float *w, const int32_t *row_of, const int64_t *y_row_index,
-                    const double *y, uint16_t *out) {
+                    const double *y, uint16_t *out, double *exact) {
   #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < ntok; ++i) {
     int64_t t = tokens ? tokens[i] : i;
@@ -551,6 +552,7 @@ void oracle_combine(int64_t ntok, const int64_t *tokens, int32_t H, int32_t k,
         acc += (double)w[t * k + j] * y[yr * H + n];
       }
       out[i * (int64_t)H + n] = oracle_f64_to_bf16(acc);
+      if (exact) exact[i * (int64_t)H + n] = acc;
     }
   }
 }
@@ -562,7 +564,8 @@ void oracle_combine(int64_t ntok, const int64_t *tokens, int32_t H, int32_t k,
  * All buffers are host memory owned by the caller. logits == NULL selects
  * pre-routed mode (ids_in/w_in). acc1 and h may be NULL. Sizes: A = T*k;
  * ids, w, row_of [A]; counts [E]; offsets [E+1]; sorted, sh [A]; qx [T][H];
- * sx [T]; acc1 [A][2F]; h, qh [A][F]; y [A][H] (fp64); out [T][H] bf16.
+ * sx [T]; acc1 [A][2F]; h, qh [A][F]; y [A][H] (fp64); out [T][H] bf16;
+ * out_exact [T][H] fp64 (may be NULL): the combine's sum before rounding.
  * Returns the number of kept rows. */
 int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                        const uint16_t *x, const float *logits,
@@ -573,7 +576,7 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
                        int32_t *ids, float *w, int32_t *counts, int32_t *offsets,
                        int32_t *sorted, int32_t *row_of, int8_t *qx, float *sx,
                        int32_t *acc1, double *acc1f, float *h, int8_t *qh, float *sh,
-                       double *y, uint16_t *out) {
+                       double *y, uint16_t *out, double *out_exact) {
   int64_t A = T * k;
   if (logits) oracle_route(T, E, k, logits, ids, w);
   else {
@@ -588,7 +591,7 @@ int64_t oracle_forward(int64_t T, int32_t H, int32_t F, int32_t E, int32_t k,
   oracle_expert_rows(kept, rows, H, F, k, ids, sorted, qx, sx, q_gu, sw_gu, q_d, sw_d, fmt,
                      acc1, acc1f, h, qh, sh, y);
   free(rows);
-  oracle_combine(T, NULL, H, k, w, row_of, NULL, y, out);
+  oracle_combine(T, NULL, H, k, w, row_of, NULL, y, out, out_exact);
   return kept;
 }
 

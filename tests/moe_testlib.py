@@ -7,12 +7,13 @@ Parity bar (what the benchmark spec of the layer fixes):
   - routing weights: |diff| <= 1e-6;
   - requantised hidden codes: |diff| <= 1 everywhere and diff != 0 in at most
     0.1 % of entries; their scales: relative diff <= 1e-5;
-  - layer output (bf16): |diff| <= 2e-2 * RMS(oracle output) element by element, plus
-    one bf16 step at the element's magnitude. Both sides round the final sum to bf16,
-    the kernels from fp32 and the oracle from fp64, so an element whose exact value
-    lies within that difference of a rounding midpoint rounds one step apart; that
-    step (up to 2^-7 of the value) exceeds 2e-2 * RMS wherever the output is more
-    than 2.56x its RMS.
+  - layer output (bf16), element by element against the oracle's exact fp64
+    sum before its rounding: |gpu - exact| <= 2e-2 * RMS(exact) + half a bf16
+    step at |gpu|. The half step is the GPU's own final rounding to bf16, the
+    one part of the difference that no implementation can avoid; everything
+    else (requantisation flips, fp32 sums) must fit in 2e-2 * RMS. How many
+    elements needed the half step, and the largest error over RMS without it,
+    are reported.
 """
 from __future__ import annotations
 
@@ -148,15 +149,46 @@ def bf16_step(v: np.ndarray) -> np.ndarray:
     return np.where(a > 0, 2.0 ** (e - 7), 0.0)
 
 
-def check_out(out_g_bits, out_o_bits):
-    from synth import bf16_bits_to_f32
-    g = bf16_bits_to_f32(out_g_bits).astype(np.float64)
-    o = bf16_bits_to_f32(out_o_bits).astype(np.float64)
-    rms = np.sqrt(np.mean(o ** 2)) if o.size else 0.0
-    diff = np.abs(g - o)
-    lim = OUT_RMS_FRAC * rms + bf16_step(np.maximum(np.abs(g), np.abs(o))) + 1e-30
-    worst = np.max(diff - lim, initial=-1.0)
-    err = np.max(diff, initial=0.0)
-    assert worst <= 0, "output err %.4g over the bar (max err %.4g, 2e-2 x rms %.4g)" % (
-        worst, err, OUT_RMS_FRAC * rms)
-    return err / rms if rms else 0.0
+class OutCheck:
+    """Output bar over one or more chunks of tokens: |gpu - exact| <=
+    2e-2 * RMS(exact over every chunk) + half a bf16 step at |gpu|."""
+
+    def __init__(self):
+        self.sumsq = 0.0
+        self.n = 0
+        self.diff = []     # |gpu - exact| per element, by chunk
+        self.half = []     # half a bf16 step at |gpu|
+
+    def add(self, out_g_bits, exact):
+        from synth import bf16_bits_to_f32
+        g = bf16_bits_to_f32(out_g_bits).astype(np.float64).ravel()
+        x = np.asarray(exact, np.float64).ravel()
+        assert g.shape == x.shape
+        self.sumsq += float(np.sum(x * x))
+        self.n += x.size
+        self.diff.append(np.abs(g - x))
+        self.half.append(0.5 * bf16_step(g))
+
+    def finish(self, label=""):
+        rms = np.sqrt(self.sumsq / self.n) if self.n else 0.0
+        diff = np.concatenate(self.diff) if self.diff else np.zeros(0)
+        half = np.concatenate(self.half) if self.half else np.zeros(0)
+        bar = OUT_RMS_FRAC * rms
+        excess = diff - (bar + half + 1e-30)
+        worst = float(np.max(excess, initial=-1.0))
+        err = float(np.max(diff, initial=0.0))
+        n_step = int(np.count_nonzero(diff > bar))
+        rel = err / rms if rms else 0.0
+        print("[out] %s %d elements: max |gpu - exact| = %.4g x RMS (bar %.3g x RMS); "
+              "%d elements past 2e-2 x RMS, within half a bf16 step" % (
+                  label, diff.size, rel, OUT_RMS_FRAC, n_step), flush=True)
+        assert worst <= 0, ("output over the bar by %.4g (max err %.4g, 2e-2 x rms %.4g)"
+                            % (worst, err, bar))
+        return rel
+
+
+def check_out(out_g_bits, exact, label=""):
+    """The output bar on one batch: exact is the oracle's fp64 sum (out_exact)."""
+    c = OutCheck()
+    c.add(out_g_bits, exact)
+    return c.finish(label)

@@ -99,7 +99,7 @@ def clip_full_parity(torch, wl, gemm_path, static, sat_p):
         qh = res["gpu_tensors"]["qh"].view(-1, wl.F)[:kept].cpu().numpy()
         sh = res["gpu_tensors"]["sh"][:kept].cpu().numpy()
         check_requant(qh, sh, o["qh"], o["sh"])
-    check_out(res["out"], o["out"])
+    check_out(res["out"], o["out_exact"])
 
 
 def test_saturation_rank_limit(torch_cuda):
