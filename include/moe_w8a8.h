@@ -182,6 +182,9 @@ typedef struct {
 
 /* Bytes of device workspace that moe_w8a8_forward needs for T tokens, and
  * that moe_w8a8_calibrate needs (T = 0 gives at least the calibrate size).
+ * The caller allocates it once and hands it to every call
+ * ("MiniMax-M3 W8A8 inference on K100AI" §4.3: reuse device memory from a
+ * pool instead of allocating per call); the library allocates nothing.
  * A pure function of the arguments, nondecreasing in T (a workspace sized for
  * the largest batch serves every smaller one); returns 0 for invalid or
  * unsupported dimensions or T < 0. */
@@ -278,6 +281,23 @@ int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
 int moe_w8a8_router_logits(const moe_w8a8_dims *dims, const uint16_t *x, int64_t T,
                            const uint16_t *w_router, float *logits,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Pack row-major codes into the fragment-tiled layout of moe_w8a8_weights
+ * ("MiniMax-M3 W8A8 inference on K100AI" §3.2-§3.3: weights quantised by an
+ * offline tool are built into the engine's own layout), so that INT8 or FP8
+ * codes quantised elsewhere can be loaded:
+ *   src   int8 (or e4m3 bytes) [count][N][K], row-major, device memory;
+ *   dst   int8 [count][N][K] in the fragment-tiled layout (matrix c at byte
+ *         c*N*K), device memory, not overlapping src.
+ * Per expert: w_gate_up is count = E, N = 2F (gate rows, then up rows),
+ * K = H; w_down is count = E, N = H, K = F. The scales (s_gate_up, s_down)
+ * and smooth/inv_smooth are plain arrays and need no packing.
+ * Nothing is allocated; the copy is enqueued on `stream`.
+ * Errors: MOE_W8A8_ERR_INVALID (NULL pointer, count, N or K <= 0, a pointer
+ * not 16-byte aligned, overlapping buffers, more than 2^40 bytes),
+ * MOE_W8A8_ERR_UNSUPPORTED (N % 16 != 0 or K % 64 != 0), MOE_W8A8_ERR_HIP. */
+int moe_w8a8_pack(int64_t count, int32_t N, int32_t K, const int8_t *src, int8_t *dst,
+                  void *stream);
 
 /* Static description of a return code (never NULL). */
 const char *moe_w8a8_strerror(int code);

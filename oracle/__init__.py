@@ -43,9 +43,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    # The sanitizer test runs the pins against an instrumented build of the
+    # same source, named by this variable.
+    path = os.environ.get("MOE_ORACLE_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(force=True)
+    lib = ctypes.CDLL(path)
     sig = {
         "oracle_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
         "oracle_quant_rows": (None, [_I64, _I64, _P, _P, _P]),

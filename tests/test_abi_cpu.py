@@ -14,10 +14,13 @@ FAKE = 0x10000  # a non-NULL pointer that validation never dereferences
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(m.LIB_PATH):
+    # The sanitizer test runs these cases against an instrumented build of the
+    # library, named by this variable.
+    path = os.environ.get("MOE_W8A8_TEST_LIB", m.LIB_PATH)
+    if not os.path.exists(path):
         from w8a8_int8_expert_amd import build
         build.build()
-    return m.load_library()
+    return m.load_library(path)
 
 
 def _declared_functions():
@@ -180,3 +183,57 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         mod._lib = saved
+
+
+def test_binding_rejects_mismatched_tensors(lib):
+    """The Python binding checks dtype, shape, contiguity and device of every
+    tensor before it hands raw pointers to the library (CPU tensors on a
+    CPU-placed layer: every case is refused before any call into the library)."""
+    import torch
+    H, F, E, k, T = 256, 128, 8, 2, 5
+    g = m.MoEW8A8(H, F, E, k, device="cpu")
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    lg = torch.zeros(T, E, dtype=torch.float32)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    w = torch.zeros(T, k, dtype=torch.float32)
+    bad = [
+        dict(x=x.float(), router_logits=lg),                        # x not bf16
+        dict(x=torch.zeros(T, H + 8, dtype=torch.bfloat16), router_logits=lg),  # width != H
+        dict(x=torch.zeros(H, T, dtype=torch.bfloat16).t(), router_logits=lg),  # not contiguous
+        dict(x=x, router_logits=lg.to(torch.bfloat16)),             # logits not fp32
+        dict(x=x, router_logits=torch.zeros(T, E + 1)),             # logits [T][E+1]
+        dict(x=x, topk_ids=ids.long(), topk_w=w),                   # int64 ids (torch.topk's)
+        dict(x=x, topk_ids=torch.zeros(T, k + 1, dtype=torch.int32), topk_w=w),
+        dict(x=x, topk_ids=ids, topk_w=w.double()),
+        dict(x=x, router_logits=lg, out=torch.zeros(T, H)),         # out not bf16
+        dict(x=x, router_logits=lg, out=torch.zeros(T - 1, H, dtype=torch.bfloat16)),
+    ]
+    for kw in bad:
+        with pytest.raises(m.MoEW8A8Error):
+            g.forward(**kw)
+    with pytest.raises(m.MoEW8A8Error):
+        g.calibrate(x, torch.zeros(E, F, H), torch.zeros(E, F, H), torch.zeros(E, F, H), 0.6)
+    with pytest.raises(m.MoEW8A8Error):
+        g.calibrate(x.float(), torch.zeros(E, F, H), torch.zeros(E, F, H),
+                    torch.zeros(E, H, F), 0.6)
+    if torch.cuda.is_available():  # a tensor on another device than the layer's
+        with pytest.raises(m.MoEW8A8Error):
+            g.forward(x.cuda(), router_logits=lg)
+
+
+def test_pack_validation(lib):
+    """moe_w8a8_pack refuses bad sizes, NULL, misaligned or overlapping buffers
+    before anything is enqueued."""
+    A, B = 0x100000, 0x900000   # 16-byte aligned, 8 MiB apart
+    INV, UNS = m.MOE_W8A8_ERR_INVALID, m.MOE_W8A8_ERR_UNSUPPORTED
+    assert lib.moe_w8a8_pack(0, 16, 64, A, B, None) == INV
+    assert lib.moe_w8a8_pack(1, 0, 64, A, B, None) == INV
+    assert lib.moe_w8a8_pack(1, 16, -64, A, B, None) == INV
+    assert lib.moe_w8a8_pack(1, 16, 64, None, B, None) == INV
+    assert lib.moe_w8a8_pack(1, 16, 64, A, None, None) == INV
+    assert lib.moe_w8a8_pack(1, 16, 64, A + 8, B, None) == INV        # misaligned
+    assert lib.moe_w8a8_pack(1, 16, 64, A, A + 512, None) == INV      # overlapping
+    assert lib.moe_w8a8_pack(4, 16, 64, A, A + 2048, None) == INV     # 4 KB overlaps
+    assert lib.moe_w8a8_pack(1, 24, 64, A, B, None) == UNS            # N % 16
+    assert lib.moe_w8a8_pack(1, 16, 96, A, B, None) == UNS            # K % 64
+    assert lib.moe_w8a8_pack(1 << 20, 1 << 14, 1 << 14, A, B, None) == INV   # > 2^40 bytes

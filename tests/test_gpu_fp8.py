@@ -3,27 +3,27 @@
 Codes are decided in fp32 by the same operation sequence on both sides, so
 weight codes, scales and activation codes are bit-exact. The GEMMs
 accumulate on the FP8 matrix instructions on the GPU and exactly (fp64) in
-the oracle. Those instructions do not round each addition to fp32; measured
-on MI355X, their error follows the largest product of each 64-long block of
-the sum rather than the sum of |products|: it stays below ~3.4e-6 of
-B = sum over 64-blocks of 64 * max|a| * max|b| (a and b the operands' values
-in the block), also where outlier channels make one product dominate, while
-its ratio to sum |products| ranges over 100x. Hence, for FP8 only:
-  - GEMM1 sums within 2^-15 * B (9x above the largest error seen; a missing
-    16-byte chunk of products shows up at ~1/K of B, far above it);
-  - requantised codes within one e4m3 step plus 2^-4 (in the 448-range code
-    space) and differing in at most 1 % of entries (an h within that error of
-    one of e4m3's 8-16 rounding midpoints per binade flips a code);
-  - requant scales within 1e-3 relative (a row's largest |h| carries the
-    sum error, from both gate and up);
-  - the layer output equal, element by element, to the exact down
-    projection and combine applied to the GPU's own requantised codes and
-    scales, within the same GEMM2 accumulation bound (2^-15 * B per row,
-    carried through the gate weights) plus one bf16 step. Its distance to the
-    oracle's output is then the effect of the code differences bounded above;
-    it is printed, not held to a fixed fraction of the RMS. With outlier
-    channels or lognormal tokens, single rounding steps at outputs 20-50x the
-    RMS are a large fraction of it. INT8 keeps the spec bar of 2e-2 x RMS.
+the oracle. Those instructions do not round each addition to fp32; no
+document states their accumulation error, so it is taken as a measured
+assumption: on MI355X it stays below 3.4e-6 of B = sum over 64-long K blocks
+of 64 * max|a| * max|b| (a and b the operands' decoded values in the block),
+also where outlier channels make one product dominate. The bars take
+2^-15 * B, nine times the largest error measured.
+
+Every other bar is derived from that assumption and the oracle's own
+quantities alone (fp8_bounds below), never from the GPU's intermediates:
+  - the gate and up sums' error, carried through the dequantisation and
+    SwiGLU (first order, |silu'| <= 1.1, plus the fp32 roundings and the
+    exponential's argument rounding), bounds each h element and the row max;
+  - a requantised code may differ from the oracle's only where the oracle's
+    value v = h * 448/max lies within that bound of a rounding midpoint of
+    e4m3, and then by the gap between the two e4m3 values around it; the
+    scale differs at most by the row max's bound;
+  - each output element is within the sum, over its token's kept slots, of
+    |w| times (the flips' gaps through |W_down| and the scales, the GEMM2
+    accumulation bound of the same form, the scale's bound times |y|), plus
+    the fp32 roundings of y and of the combine, plus half a bf16 step at the
+    GPU's value (its own final rounding), of the oracle's exact fp64 sum.
 """
 import sys
 
@@ -38,9 +38,7 @@ from moe_testlib import (check_act_quant, check_routing_and_grouping, run_gpu, u
 pytestmark = pytest.mark.gpu
 
 LUT = np.array([oracle.e4m3_value(c) for c in range(256)])
-ACC_BLK = 2.0 ** -15      # GEMM sums, relative to the 64-block bound B
-QH_FRAC = 1e-2            # requantised codes that may differ
-SH_RTOL_FP8 = 1e-3
+ACC_BLK = 2.0 ** -15      # GEMM sums, relative to the 64-block bound B (measured assumption)
 
 
 def block_bound(a_vals, b_vals):
@@ -110,9 +108,93 @@ def test_fp8_forward_parity(torch_cuda, case, gemm_path):
     fp8_full_parity(wl, gemm_path)
 
 
+def fp8_bounds(o, cal, wl):
+    """Per-element bounds of the GPU's FP8 layer around the oracle's values,
+    from the oracle's quantities and the accumulation assumption only.
+    o: oracle.forward(..., fmt=FMT_FP8) with acc1 and h."""
+    kept, F, H, k = o["kept"], wl.F, wl.H, wl.k
+    tok = o["sorted"] // k
+    exp_id = o["ids"].reshape(-1)[o["sorted"]]
+    xv = LUT[o["qx"].view(np.uint8)]
+    sx = o["sx"].astype(np.float64)[tok]
+    acc = o["acc1"]
+    b1 = np.empty((kept, 2 * F))
+    for e in np.unique(exp_id):
+        rows = np.nonzero(exp_id == e)[0]
+        b1[rows] = block_bound(xv[tok[rows]], LUT[cal["q_gu"][e].view(np.uint8)])
+    acc_tol = ACC_BLK * b1
+    swg = cal["sw_gu"].astype(np.float64)[exp_id]
+    g = acc[:, :F] * sx[:, None] * swg[:, :F]
+    u = acc[:, F:] * sx[:, None] * swg[:, F:]
+    dg = acc_tol[:, :F] * sx[:, None] * np.abs(swg[:, :F]) + 2.0 ** -22 * np.abs(g)
+    du = acc_tol[:, F:] * sx[:, None] * np.abs(swg[:, F:]) + 2.0 ** -22 * np.abs(u)
+    silu = g / (1.0 + np.exp(-g))
+    hx = silu * u
+    # |silu'| <= 1.1; the GPU's exponential rounds its argument (relative 2^-24
+    # of g, i.e. |g| * 2^-24 of the result) and a few fp32 operations follow
+    rs = (16.0 + 2.0 * np.abs(g)) * 2.0 ** -24
+    dh = 1.1 * dg * (np.abs(u) + du) + (np.abs(silu) + 1.1 * dg) * du + (rs + 2.0 ** -23) * np.abs(hx)
+    h = o["h"].astype(np.float64)
+    amax = np.abs(h).max(axis=1)
+    da = dh.max(axis=1)
+    # a row's maximum must stand clear of its own error bound (an all-zero row
+    # is exact); the workloads here never come near that
+    zero = (amax == 0) & (da == 0)
+    assert np.all(zero | (amax > 2.0 * da)), "a row maximum within its error bound"
+    rho = np.where(zero, 0.0, da / np.maximum(amax - da, 1e-300)) + 2.0 ** -22
+    rr = np.where(amax > 0, 448.0 / np.maximum(amax, 1e-300), 0.0)
+    v = np.abs(h) * rr[:, None]
+    dv = rr[:, None] * (dh + np.abs(h) * rho[:, None]) + 2.0 ** -22 * v
+    # e4m3 rounding midpoints (non-negative side) and the gap across each
+    pos = LUT[:127]
+    mids = 0.5 * (pos[:-1] + pos[1:])
+    gaps = np.diff(pos)
+    vc = np.minimum(v, 448.0)
+    j = np.clip(np.searchsorted(mids, vc), 1, mids.size - 1)
+    d_lo, d_hi = vc - mids[j - 1], mids[j] - vc
+    near = np.where(np.abs(d_lo) <= np.abs(d_hi), j - 1, j)
+    dist = np.minimum(np.abs(d_lo), np.abs(d_hi))
+    j0 = np.searchsorted(mids, vc)
+    dist = np.where(j0 == 0, mids[0] - vc, dist)
+    near = np.where(j0 == 0, 0, near)
+    # |gpu code - oracle code| <= |gpu code - v_gpu| + |v_gpu - v| + |v - oracle code|
+    # <= dv + the e4m3 spacing at |v| + dv (each rounding within half of it)
+    spacing = gaps[np.clip(np.searchsorted(pos, np.minimum(vc + dv, 448.0)) - 1, 0, gaps.size - 1)]
+    flip = np.where(dist <= dv, dv + spacing, 0.0)
+    # GEMM2 and y
+    qv = LUT[o["qh"].view(np.uint8)]
+    sh = o["sh"].astype(np.float64)
+    y_tol = np.empty((kept, H))
+    y_abs = np.empty((kept, H))
+    for e in np.unique(exp_id):
+        rows = np.nonzero(exp_id == e)[0]
+        wd = LUT[cal["q_d"][e].view(np.uint8)]
+        sw = np.abs(cal["sw_d"][e].astype(np.float64))[None, :]
+        s_ex = qv[rows] @ wd.T
+        y = np.abs(s_ex) * sh[rows, None] * sw
+        dS = flip[rows] @ np.abs(wd).T + ACC_BLK * block_bound(np.abs(qv[rows]) + flip[rows], wd)
+        t1 = dS * sh[rows, None] * (1.0 + rho[rows, None]) * sw + y * rho[rows, None]
+        y_tol[rows] = t1 + 2.0 ** -22 * (y + t1)
+        y_abs[rows] = y + t1
+    out_tol = np.zeros((wl.T, H))
+    mag = np.zeros((wl.T, H))
+    w = np.abs(o["w"].astype(np.float64))
+    for jj in range(k):
+        r = o["row_of"][:, jj]
+        keep = r >= 0
+        out_tol[keep] += w[keep, jj][:, None] * y_tol[r[keep]]
+        mag[keep] += w[keep, jj][:, None] * y_abs[r[keep]]
+    out_tol += (k + 2) * 2.0 ** -23 * mag
+    return dict(acc_tol=acc_tol, h_tol=dh, sh_rtol=rho, code_gap=flip, out_tol=out_tol,
+                n_may_flip=int(np.count_nonzero(flip)))
+
+
 def fp8_full_parity(wl, gemm_path):
-    """Every stage of the FP8 layer on workload wl against the oracle, to the FP8 bars."""
+    """Every stage of the FP8 layer on workload wl against the oracle, to the
+    bars fp8_bounds derives."""
     import w8a8_int8_expert_amd as m
+    from moe_testlib import bf16_step
+    from synth import bf16_bits_to_f32
     layer = synth.make_layer(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
@@ -127,69 +209,66 @@ def fp8_full_parity(wl, gemm_path):
     kept = o["kept"]
     if kept == 0:
         return
-    # GEMM1: fp32 sums against the exact ones, within the 64-block bound
+    b = fp8_bounds(o, cal, wl)
+    # GEMM1: fp32 sums against the exact ones
     acc1 = res["gpu_tensors"]["acc1"].view(-1, 2 * wl.F)[:kept].cpu().numpy().view(np.float32)
-    tok = o["sorted"] // wl.k
-    exp_id = o["ids"].reshape(-1)[o["sorted"]]
-    xv = LUT[o["qx"].view(np.uint8)]
-    bound = np.empty((kept, 2 * wl.F))
-    for e in np.unique(exp_id):
-        rows = np.nonzero(exp_id == e)[0]
-        bound[rows] = block_bound(xv[tok[rows]], LUT[cal["q_gu"][e].view(np.uint8)])
     err = np.abs(acc1.astype(np.float64) - o["acc1"])
-    rel = err / np.maximum(bound, 1e-300)
-    _say("[fp8] GEMM1 error / 64-block bound: median %.3g, 99.9%% %.3g, max %.3g" % (
+    rel = err / np.maximum(b["acc_tol"], 1e-300)
+    _say("[fp8] GEMM1 error / bound: median %.3g, 99.9%% %.3g, max %.3g" % (
         np.median(rel), np.quantile(rel, 0.999), rel.max()))
-    assert np.all(err <= ACC_BLK * bound + 1e-30), "max %.3g of the block bound" % rel.max()
-    # Requantised codes, compared by value in the code space (v * 448/max):
-    # at most one e4m3 step at their magnitude plus 2^-4 absolute. The
-    # absolute part covers h near zero, where e4m3 steps (2^-9) are finer
-    # than the accumulation error that reaches h when the gate or up sum
-    # cancels; 2^-4 is 1/7168 of the row's range.
+    assert np.all(err <= b["acc_tol"] + 1e-30), "GEMM1 sums: max %.3g of the bound" % rel.max()
+    h = res["gpu_tensors"]["h"].view(-1, wl.F)[:kept].cpu().numpy().astype(np.float64)
+    herr = np.abs(h - o["h"].astype(np.float64))
+    assert np.all(herr <= b["h_tol"] + 1e-30), "SwiGLU output: max %.3g of the bound" % (
+        np.max(herr / np.maximum(b["h_tol"], 1e-300)))
+    # Requantised codes: equal to the oracle's, or one e4m3 gap away where the
+    # oracle's value lies within the bound of a rounding midpoint
     qh = res["gpu_tensors"]["qh"].view(-1, wl.F)[:kept].cpu().numpy()
     tg, to = LUT[qh.view(np.uint8)], LUT[o["qh"].view(np.uint8)]
-    mag = np.maximum(np.abs(tg), np.abs(to))
-    step = np.where(mag < 2.0 ** -6, 2.0 ** -9,
-                    2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3))
     dist = np.abs(tg - to)
-    assert np.all(dist <= step + 2.0 ** -4), "max excess %.4g" % np.max(dist - step)
-    frac = np.count_nonzero(dist) / dist.size
-    _say("[fp8] requantised codes differing: %.4f %%" % (100 * frac))
-    assert frac <= QH_FRAC
-    sh = res["gpu_tensors"]["sh"][:kept].cpu().numpy()
-    np.testing.assert_allclose(sh, o["sh"], rtol=SH_RTOL_FP8, atol=0)
-    # Output: the exact down projection and combine on the GPU's own codes and
-    # scales, and the GEMM2 accumulation bound carried through the gate weights.
-    from synth import bf16_bits_to_f32
-    shg = sh.astype(np.float64)
+    n_diff = int(np.count_nonzero(dist))
+    _say("[fp8] requantised codes differing: %d (%.4f %%); may flip by the bound: %d" % (
+        n_diff, 100.0 * n_diff / dist.size, b["n_may_flip"]))
+    assert np.all(dist <= b["code_gap"]), "a code differs where no flip is possible"
+    sh = res["gpu_tensors"]["sh"][:kept].cpu().numpy().astype(np.float64)
+    sh_o = o["sh"].astype(np.float64)
+    assert np.all(np.abs(sh - sh_o) <= b["sh_rtol"] * sh_o + 1e-30), "requant scales"
+    # Output, given the GPU's own codes and scales (checked against the oracle's
+    # just above): the exact down projection and combine of those, within the
+    # GEMM2 accumulation bound, the fp32 roundings and half a bf16 step.
+    got = bf16_bits_to_f32(res["out"]).astype(np.float64)
+    half = 0.5 * bf16_step(got)
     qv = LUT[qh.view(np.uint8)]
+    exp_id = o["ids"].reshape(-1)[o["sorted"]]
     y_own = np.empty((kept, wl.H))
     y_tol = np.empty((kept, wl.H))
     for e in np.unique(exp_id):
         rows = np.nonzero(exp_id == e)[0]
         wd = LUT[cal["q_d"][e].view(np.uint8)]
-        sc = shg[rows, None] * np.abs(cal["sw_d"][e].astype(np.float64))[None, :]
-        y_own[rows] = (qv[rows] @ wd.T) * shg[rows, None] * cal["sw_d"][e].astype(np.float64)[None, :]
-        y_tol[rows] = ACC_BLK * block_bound(qv[rows], wd) * sc
+        sc = sh[rows, None] * cal["sw_d"][e].astype(np.float64)[None, :]
+        y_own[rows] = (qv[rows] @ wd.T) * sc
+        y_tol[rows] = ACC_BLK * block_bound(qv[rows], wd) * np.abs(sc)
     row_of = o["row_of"]
-    w = o["w"].astype(np.float64)
-    T = wl.T
-    tol = np.zeros((T, wl.H))
-    mag = np.zeros((T, wl.H))
+    w = np.abs(o["w"].astype(np.float64))
+    tol = np.zeros((wl.T, wl.H))
+    mag = np.zeros((wl.T, wl.H))
     for j in range(wl.k):
         r = row_of[:, j]
         keep = r >= 0
-        tol[keep] += np.abs(w[keep, j])[:, None] * y_tol[r[keep]]
-        mag[keep] += np.abs(w[keep, j])[:, None] * np.abs(y_own[r[keep]])
-    own = bf16_bits_to_f32(oracle.combine(None, o["w"], row_of, y_own)).astype(np.float64)
-    got = bf16_bits_to_f32(res["out"]).astype(np.float64)
-    want = bf16_bits_to_f32(o["out"]).astype(np.float64)
-    # one bf16 step at the larger of the two values, and fp32 sums (2^-20 of the terms)
-    step = 2.0 ** -7 * np.maximum(np.abs(got), np.abs(own))
-    lim = tol + step + 2.0 ** -20 * mag + 1e-30
-    excess = np.abs(got - own) - lim
-    rms = np.sqrt(np.mean(want ** 2))
-    _say("[fp8] output vs own-code pipeline: max %.4g of RMS (worst excess %.3g); "
-         "vs oracle: max %.4g of RMS" % (np.abs(got - own).max() / rms, excess.max(),
-                                          np.abs(got - want).max() / rms))
-    assert np.all(excess <= 0), "output off the own-code pipeline by %.4g" % excess.max()
+        tol[keep] += w[keep, j][:, None] * y_tol[r[keep]]
+        mag[keep] += w[keep, j][:, None] * (np.abs(y_own[r[keep]]) + y_tol[r[keep]])
+    _, own = oracle.combine(None, o["w"], row_of, y_own, want_exact=True)
+    lim_own = tol + (wl.k + 2) * 2.0 ** -23 * mag + half + 1e-30
+    d_own = np.abs(got - own)
+    assert np.all(d_own <= lim_own), "output off its own codes' pipeline by %.4g" % np.max(
+        d_own - lim_own)
+    # Output against the oracle's exact sum, within the worst case of every
+    # code that may flip flipping (fp8_bounds)
+    exact = o["out_exact"]
+    lim = b["out_tol"] + half + 1e-30
+    diff = np.abs(got - exact)
+    rms = np.sqrt(np.mean(exact ** 2))
+    _say("[fp8] output vs oracle: max %.4g of RMS; bound median %.3g, max %.4g of RMS; "
+         "largest error / bound %.3g" % (diff.max() / rms, np.median(lim) / rms, lim.max() / rms,
+                                         np.max(diff / lim)))
+    assert np.all(diff <= lim), "output past the bound by %.4g" % np.max(diff - lim)

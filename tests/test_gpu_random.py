@@ -57,10 +57,44 @@ def test_random_config_parity(torch_cuda, i):  # noqa: F811
 
 
 
+# Six draws over the widest routing the library accepts: 129 to 1024 experts
+# (two to sixteen experts per router lane) and top-k up to 32, small hidden and
+# FFN sizes, with or without capacity and tied logits.
+N_WIDE = 6
+
+
+def _draw_wide(i):
+    rng = np.random.default_rng(np.random.SeedSequence([2026, i]))
+    E = int(rng.choice([129, 200, 256, 257, 512, 700, 1000, 1024]))
+    k = int(rng.choice([1, 3, 8, 9, 16, 17, 31, 32]))
+    H = int(rng.choice([256, 512]))
+    F = int(rng.choice([128, 256]))
+    T = int(rng.integers(1, max(2, int(2.5e9 // (k * 3 * H * F))) + 1))
+    T = min(T, 1500)
+    over = dict(T=T, H=H, F=F, E=E, k=k, layer_seed=9000 + i, input_seed=9500 + i)
+    if rng.random() < 0.4:
+        over["capacity_factor"] = float(np.round(rng.uniform(0.6, 1.5), 2))
+    if rng.random() < 0.4:
+        over["logit_step"] = 0.25
+    return over, int(rng.integers(1, 3))
+
+
+CASES_WIDE = [_draw_wide(i) for i in range(N_WIDE)]
+
+
+@pytest.mark.parametrize("i", range(N_WIDE))
+def test_random_config_wide_routing_parity(torch_cuda, i):  # noqa: F811
+    over, path = CASES_WIDE[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random wide] case=%d path=%d %s" % (i, path, over))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    _full_parity(wl, inputs, cal, path)
+
+
 # The FP8 (e4m3) expert path on twelve further draws, to its own bars (activation
-# codes and scales bit-exact; GEMM sums within the 64-block accumulation bound;
-# requantised codes within one e4m3 step; output equal to the exact pipeline on
-# the GPU's own codes within the accumulation bound and one bf16 step).
+# codes and scales bit-exact; every other bar derived from the oracle's
+# quantities and the accumulation assumption, test_gpu_fp8.fp8_bounds).
 N_FP8 = 12
 CASES_FP8 = [_draw(100 + i) for i in range(N_FP8)]
 

@@ -50,7 +50,7 @@ STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", 
 
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_calibrate_clip",
-           "moe_w8a8_forward", "moe_w8a8_router_logits", "moe_w8a8_strerror")
+           "moe_w8a8_forward", "moe_w8a8_router_logits", "moe_w8a8_pack", "moe_w8a8_strerror")
 
 _lib = None
 
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_w8a8_router_logits.restype = ctypes.c_int
     lib.moe_w8a8_router_logits.argtypes = [D, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_size_t,
                                            _P]
+    lib.moe_w8a8_pack.restype = ctypes.c_int
+    lib.moe_w8a8_pack.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
     lib.moe_w8a8_strerror.restype = ctypes.c_char_p
     lib.moe_w8a8_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -146,6 +148,11 @@ def moe_w8a8_router_logits(d, x, T, w_router, logits, workspace, workspace_bytes
         int(workspace_bytes), _stream(stream)))
 
 
+def moe_w8a8_pack(count, N, K, src, dst, stream=None) -> int:
+    return int(load_library().moe_w8a8_pack(int(count), int(N), int(K), _ptr(src), _ptr(dst),
+                                             _stream(stream)))
+
+
 class MoEW8A8Error(RuntimeError):
     pass
 
@@ -164,6 +171,8 @@ class MoEW8A8:
         load_library()
         self.d = dims(hidden, ffn, num_experts, top_k)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         H, F, E = hidden, ffn, num_experts
         kw = dict(device=self.device)
         self.w_gate_up = torch.empty(E * 2 * F * H, dtype=torch.int8, **kw)
@@ -180,9 +189,27 @@ class MoEW8A8:
         self.act_clip = torch.zeros(1, dtype=torch.float32, **kw)
         self._ws = None
 
+    def _expect(self, t, name, dtype, shape):
+        """Raise MoEW8A8Error unless t is a contiguous tensor of this dtype and
+        shape on the layer's device (the C ABI reads raw pointers)."""
+        import torch
+        if not isinstance(t, torch.Tensor):
+            raise MoEW8A8Error("%s must be a torch tensor" % name)
+        if t.dtype != dtype:
+            raise MoEW8A8Error("%s must be %s, got %s" % (name, dtype, t.dtype))
+        if tuple(t.shape) != tuple(shape):
+            raise MoEW8A8Error("%s must have shape %s, got %s" % (name, tuple(shape),
+                                                                   tuple(t.shape)))
+        if not t.is_contiguous():
+            raise MoEW8A8Error("%s must be contiguous" % name)
+        if t.device != self.device:
+            raise MoEW8A8Error("%s must be on %s, got %s" % (name, self.device, t.device))
+
     def calibrate_clip(self, calib_x, percentile: float):
         """Static activation clip at the percentile of the calibration tokens'
         smoothed values (after calibrate); forward then uses it."""
+        import torch
+        self._expect(calib_x, "calib_x", torch.bfloat16, (calib_x.shape[0], self.d.hidden))
         _check(moe_w8a8_calibrate_clip(self.d, percentile, calib_x, calib_x.shape[0],
                                        self.inv_smooth, self.act_clip), "moe_w8a8_calibrate_clip")
         self.weights.act_clip = self.act_clip.data_ptr()
@@ -212,12 +239,35 @@ class MoEW8A8:
         if self.w_router is None:
             raise MoEW8A8Error("no router matrix (set_router)")
         T = x.shape[0]
+        self._expect(x, "x", torch.bfloat16, (T, self.d.hidden))
         if out is None:
             out = torch.empty(T, self.d.num_experts, dtype=torch.float32, device=self.device)
+        self._expect(out, "out", torch.float32, (T, self.d.num_experts))
         ws = self.workspace(T)
         _check(moe_w8a8_router_logits(self.d, x, T, self.w_router, out, ws, ws.numel()),
                "moe_w8a8_router_logits")
         return out
+
+    def load_quantized(self, q_gate_up, s_gate_up, q_down, s_down, smooth, inv_smooth):
+        """Load weights quantised elsewhere: row-major codes q_gate_up int8
+        [E][2F][H] (gate rows, then up rows) and q_down int8 [E][H][F] (INT8 or
+        e4m3 bytes, in the layer's format), packed on the device by
+        moe_w8a8_pack; scales s_gate_up fp32 [E][2F], s_down fp32 [E][H];
+        smooth and inv_smooth fp32 [H]. Every tensor on the layer's device."""
+        import torch
+        H, F, E = self.d.hidden, self.d.ffn, self.d.num_experts
+        self._expect(q_gate_up, "q_gate_up", torch.int8, (E, 2 * F, H))
+        self._expect(q_down, "q_down", torch.int8, (E, H, F))
+        self._expect(s_gate_up, "s_gate_up", torch.float32, (E, 2 * F))
+        self._expect(s_down, "s_down", torch.float32, (E, H))
+        self._expect(smooth, "smooth", torch.float32, (H,))
+        self._expect(inv_smooth, "inv_smooth", torch.float32, (H,))
+        _check(moe_w8a8_pack(E, 2 * F, H, q_gate_up, self.w_gate_up), "moe_w8a8_pack")
+        _check(moe_w8a8_pack(E, H, F, q_down, self.w_down), "moe_w8a8_pack")
+        self.s_gate_up.copy_(s_gate_up)
+        self.s_down.copy_(s_down)
+        self.smooth.copy_(smooth)
+        self.inv_smooth.copy_(inv_smooth)
 
     def workspace(self, T: int):
         import torch
@@ -230,6 +280,12 @@ class MoEW8A8:
 
     def calibrate(self, calib_x, w_gate, w_up, w_down, alpha: float):
         """calib_x: bf16 [Nc][H]; w_gate, w_up: f32 [E][F][H]; w_down: f32 [E][H][F]."""
+        import torch
+        H, F, E = self.d.hidden, self.d.ffn, self.d.num_experts
+        self._expect(calib_x, "calib_x", torch.bfloat16, (calib_x.shape[0], H))
+        self._expect(w_gate, "w_gate", torch.float32, (E, F, H))
+        self._expect(w_up, "w_up", torch.float32, (E, F, H))
+        self._expect(w_down, "w_down", torch.float32, (E, H, F))
         ws = self.workspace(0)
         _check(moe_w8a8_calibrate(self.d, alpha, calib_x, calib_x.shape[0], w_gate, w_up, w_down,
                                   self.weights, ws, ws.numel()), "moe_w8a8_calibrate")
@@ -240,9 +296,24 @@ class MoEW8A8:
         topk_w), or neither with a router matrix set (set_router)."""
         import torch
         T = x.shape[0]
-        if out is None:
-            out = torch.empty(T, self.d.hidden, dtype=torch.bfloat16, device=self.device)
+        out = self._check_forward_args(x, router_logits, topk_ids, topk_w, out)
         ws = self.workspace(T)
         _check(moe_w8a8_forward(self.d, self.weights, x, T, router_logits, topk_ids, topk_w,
                                 capacity_factor, out, ws, ws.numel(), debug), "moe_w8a8_forward")
+        return out
+
+    def _check_forward_args(self, x, router_logits, topk_ids, topk_w, out):
+        import torch
+        H, E, k = self.d.hidden, self.d.num_experts, self.d.top_k
+        T = x.shape[0]
+        self._expect(x, "x", torch.bfloat16, (T, H))
+        if router_logits is not None:
+            self._expect(router_logits, "router_logits", torch.float32, (T, E))
+        if topk_ids is not None:
+            self._expect(topk_ids, "topk_ids", torch.int32, (T, k))
+        if topk_w is not None:
+            self._expect(topk_w, "topk_w", torch.float32, (T, k))
+        if out is None:
+            out = torch.empty(T, H, dtype=torch.bfloat16, device=self.device)
+        self._expect(out, "out", torch.bfloat16, (T, H))
         return out

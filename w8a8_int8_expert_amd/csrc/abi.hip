@@ -96,6 +96,19 @@ extern "C" const char *moe_w8a8_strerror(int code) {
     if ((expr) != hipSuccess) return MOE_W8A8_ERR_HIP;   \
   } while (0)
 
+extern "C" int moe_w8a8_pack(int64_t count, int32_t N, int32_t K, const int8_t *src, int8_t *dst,
+                             void *stream) {
+  if (count <= 0 || N <= 0 || K <= 0 || !src || !dst) return MOE_W8A8_ERR_INVALID;
+  if ((uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0) return MOE_W8A8_ERR_INVALID;
+  if (N % 16 != 0 || K % 64 != 0) return MOE_W8A8_ERR_UNSUPPORTED;
+  if ((int64_t)N * K > ((int64_t)1 << 40) / count) return MOE_W8A8_ERR_INVALID;
+  const uintptr_t bytes = (uintptr_t)(count * (int64_t)N * K);
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_W8A8_ERR_INVALID;  // overlap
+  MOE_CHECK(launch_pack(src, dst, count, N, K, (hipStream_t)stream));
+  return MOE_W8A8_OK;
+}
+
 extern "C" int moe_w8a8_router_logits(const moe_w8a8_dims *d, const uint16_t *x, int64_t T,
                                       const uint16_t *w_router, float *logits, void *workspace,
                                       size_t workspace_bytes, void *stream) {
@@ -159,12 +172,12 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
   return MOE_W8A8_OK;
 }
 
-extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *wt,
-                                const uint16_t *x, int64_t T, const float *router_logits,
-                                const int32_t *topk_ids, const float *topk_w,
-                                float capacity_factor, uint16_t *out, void *workspace,
-                                size_t workspace_bytes, const moe_w8a8_debug *dbg,
-                                void *stream) {
+namespace {
+// The forward on a given workspace.
+int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint16_t *x,
+                 int64_t T, const float *router_logits, const int32_t *topk_ids,
+                 const float *topk_w, float capacity_factor, uint16_t *out, void *workspace,
+                 size_t workspace_bytes, const moe_w8a8_debug *dbg, void *stream) {
   if (!dims_valid(d) || !wt || T < 0) return MOE_W8A8_ERR_INVALID;
   if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
   const bool routed = router_logits != nullptr;
@@ -306,4 +319,15 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
       MOE_CHECK(launch_debug_row_of(row_of, ids, offsets, poffsets, A, dbg->row_of, st));
   }
   return MOE_W8A8_OK;
+}
+}  // namespace
+
+extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *wt,
+                                const uint16_t *x, int64_t T, const float *router_logits,
+                                const int32_t *topk_ids, const float *topk_w,
+                                float capacity_factor, uint16_t *out, void *workspace,
+                                size_t workspace_bytes, const moe_w8a8_debug *dbg,
+                                void *stream) {
+  return forward_impl(d, wt, x, T, router_logits, topk_ids, topk_w, capacity_factor, out,
+                      workspace, workspace_bytes, dbg, stream);
 }

@@ -218,6 +218,9 @@ hipError_t launch_debug_rows(const int32_t *offsets, const int32_t *poffsets, in
 hipError_t launch_debug_row_of(const int32_t *row_of_p, const int32_t *ids, const int32_t *offsets,
                                const int32_t *poffsets, int64_t A, int32_t *row_of,
                                hipStream_t st);
+// row-major [count][N][K] codes -> fragment-tiled (N % 16 == 0, K % 64 == 0)
+hipError_t launch_pack(const int8_t *src, int8_t *dst, int64_t count, int N, int K,
+                       hipStream_t st);
 // calibrate
 hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const float *w_gate,
                                const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,
