@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the W8A8 MoE expert layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 A step is one moe_w8a8_forward over one batch (route, permute, activation
 quant, GEMM1 + SwiGLU + requant, GEMM2, combine) with inputs and quantised
-weights resident in HBM. The headline line is the 27B-class decode step
-(32 tokens, hidden 4096, 64 experts, top-8, FFN 1536): tokens/s, plus the HBM
-roofline of its dominant kernel (GEMM1) timed live with HIP events on the
-layer's stream. The prefill of the same layer (16384 tokens) is measured too
-and reported against the dense INT8 MFMA peak. The CPU oracle is timed on the
-host on a bounded sample of the decode workload.
+weights resident in HBM. Each of the K timed steps is timed alone by a pair of
+HIP events, with a 512 MiB buffer overwritten between steps (outside the
+events), so that no weight is served from the 256 MB last-level cache; the
+headline is the median (the minimum and the back-to-back mean are reported
+too). The headline workload is the 27B-class decode step (32 tokens, hidden
+4096, 64 experts, top-8, FFN 1536); the prefill of the same layer (16384
+tokens), the tiny layer, one GPU's expert-parallel share and the outlier/skew
+stress layer are measured the same way and reported under "configs", each with
+its HBM and INT8 fractions of the algorithmic work, per-stage launch times
+(dispatch-stamped events, averaged over max(20, K) launches) and the CPU
+oracle's tokens/s on a bounded sample of the same workload.
 
 Prints ONE JSON line on stdout.
 """
@@ -33,8 +38,6 @@ METRIC = "W8A8 MoE layer tokens/s; HBM GB/s (decode) & INT8 MFMA % of peak (pref
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
-# Steps between two steps that carry stage events (decode; prefill steps all do).
-EVENT_STRIDE = 10
 COLD_FLUSH_BYTES = 512 << 20  # overwritten between cold-cache forwards
 STAGE_INDEX = {s: i for i, s in enumerate(
     ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", "combine", "router"))}
@@ -309,6 +312,9 @@ def launched_stages(wl):
 
 
 def layer_bytes(wl, counts, T):
+    """Algorithmic HBM bytes of one forward: the touched experts' INT8 weights
+    and scales, inv_s, x in and out (bf16), and the routing input (fp32 logits,
+    or ids and weights when pre-routed)."""
     touched = int((counts > 0).sum())
     b = touched * (3 * wl.H * wl.F + 4 * (2 * wl.F + wl.H)) + 4 * wl.H + 4 * T * wl.H
     b += 8 * T * wl.k if wl.pre_routed else 4 * T * wl.E
@@ -319,23 +325,52 @@ def gemm1_bytes(wl, touched):
     return touched * (2 * wl.F * wl.H + 4 * 2 * wl.F)
 
 
-def cpu_baseline(wl, layer, inputs, seconds):
+def host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+# Bounded samples of each workload for the CPU oracle: (tokens, minimum seconds).
+ORACLE_SAMPLE = {"tiny": (None, 2.0), "decode": (None, 8.0), "prefill": (512, 0.0),
+                 "ep_share": (1024, 0.0), "stress": (256, 0.0)}
+
+
+def cpu_baseline(wl, cal, inputs):
+    """The oracle (as it stands) on a bounded sample of the workload: the whole
+    sample repeated for at least the sample's minimum seconds (at least once)."""
     import oracle
-    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
+    n, min_s = ORACLE_SAMPLE[wl.name]
+    T = inputs.x.shape[0] if n is None else min(n, inputs.x.shape[0])
+    sl = slice(0, T)
+    kw = dict(logits=None if inputs.logits is None else inputs.logits[sl],
+              ids=None if inputs.ids is None else inputs.ids[sl],
+              w=None if inputs.w is None else inputs.w[sl])
+    x = inputs.x[sl]
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits, ids=inputs.ids, w=inputs.w,
-                       capacity_factor=wl.capacity_factor, want_acc1=False, want_h=False)
+        oracle.forward(x, cal, wl.k, capacity_factor=wl.capacity_factor, want_acc1=False,
+                       want_h=False, **kw)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds:
+        if el >= min_s:
             break
-    T = inputs.x.shape[0]
+    what = "all %d tokens" % T if n is None else "the first %d of %d tokens" % (T, wl.T)
+    if n is not None and wl.capacity_factor > 0:
+        what += " (capacity taken over the sample)"
     return {"value": round(T * reps / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%s workload (%d tokens, whole layer route..combine) x %d reps, %.1f s"
-                      % (wl.name, T, reps, el)}
+            "sample": "%s workload, %s, whole layer route..combine, x %d, %.1f s"
+                      % (wl.name, what, reps, el)}
 
 
 def copy_probe(torch, nbytes=1 << 30, reps=5):
@@ -348,26 +383,79 @@ def copy_probe(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def make_layer_for(name):
+    """(the layer's workload, the layer): prefill runs on the decode layer."""
+    import synth
+    lwl = synth.workload("decode") if name == "prefill" else synth.workload(name)
+    log("generating the %s layer (H=%d F=%d E=%d)" % (lwl.name, lwl.H, lwl.F, lwl.E))
+    return lwl, synth.make_layer(lwl)
+
+
+def measure(gl, wl, inputs, steps, warmup, hip):
+    """One workload: flushed per-forward times (median and minimum, the headline
+    form), the back-to-back mean, and every stage's average launch time over
+    max(20, steps) dispatch-stamped launches."""
+    t_mean = time_workload(gl, wl, inputs, steps, warmup, hip, [], 1)
+    cmed, cmin = time_cold(gl, wl, inputs, steps, warmup)
+    st = time_workload(gl, wl, inputs, max(20, steps), 2, hip, launched_stages(wl), 1)
+    return dict(ms_median=cmed, ms_min=cmin, ms_b2b=t_mean["seconds"] * 1e3 / steps,
+                stage_ms=st["stage_ms"], counts=t_mean["counts"], n_stage=max(20, steps))
+
+
+def config_block(wl, m_):
+    """Per-workload record: tokens/s at the flushed median, HBM and INT8
+    fractions of the algorithmic work, stage times and the dominant kernel."""
+    T = wl.T
+    lb, touched = layer_bytes(wl, m_["counts"], T)
+    A = int(m_["counts"].sum())
+    ops = 6 * A * wl.H * wl.F
+    sec = m_["ms_median"] * 1e-3
+    g1, g2 = m_["stage_ms"]["gemm1"] * 1e-3, m_["stage_ms"]["gemm2"] * 1e-3
+    stream = T * wl.k <= 32 * wl.E
+    blk = {
+        "workload": wl.description, "tokens": T, "kept_rows": A, "touched_experts": touched,
+        "gemm_path": "stream" if stream else "tiled",
+        "tokens_per_s": round(T / sec, 1),
+        "ms_per_step_median": round(m_["ms_median"], 5), "ms_per_step_min": round(m_["ms_min"], 5),
+        "ms_per_step_back_to_back": round(m_["ms_b2b"], 5),
+        "hbm": {"algorithmic_bytes": lb, "GBps": round(lb / sec / 1e9, 1),
+                "frac": round(lb / sec / 1e9 / HBM_PEAK_GBS, 4)},
+        "int8": {"algorithmic_ops": ops, "TOPs": round(ops / sec / 1e12, 1),
+                 "frac": round(ops / sec / 1e12 / INT8_PEAK_TOPS, 4)},
+        "gemm1": {"avg_launch_us": round(g1 * 1e6, 2),
+                  "hbm_frac": round(gemm1_bytes(wl, touched) / g1 / 1e9 / HBM_PEAK_GBS, 4),
+                  "int8_frac": round(4.0 * A * wl.H * wl.F / g1 / 1e12 / INT8_PEAK_TOPS, 4)},
+        "gemm2": {"avg_launch_us": round(g2 * 1e6, 2),
+                  "hbm_frac": round(touched * (wl.H * wl.F + 4 * wl.H) / g2 / 1e9 / HBM_PEAK_GBS,
+                                    4),
+                  "int8_frac": round(2.0 * A * wl.H * wl.F / g2 / 1e12 / INT8_PEAK_TOPS, 4)},
+        "stage_us": {k: round(v * 1e3, 2) for k, v in m_["stage_ms"].items()},
+        "stage_launches_timed": m_["n_stage"],
+        "bound": "hbm" if lb / (HBM_PEAK_GBS * 1e9) >= ops / (INT8_PEAK_TOPS * 1e12) else "mfma",
+        "roofline_us": {"hbm": round(lb / (HBM_PEAK_GBS * 1e9) * 1e6, 1),
+                        "int8": round(ops / (INT8_PEAK_TOPS * 1e12) * 1e6, 1)},
+    }
+    return blk
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "prefill", "ep_share", "stress"])
-    ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    choices=["tiny", "decode", "prefill", "ep_share", "stress"],
+                    help="time this workload only (it becomes the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--alpha-sweep", action="store_true",
                     help="only the quantisation-error sweep over alpha and the clip variants")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this layer has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -381,140 +469,115 @@ def main():
     hip = Hip()
     torch.cuda.set_device(0)
 
-    wl = synth.workload(args.workload)
-    layer_wl = synth.workload("decode") if wl.name == "prefill" else wl
-    log("generating %s layer (H=%d F=%d E=%d)" % (layer_wl.name, wl.H, wl.F, wl.E))
-    layer = synth.make_layer(layer_wl)
-    gl = GpuLayer(layer_wl, layer, torch)
     if args.alpha_sweep:
+        lwl, layer = make_layer_for("decode")
+        gl = GpuLayer(lwl, layer, torch)
         log("alpha sweep")
         print(json.dumps({"alpha_sweep": alpha_sweep(
             gl, layer, 128, [0.5, 0.55, 0.6, 0.65, 0.7], 99.9)}), flush=True)
         return
-    inputs = synth.make_inputs(wl, layer)
-    gl.wl = wl
-    log("timing %s: %d warmup + %d steps" % (wl.name, args.warmup, args.steps))
-    r = time_workload(gl, wl, inputs, args.steps, args.warmup, hip, launched_stages(wl),
-                      EVENT_STRIDE if wl.name == "decode" else 1)
-    T = wl.T
-    sec = r["seconds"]
-    ms_step = sec * 1e3 / args.steps
-    tok_s = T * args.steps / sec
-    lb, touched = layer_bytes(wl, r["counts"], T)
-    A = int(r["counts"].sum())
-    path = "stream" if T * wl.k <= 32 * wl.E else "tiled"
-    gemm1_ms = r["stage_ms"]["gemm1"]
-    if path == "stream":
-        g1b = gemm1_bytes(wl, touched)
-        achieved = g1b / (gemm1_ms * 1e-3) / 1e9
-        traffic = stored_traffic("gemm1_stream", wl.name)
+
+    head = args.workload or "decode"
+    order = [head] if args.workload else ["decode", "prefill", "tiny", "ep_share", "stress"]
+    configs, extra = {}, {}
+    cpu = {}
+    gl = layer = lwl = None
+    for name in order:
+        wl = synth.workload(name)
+        want_lwl = synth.workload("decode") if name == "prefill" else wl
+        if lwl is None or lwl.name != want_lwl.name:
+            gl = layer = None
+            torch.cuda.empty_cache()
+            lwl, layer = make_layer_for(name)
+            gl = GpuLayer(lwl, layer, torch)
+            cal = None
+        inputs = synth.make_inputs(wl, layer)
+        gl.wl = wl
+        log("timing %s: %d warmup + %d flushed steps, %d stamped launches"
+            % (name, args.warmup, args.steps, max(20, args.steps)))
+        meas = measure(gl, wl, inputs, args.steps, args.warmup, hip)
+        configs[name] = config_block(wl, meas)
+        if name == "decode" and not args.no_fp8:
+            log("FP8 (e4m3) expert path, decode")
+            gf = GpuLayer(lwl, layer, torch, fp8=True)
+            gf.wl = wl
+            fm = measure(gf, wl, inputs, args.steps, args.warmup, hip)
+            pwl = synth.workload("prefill")
+            pin = synth.make_inputs(pwl, layer)
+            gf.wl = pwl
+            log("FP8 prefill")
+            pm = measure(gf, pwl, pin, max(5, args.steps // 4), 2, hip)
+            fd, fpf = config_block(wl, fm), config_block(pwl, pm)
+            extra["fp8"] = {
+                "decode": {"tokens_per_s": fd["tokens_per_s"],
+                           "ms_per_step_median": fd["ms_per_step_median"],
+                           "gemm1_hbm_frac": fd["gemm1"]["hbm_frac"], "layer_hbm_frac":
+                           fd["hbm"]["frac"], "stage_us": fd["stage_us"]},
+                "prefill": {"tokens_per_s": fpf["tokens_per_s"],
+                            "ms_per_step_median": fpf["ms_per_step_median"],
+                            "gemm1_frac_fp8_peak": fpf["gemm1"]["int8_frac"],
+                            "layer_frac_fp8_peak": fpf["int8"]["frac"],
+                            "stage_us": fpf["stage_us"]}}
+            del gf
+            torch.cuda.empty_cache()
+        if name == "decode" and not args.no_router:
+            log("router-projection mode")
+            w_router = synth.make_router(lwl)
+            rp = {"decode": time_router(gl, wl, inputs, w_router, args.steps, args.warmup)}
+            pwl = synth.workload("prefill")
+            rp["prefill"] = time_router(gl, pwl, synth.make_inputs(pwl, layer), w_router,
+                                        max(5, args.steps // 4), 2)
+            extra["router_projection"] = rp
+        if not args.no_cpu_baseline:
+            import oracle
+            if cal is None:
+                cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down,
+                                       lwl.alpha)
+            log("timing the CPU oracle on a sample of %s" % name)
+            cpu[name] = cpu_baseline(wl, cal, inputs)
+            configs[name]["oracle_tokens_per_s"] = cpu[name]["value"]
+            configs[name]["oracle_sample"] = cpu[name]["sample"]
+
+    h = configs[head]
+    wl = synth.workload(head)
+    if h["gemm_path"] == "stream":
+        g1b = gemm1_bytes(wl, h["touched_experts"])
+        g1s = h["gemm1"]["avg_launch_us"] * 1e-6
+        achieved = g1b / g1s / 1e9
+        traffic = stored_traffic("gemm1_stream", head)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
                 "kernel": "gemm_stream_kernel<gate/up> (GEMM1)",
-                "algorithmic_bytes_per_launch": g1b, "avg_launch_us": round(gemm1_ms * 1e3, 2)}
+                "algorithmic_bytes_per_launch": g1b, "avg_launch_us": h["gemm1"]["avg_launch_us"],
+                "launches_timed": h["stage_launches_timed"]}
     else:
-        ops = 4 * A * wl.H * wl.F
-        achieved = ops / (gemm1_ms * 1e-3) / 1e12
-        traffic = stored_traffic("gemm1_tiled", wl.name)
+        ops = 4 * h["kept_rows"] * wl.H * wl.F
+        g1s = h["gemm1"]["avg_launch_us"] * 1e-6
+        achieved = ops / g1s / 1e12
+        traffic = stored_traffic("gemm1_tiled", head)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
                 "kernel": "gemm_tiled_kernel<gate/up> (GEMM1)",
-                "algorithmic_ops_per_launch": ops, "avg_launch_us": round(gemm1_ms * 1e3, 2)}
+                "algorithmic_ops_per_launch": ops, "avg_launch_us": h["gemm1"]["avg_launch_us"],
+                "launches_timed": h["stage_launches_timed"]}
     res = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step_median"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": wl.description, "tokens": T, "hidden": wl.H, "experts": wl.E,
-                   "top_k": wl.k, "ffn": wl.F, "gemm_path": path},
+        "config": {"workload": wl.description, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                   "top_k": wl.k, "ffn": wl.F, "gemm_path": h["gemm_path"],
+                   "timing": "median of per-forward HIP-event times, 512 MiB overwritten "
+                             "between forwards"},
         "roofline": roof,
-        "layer_hbm": {"algorithmic_bytes": lb, "touched_experts": touched,
-                      "achieved_GBps": round(lb / sec * args.steps / 1e9, 1),
-                      "frac": round(lb / sec * args.steps / 1e9 / HBM_PEAK_GBS, 4)},
-        "layer_int8": {"algorithmic_ops": 6 * A * wl.H * wl.F,
-                       "achieved_TOPs": round(6.0 * A * wl.H * wl.F / sec * args.steps / 1e12, 1),
-                       "frac": round(6.0 * A * wl.H * wl.F / sec * args.steps / 1e12 /
-                                     INT8_PEAK_TOPS, 4)},
-        "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage_ms"].items()},
+        "configs": configs,
     }
-    log("timing %d forwards with the last-level cache flushed before each" % args.steps)
-    cmed, cmin = time_cold(gl, wl, inputs, args.steps, args.warmup)
-    res["cold_cache"] = {"flush_bytes": COLD_FLUSH_BYTES, "ms_per_step_median": round(cmed, 5),
-                         "ms_per_step_min": round(cmin, 5),
-                         "tokens_per_s_median": round(T / (cmed * 1e-3), 1)}
-    if wl.name == "decode" and not args.no_prefill:
-        pwl = synth.workload("prefill")
-        log("timing prefill: 3 warmup + %d steps" % args.prefill_steps)
-        pin = synth.make_inputs(pwl, layer)
-        gl.wl = pwl
-        pr = time_workload(gl, pwl, pin, args.prefill_steps, 3, hip, launched_stages(pwl), 1)
-        pA = int(pr["counts"].sum())
-        psec = pr["seconds"]
-        g1ops = 4 * pA * pwl.H * pwl.F
-        g2ops = 2 * pA * pwl.H * pwl.F
-        g1 = g1ops / (pr["stage_ms"]["gemm1"] * 1e-3) / 1e12
-        g2 = g2ops / (pr["stage_ms"]["gemm2"] * 1e-3) / 1e12
-        layer_tops = (g1ops + g2ops) * args.prefill_steps / psec / 1e12
-        res["prefill"] = {
-            "workload": pwl.description, "tokens_per_s": round(pwl.T * args.prefill_steps / psec, 1),
-            "ms_per_step": round(psec * 1e3 / args.prefill_steps, 4),
-            "gemm1": {"achieved_TOPs": round(g1, 1), "frac_int8_peak": round(g1 / INT8_PEAK_TOPS, 4),
-                      "avg_launch_us": round(pr["stage_ms"]["gemm1"] * 1e3, 1)},
-            "gemm2": {"achieved_TOPs": round(g2, 1), "frac_int8_peak": round(g2 / INT8_PEAK_TOPS, 4),
-                      "avg_launch_us": round(pr["stage_ms"]["gemm2"] * 1e3, 1)},
-            "layer_frac_int8_peak": round(layer_tops / INT8_PEAK_TOPS, 4),
-            "stage_us": {k: round(v * 1e3, 1) for k, v in pr["stage_ms"].items()},
-        }
-        del pr
-    if wl.name == "decode" and not args.no_fp8:
-        log("FP8 (e4m3) expert path: calibrating and timing decode")
-        gf = GpuLayer(layer_wl, layer, torch, fp8=True)
-        fr = time_workload(gf, wl, inputs, args.steps, args.warmup, hip, launched_stages(wl),
-                           EVENT_STRIDE)
-        fsec = fr["seconds"]
-        g1b = gemm1_bytes(wl, touched)
-        fp8 = {"decode": {
-            "tokens_per_s": round(T * args.steps / fsec, 1),
-            "ms_per_step": round(fsec * 1e3 / args.steps, 5),
-            "gemm1_hbm_frac": round(g1b / (fr["stage_ms"]["gemm1"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "layer_hbm_frac": round(lb / fsec * args.steps / 1e9 / HBM_PEAK_GBS, 4),
-            "stage_us": {k: round(v * 1e3, 2) for k, v in fr["stage_ms"].items()}}}
-        if not args.no_prefill:
-            log("FP8 prefill: 3 warmup + %d steps" % args.prefill_steps)
-            pwl = synth.workload("prefill")
-            gf.wl = pwl
-            pin = synth.make_inputs(pwl, layer)
-            pr = time_workload(gf, pwl, pin, args.prefill_steps, 3, hip, launched_stages(pwl), 1)
-            pA = int(pr["counts"].sum())
-            ops = 6.0 * pA * pwl.H * pwl.F
-            fp8["prefill"] = {
-                "tokens_per_s": round(pwl.T * args.prefill_steps / pr["seconds"], 1),
-                "ms_per_step": round(pr["seconds"] * 1e3 / args.prefill_steps, 4),
-                "layer_frac_fp8_peak": round(ops * args.prefill_steps / pr["seconds"] / 1e12 /
-                                             FP8_PEAK_TFLOPS, 4),
-                "gemm1_frac_fp8_peak": round(4.0 * pA * pwl.H * pwl.F /
-                                             (pr["stage_ms"]["gemm1"] * 1e-3) / 1e12 /
-                                             FP8_PEAK_TFLOPS, 4),
-                "stage_us": {k: round(v * 1e3, 1) for k, v in pr["stage_ms"].items()}}
-            del pr
-        res["fp8"] = fp8
-        del gf, fr
-        torch.cuda.empty_cache()
-    if wl.name == "decode" and not args.no_router:
-        log("timing router-projection mode")
-        w_router = synth.make_router(layer_wl)
-        rp = {"decode": time_router(gl, wl, inputs, w_router, args.steps, args.warmup)}
-        if not args.no_prefill:
-            pwl = synth.workload("prefill")
-            rp["prefill"] = time_router(gl, pwl, synth.make_inputs(pwl, layer), w_router,
-                                        args.prefill_steps, 3)
-        res["router_projection"] = rp
+    res.update(extra)
     res["cpu_baseline"] = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle for %.0f s" % args.cpu_seconds)
-        res["cpu_baseline"] = cpu_baseline(wl, layer, inputs, args.cpu_seconds)
+    if head in cpu:
+        res["cpu_baseline"] = dict(cpu[head], **host_info())
     print(json.dumps(res), flush=True)
 
 
