@@ -59,6 +59,7 @@ extern "C" {
 #define MOE_W8A8_ERR_UNSUPPORTED (-2) /* shape outside the supported set (below)     */
 #define MOE_W8A8_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than required     */
 #define MOE_W8A8_ERR_HIP (-4)         /* a HIP launch or copy reported an error      */
+#define MOE_W8A8_ERR_SCRATCH (-5)     /* batch too large for the static scratch      */
 
 /* Layer dimensions. Supported set: hidden H a multiple of 256 in [256, 65536];
  * ffn F a multiple of 128 in [128, 65536]; 1 <= num_experts E <= 1024;
@@ -262,6 +263,29 @@ int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
                      uint16_t *out,
                      void *workspace, size_t workspace_bytes,
                      const moe_w8a8_debug *debug, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as moe_w8a8_forward, same arguments and results, but its workspace
+ * is a static device array of MOE_W8A8_SCRATCH_BYTES inside the library (one
+ * per GPU, held from the first call on that GPU until the process ends)
+ * instead of a caller buffer. Nothing is allocated or freed by the call.
+ * Limit: moe_w8a8_workspace_size(dims, T) <= MOE_W8A8_SCRATCH_BYTES (64 MiB:
+ * e.g. up to ~200 tokens of a hidden-4096, 64-expert, top-8, FFN-1536 layer);
+ * a larger batch returns MOE_W8A8_ERR_SCRATCH with nothing enqueued.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on a
+ * GPU (concurrent streams, or host threads) race and must be serialised by
+ * the caller; consecutive calls on one stream are safe (each call's kernels
+ * ignore what the array held before). Errors: as moe_w8a8_forward, with
+ * MOE_W8A8_ERR_SCRATCH in place of MOE_W8A8_ERR_WORKSPACE. */
+#define MOE_W8A8_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_w8a8_forward_noalloc(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
+                             const uint16_t *x, int64_t T,
+                             const float *router_logits,
+                             const int32_t *topk_ids, const float *topk_w,
+                             float capacity_factor,
+                             uint16_t *out,
+                             const moe_w8a8_debug *debug, void *stream);
 
 /* Router projection ("超大规模模型推理的Day0适配实践" §四: the gate belongs to
  * the fused MoE operator and the top-k it feeds must be exact; "MiniMax-M3

@@ -22,6 +22,8 @@ MOE_W8A8_ERR_INVALID = -1
 MOE_W8A8_ERR_UNSUPPORTED = -2
 MOE_W8A8_ERR_WORKSPACE = -3
 MOE_W8A8_ERR_HIP = -4
+MOE_W8A8_ERR_SCRATCH = -5
+MOE_W8A8_SCRATCH_BYTES = 64 << 20
 MOE_W8A8_FORMAT_INT8 = 0
 MOE_W8A8_FORMAT_FP8 = 1
 
@@ -50,7 +52,8 @@ STAGES = ("route", "scan", "scatter", "act_quant", "gemm1", "requant", "gemm2", 
 
 
 EXPORTS = ("moe_w8a8_workspace_size", "moe_w8a8_calibrate", "moe_w8a8_calibrate_clip",
-           "moe_w8a8_forward", "moe_w8a8_router_logits", "moe_w8a8_pack", "moe_w8a8_strerror")
+           "moe_w8a8_forward", "moe_w8a8_forward_noalloc", "moe_w8a8_router_logits",
+           "moe_w8a8_pack", "moe_w8a8_strerror")
 
 _lib = None
 
@@ -74,6 +77,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_w8a8_forward.restype = ctypes.c_int
     lib.moe_w8a8_forward.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P, ctypes.c_float, _P,
                                      _P, ctypes.c_size_t, G, _P]
+    lib.moe_w8a8_forward_noalloc.restype = ctypes.c_int
+    lib.moe_w8a8_forward_noalloc.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P,
+                                             ctypes.c_float, _P, G, _P]
     lib.moe_w8a8_calibrate_clip.restype = ctypes.c_int
     lib.moe_w8a8_calibrate_clip.argtypes = [D, ctypes.c_float, _P, ctypes.c_int64, _P, _P, _P]
     lib.moe_w8a8_router_logits.restype = ctypes.c_int
@@ -132,6 +138,15 @@ def moe_w8a8_forward(d, weights: moe_w8a8_weights, x, T, router_logits, topk_ids
         _ptr(topk_ids), _ptr(topk_w), float(capacity_factor), _ptr(out), _ptr(workspace),
         int(workspace_bytes), ctypes.byref(debug) if debug is not None else None,
         _stream(stream)))
+
+
+def moe_w8a8_forward_noalloc(d, weights: moe_w8a8_weights, x, T, router_logits, topk_ids, topk_w,
+                             capacity_factor, out, debug: Optional[moe_w8a8_debug] = None,
+                             stream=None) -> int:
+    return int(load_library().moe_w8a8_forward_noalloc(
+        ctypes.byref(d), ctypes.byref(weights), _ptr(x), int(T), _ptr(router_logits),
+        _ptr(topk_ids), _ptr(topk_w), float(capacity_factor), _ptr(out),
+        ctypes.byref(debug) if debug is not None else None, _stream(stream)))
 
 
 def moe_w8a8_calibrate_clip(d, percentile, calib_x, n_calib, inv_smooth, act_clip,
@@ -300,6 +315,19 @@ class MoEW8A8:
         ws = self.workspace(T)
         _check(moe_w8a8_forward(self.d, self.weights, x, T, router_logits, topk_ids, topk_w,
                                 capacity_factor, out, ws, ws.numel(), debug), "moe_w8a8_forward")
+        return out
+
+    def forward_noalloc(self, x, out, router_logits=None, topk_ids=None, topk_w=None,
+                        capacity_factor: float = 0.0, debug: Optional[moe_w8a8_debug] = None):
+        """forward into a caller-given out, with the library's static scratch
+        as workspace (moe_w8a8_forward_noalloc): nothing is allocated."""
+        T = x.shape[0]
+        if out is None:
+            raise MoEW8A8Error("forward_noalloc needs a caller-given out tensor")
+        out = self._check_forward_args(x, router_logits, topk_ids, topk_w, out)
+        _check(moe_w8a8_forward_noalloc(self.d, self.weights, x, T, router_logits, topk_ids,
+                                        topk_w, capacity_factor, out, debug),
+               "moe_w8a8_forward_noalloc")
         return out
 
     def _check_forward_args(self, x, router_logits, topk_ids, topk_w, out):

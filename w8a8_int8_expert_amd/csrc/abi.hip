@@ -3,6 +3,8 @@
 // the launch sequence of one forward / calibrate call on the caller's stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 #include "moe_w8a8.h"
 
@@ -87,6 +89,8 @@ extern "C" const char *moe_w8a8_strerror(int code) {
     case MOE_W8A8_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_W8A8_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_W8A8_ERR_HIP: return "HIP runtime error";
+    case MOE_W8A8_ERR_SCRATCH:
+      return "batch too large for the static scratch of moe_w8a8_forward_noalloc";
     default: return "unknown error code";
   }
 }
@@ -173,7 +177,7 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
 }
 
 namespace {
-// The forward on a given workspace.
+// The forward on a given workspace (the caller's, or the static scratch).
 int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint16_t *x,
                  int64_t T, const float *router_logits, const int32_t *topk_ids,
                  const float *topk_w, float capacity_factor, uint16_t *out, void *workspace,
@@ -330,4 +334,50 @@ extern "C" int moe_w8a8_forward(const moe_w8a8_dims *d, const moe_w8a8_weights *
                                 void *stream) {
   return forward_impl(d, wt, x, T, router_logits, topk_ids, topk_w, capacity_factor, out,
                       workspace, workspace_bytes, dbg, stream);
+}
+
+// ------------------------------------------------- forward without allocation
+// The workspace of moe_w8a8_forward_noalloc: a file-scope device array, one
+// copy per GPU, alive until the process ends. In host code `scratch` names a
+// host-side stand-in, not the device memory: its device address is taken
+// once per device with hipGetSymbolAddress and only that address is used.
+namespace {
+static __device__ __align__(256) char scratch[MOE_W8A8_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (resolved on the first call on it).
+hipError_t scratch_on_current_device(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int moe_w8a8_forward_noalloc(const moe_w8a8_dims *d, const moe_w8a8_weights *wt,
+                                        const uint16_t *x, int64_t T, const float *router_logits,
+                                        const int32_t *topk_ids, const float *topk_w,
+                                        float capacity_factor, uint16_t *out,
+                                        const moe_w8a8_debug *dbg, void *stream) {
+  if (!dims_valid(d) || !wt || T < 0) return MOE_W8A8_ERR_INVALID;
+  if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
+  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
+  if (moe_w8a8_workspace_size(d, T) > MOE_W8A8_SCRATCH_BYTES) return MOE_W8A8_ERR_SCRATCH;
+  void *ws = nullptr;
+  MOE_CHECK(scratch_on_current_device(&ws));
+  return forward_impl(d, wt, x, T, router_logits, topk_ids, topk_w, capacity_factor, out, ws,
+                      MOE_W8A8_SCRATCH_BYTES, dbg, stream);
 }
