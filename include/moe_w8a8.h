@@ -24,7 +24,9 @@
  *               §1.2 and §4.3: INT8 GEMM with integer accumulation; stay in
  *               the INT8 domain between consecutive matmuls);
  *   5. GEMM2    per expert, INT8 down projection, dequantised per row and
- *               per output channel to fp32;
+ *               per output channel to fp32 (for large batches held until the
+ *               combine as int16 codes with one fp32 scale per 16 outputs,
+ *               error at most ~2^-16 of the group's largest value);
  *   6. combine  out[t] = sum over kept slots of w[t][j] * y[row], summed in
  *               fp32 and rounded to bfloat16 (Day0 page §四: un-sort and
  *               weighted sum).
@@ -145,7 +147,8 @@ typedef struct {
  *                                 bits of the fp32 sums in FP8 format)
  *   h fp32 [A][F]                 SwiGLU output before requantisation
  *   qh int8 [A][F], sh fp32 [A]   requantised hidden rows and their scales
- *   y fp32 [A][H]                 dequantised down-projection rows */
+ *   y fp32 [A][H]                 dequantised down-projection rows, as the
+ *                                 combine reads them */
 typedef struct {
   int32_t *topk_ids;
   float *topk_w;
@@ -271,7 +274,7 @@ int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,
  * per GPU, held from the first call on that GPU until the process ends)
  * instead of a caller buffer. Nothing is allocated or freed by the call.
  * Limit: moe_w8a8_workspace_size(dims, T) <= MOE_W8A8_SCRATCH_BYTES (64 MiB:
- * e.g. up to ~200 tokens of a hidden-4096, 64-expert, top-8, FFN-1536 layer);
+ * e.g. up to ~220 tokens of a hidden-4096, 64-expert, top-8, FFN-1536 layer);
  * a larger batch returns MOE_W8A8_ERR_SCRATCH with nothing enqueued.
  * Every call on one GPU uses that GPU's one array, so calls that overlap on a
  * GPU (concurrent streams, or host threads) race and must be serialised by

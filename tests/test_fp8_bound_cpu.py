@@ -1,11 +1,13 @@
 """CPU check of the FP8 parity bounds (fp8_bounds in test_gpu_fp8): a pipeline
-whose GEMM sums carry errors anywhere inside the accumulation assumption, and
+whose GEMM sums carry errors anywhere inside the accumulation bound, and
 whose other steps round in fp32 as the kernels do, stays inside every bound
 derived from the oracle's quantities. Each GEMM sum is moved by a seeded
 uniform draw over the whole allowance (far more than the hardware's measured
 error), the SwiGLU and the dequantisations run in fp32, the requantisation is
-the oracle's own quantiser on the perturbed rows, and the combine sums in fp32
-in slot order before its rounding to bf16."""
+the oracle's own quantiser on the perturbed rows, y is rounded to int16 codes
+with one scale per 16 columns as the tiled path holds it (or kept in fp32 as
+the streaming path does), and the combine sums in fp32 in slot order before
+its rounding to bf16."""
 import numpy as np
 import pytest
 
@@ -13,7 +15,18 @@ import oracle
 import synth
 from moe_testlib import bf16_step
 from synth import bf16_bits_to_f32, f32_to_bf16_bits
-from test_gpu_fp8 import ACC_BLK, LUT, block_bound, fp8_bounds
+from test_gpu_fp8 import LUT, acc_bound, fp8_bounds
+
+def _y16(y):
+    """y rows rounded as the tiled path holds them (signed normalised int16
+    codes of v / group max, one scale per 16 columns)."""
+    g = np.abs(y).reshape(y.shape[0], -1, 16).max(-1, keepdims=True)
+    inv = np.where(g > 1e-30, np.float32(1) / np.maximum(g, np.float32(1e-30)), 0)
+    q = np.clip(np.rint(y.reshape(g.shape[0], -1, 16) * inv.astype(np.float32) * 32767),
+                -32767, 32767)
+    sc = np.where(g > 1e-30, g / np.float32(32767), 0).astype(np.float32)
+    return (q.astype(np.float32) * sc).astype(np.float32).reshape(y.shape)
+
 
 CASES = {
     "tiny": dict(T=40),
@@ -23,8 +36,8 @@ CASES = {
 
 
 @pytest.mark.parametrize("case", sorted(CASES))
-@pytest.mark.parametrize("seed", [0, 1])
-def test_fp8_bounds_hold_for_perturbed_pipeline(case, seed):
+@pytest.mark.parametrize("seed,y16", [(0, True), (1, False)])
+def test_fp8_bounds_hold_for_perturbed_pipeline(case, seed, y16):
     wl = synth.workload("tiny", **CASES[case])
     layer = synth.make_layer(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
@@ -32,7 +45,7 @@ def test_fp8_bounds_hold_for_perturbed_pipeline(case, seed):
     inputs = synth.make_inputs(wl, layer)
     o = oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits,
                        capacity_factor=wl.capacity_factor, fmt=oracle.FMT_FP8)
-    b = fp8_bounds(o, cal, wl)
+    b = fp8_bounds(o, cal, wl, y16)
     rng = np.random.default_rng(seed)
     F, H, k = wl.F, wl.H, wl.k
     acc = (o["acc1"] + rng.uniform(-1, 1, o["acc1"].shape) * b["acc_tol"]).astype(np.float32)
@@ -56,9 +69,12 @@ def test_fp8_bounds_hold_for_perturbed_pipeline(case, seed):
         rows = np.nonzero(e_id == e)[0]
         wd = LUT[cal["q_d"][e].view(np.uint8)]
         s2 = qv[rows] @ wd.T
-        s2 += rng.uniform(-1, 1, s2.shape) * ACC_BLK * block_bound(qv[rows], wd)
+        s2 += rng.uniform(-1, 1, s2.shape) * acc_bound(qv[rows], wd)
         y[rows] = (s2.astype(np.float32) * sh[rows, None]).astype(np.float32) * \
             cal["sw_d"][e][None, :]
+    # y rows as the tiled path holds them: int16 codes, one scale per 16 columns
+    if y16:
+        y = _y16(y)
     out = np.zeros((wl.T, H), np.float32)
     for j in range(k):
         r = o["row_of"][:, j]

@@ -53,6 +53,8 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   L.amax = take(sizeof(uint32_t) * (size_t)L.P);
   L.qh = take(P16 * F);
   L.sh = take(sizeof(float) * (size_t)L.P);
+  // y rows: fp32 (streaming path) or int16 codes + scales (tiled path) in
+  // the same region, sized for the larger
   L.y = take(sizeof(float) * (size_t)L.P * H);
   L.rpart = take(sizeof(float) * (size_t)router_parts(H) * (size_t)T * (size_t)E);
   L.total = o;
@@ -236,7 +238,13 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
   uint32_t *amax = (uint32_t *)(ws + L.amax);
   int8_t *qh = (int8_t *)(ws + L.qh);
   float *sh = (float *)(ws + L.sh);
-  float *y = (float *)(ws + L.y);
+  // y rows: the tiled path codes them to int16 with a scale per 16 columns
+  // (the codes first, then the scales, inside the fp32-sized region)
+  YRows y{(float *)(ws + L.y), nullptr, nullptr};
+  if (path == 2) {
+    const size_t codes = (size_t)L.P * H * sizeof(int16_t);
+    y = YRows{nullptr, (int16_t *)(ws + L.y), (float *)(ws + L.y + (codes + 255) / 256 * 256)};
+  }
   int32_t *acc1_dbg = dbg ? dbg->acc1 : nullptr;
   hipStream_t st = (hipStream_t)stream;
 
@@ -292,7 +300,7 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
   }
   MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, fp8, st, tm(kReq)));
   if (path == 1)
-    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, poffsets, wt->w_down, wt->s_down, H, F, E, y,
+    MOE_CHECK(launch_gemm2_stream(qh, sh, counts, poffsets, wt->w_down, wt->s_down, H, F, E, y.f,
                                   fp8, st, tm(kG2)));
   else
     MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, poffsets, mtile_off, A, wt->w_down, wt->s_down,

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void debug_rows_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ poffsets, int E,
     const int32_t *__restrict__ sorted_p, const float *__restrict__ h_p,
     const int8_t *__restrict__ qh_t, const float *__restrict__ sh_p,
-    const float *__restrict__ y_p, int F, int H, int32_t *__restrict__ sorted,
+    const YRows y_p, int F, int H, int32_t *__restrict__ sorted,
     float *__restrict__ h, int8_t *__restrict__ qh, float *__restrict__ sh,
     float *__restrict__ y) {
   const int i = blockIdx.x;
@@ -40,8 +40,12 @@ __global__ __launch_bounds__(256) void debug_rows_kernel(
       qh[(size_t)i * F + j] = qh_t[at];
     }
   }
+  // y as the combine reads it (int16 rows: code times its group's scale)
   if (y)
-    for (int j = tid; j < H; j += 256) y[(size_t)i * H + j] = y_p[p * H + j];
+    for (int j = tid; j < H; j += 256)
+      y[(size_t)i * H + j] =
+          y_p.f ? y_p.f[p * H + j]
+                : (float)y_p.q[p * H + j] * y_p.s[p * (size_t)(H / kYGroup) + j / kYGroup];
 }
 
 // row_of in dense rows: padded row p of assignment a (expert ids[a]) maps
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(256) void debug_row_of_kernel(const int32_t *__rest
 
 hipError_t launch_debug_rows(const int32_t *offsets, const int32_t *poffsets, int E, int64_t A,
                              const int32_t *sorted_p, const float *h_p, const int8_t *qh_t,
-                             const float *sh_p, const float *y_p, int F, int H, int32_t *sorted,
+                             const float *sh_p, YRows y_p, int F, int H, int32_t *sorted,
                              float *h, int8_t *qh, float *sh, float *y, hipStream_t st) {
   return launch_kernel(debug_rows_kernel, dim3((unsigned)A), dim3(256), st, Timing{}, offsets,
                        poffsets, E, sorted_p, h_p, qh_t, sh_p, y_p, F, H, sorted, h, qh, sh, y);

@@ -97,7 +97,8 @@ struct TiledArgs {
   const int8_t *w;          // fragment-tiled weights
   const float *wscale;
   int K, F, H;
-  float *out;               // GEMM1: h [rows][F]; GEMM2: y [rows][H]
+  float *out;               // GEMM1: h [rows][F]
+  YRows y;                  // GEMM2: y rows (int16 codes, a scale per 16 columns)
   uint32_t *amax;           // GEMM1: row max |h| (float bits)
   int32_t *acc1_dbg;        // GEMM1: optional INT32 accumulators, dense rows [A][2F]
 };
@@ -502,17 +503,31 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
             slice[r * kEpiPitch + 32 * c + (lane & 31)] =
                 (float)acc[i][3 * hc + c][v] * shv * sd[3 * hc + c];
         }
-        // 32 rows x 96 columns: 24 lanes per row, 4 floats each.
+        // 32 rows x 96 columns: 12 lanes per row, 8 floats each, so that
+        // every lane stores 16 bytes of codes; the two lanes 2g, 2g+1 of a
+        // row hold one 16-column group (groups start on multiples of 16
+        // columns), which takes one scale.
         const int nc = n0 + 96 * hc;
+        const int hg = H / kYGroup;
 #pragma unroll
-        for (int j = 0; j < 12; ++j) {
+        for (int j = 0; j < 6; ++j) {
           const int c = j * 64 + lane;
-          const int r = c / 24, c4 = (c % 24) * 4;
+          const int r = c / 12, c8 = (c % 12) * 8;
           const int m = mw + 32 * i + r;
-          if (m0 + m < R && nc + c4 < H) {
-            const v4f yv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c4);
-            __builtin_nontemporal_store(
-                yv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * H + nc + c4));
+          const v4f ya = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c8);
+          const v4f yb = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c8 + 4);
+          float gm = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            gm = __builtin_fmaxf(gm, __builtin_fmaxf(__builtin_fabsf(ya[q]), __builtin_fabsf(yb[q])));
+          gm = __builtin_fmaxf(gm, __shfl_xor(gm, 1, 64));
+          if (m0 + m < R && nc + c8 < H) {
+            const size_t row = (size_t)(row0 + m0 + m);
+            const float inv = y16_inv(gm);
+            const v4i q = {y16x2(ya[0], ya[1], inv), y16x2(ya[2], ya[3], inv),
+                           y16x2(yb[0], yb[1], inv), y16x2(yb[2], yb[3], inv)};
+            __builtin_nontemporal_store(q, reinterpret_cast<v4i *>(a.y.q + row * H + nc + c8));
+            if ((lane & 1) == 0) a.y.s[row * hg + (nc + c8) / kYGroup] = y16_scale(gm);
           }
         }
       }
@@ -550,13 +565,13 @@ hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
                               const int8_t *w_d, const float *s_d, int H, int F, int E,
-                              float *y, bool fp8, hipStream_t st, Timing tm) {
+                              YRows y, bool fp8, hipStream_t st, Timing tm) {
   TiledArgs a{};
   a.act = qh; a.row_scale = sh; a.counts = counts; a.offsets = offsets;
   a.mtile_off = mtile_off; a.E = E;
   a.mt_max = (int)((A + BM - 1) / BM + E);
   a.nt = (H + BN - 1) / BN; a.gn = group_n(a.nt);
-  a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.out = y;
+  a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.y = y;
   const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
   if (fp8) return launch_kernel(gemm_tiled_kernel<false, true>, grid, dim3(512), st, tm, a);
   return launch_kernel(gemm_tiled_kernel<false, false>, grid, dim3(512), st, tm, a);

@@ -259,16 +259,16 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
 }
 
 // ------------------------------------------------------------------ combine
-// "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum. Two
-// groups of four consecutive outputs of token t, at n0 and n1 (a group at
-// or past H is skipped; H is a multiple of 4):
+// "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum of token t:
 //   out[t][n] = bf16( sum over slots j < k with row_of[t*k+j] >= 0 of
 //                     w[t][j] * y[row][n] )
 // summed in fp32 in slot order (independent of scheduling), bf16 with ties
-// to even. y is fp32 [rows][H]: its only rounding is the final one to
-// bfloat16. Dropped slots add nothing; the remaining weights are not
+// to even. Dropped slots add nothing; the remaining weights are not
 // renormalised. Callers place the groups of a wavefront's 64 lanes so that
 // each load instruction reads 1 KB of one y row.
+//
+// combine_2x4: fp32 y rows; two groups of four consecutive outputs at n0
+// and n1 (a group at or past H is skipped; H is a multiple of 4).
 __device__ __forceinline__ void combine_2x4(const float *__restrict__ y,
                                             const float *__restrict__ wts,
                                             const int32_t *__restrict__ row_of, int64_t t, int H,
@@ -311,6 +311,66 @@ __device__ __forceinline__ void combine_2x4(const float *__restrict__ y,
   }
   if (g0) *reinterpret_cast<v2i *>(out + t * H + n0) = o0;
   if (g1) *reinterpret_cast<v2i *>(out + t * H + n1) = o1;
+}
+
+// combine_2x8: y rows as int16 codes with a scale per 16 columns (YRows,
+// y[row][n] = fl32(code * scale)); two groups of eight consecutive outputs
+// at n0 and n1 (multiples of 8; a group at or past H is skipped).
+__device__ __forceinline__ void combine_2x8(const YRows y, const float *__restrict__ wts,
+                                            const int32_t *__restrict__ row_of, int64_t t, int H,
+                                            int k, int n0, int n1, uint16_t *__restrict__ out) {
+  const bool g0 = n0 < H, g1 = n1 < H;
+  const int64_t hg = H / kYGroup;
+  float acc0[8], acc1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+  // Slots 8 at a time: all loads of a batch are issued before the sums,
+  // which then run in slot order over the kept slots.
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    v4i c0[8], c1[8];
+    float s0[8], s1[8], w[8];
+    bool kept[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int32_t r = j < k ? row_of[t * k + j] : -1;
+      kept[u] = r >= 0;
+      w[u] = kept[u] ? wts[t * k + j] : 0.0f;
+      if (kept[u]) {
+        const int16_t *yr = y.q + (int64_t)r * H;
+        const float *sr = y.s + (int64_t)r * hg;
+        if (g0) {
+          c0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(yr + n0));
+          s0[u] = sr[n0 / kYGroup];
+        }
+        if (g1) {
+          c1[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(yr + n1));
+          s1[u] = sr[n1 / kYGroup];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!kept[u]) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // code i of the group: low half of word i/2 for even i, high half for odd
+        const int wd0 = c0[u][i >> 1], wd1 = c1[u][i >> 1];
+        const float q0 = (float)((i & 1) ? (wd0 >> 16) : (int)(int16_t)wd0);
+        const float q1 = (float)((i & 1) ? (wd1 >> 16) : (int)(int16_t)wd1);
+        acc0[i] += w[u] * (q0 * s0[u]);
+        acc1[i] += w[u] * (q1 * s1[u]);
+      }
+    }
+  }
+  v4i o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = (int)((uint32_t)f32_to_bf16(acc0[2 * i]) | ((uint32_t)f32_to_bf16(acc0[2 * i + 1]) << 16));
+    o1[i] = (int)((uint32_t)f32_to_bf16(acc1[2 * i]) | ((uint32_t)f32_to_bf16(acc1[2 * i + 1]) << 16));
+  }
+  if (g0) *reinterpret_cast<v4i *>(out + t * H + n0) = o0;
+  if (g1) *reinterpret_cast<v4i *>(out + t * H + n1) = o1;
 }
 
 }  // namespace moe

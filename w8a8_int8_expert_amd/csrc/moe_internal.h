@@ -44,6 +44,23 @@ struct ActClip {
   int sat_m;          // 0 or 1: off
 };
 
+// GEMM2's output rows y as the combine reads them, in one of two forms:
+//  - f != NULL: fp32 rows [rows][H] (the streaming path: a decode step's y is
+//    small, and its GEMM2 writes each row's values as they come);
+//  - f == NULL: y[row][n] held as the int16 code q[row][n] times the fp32
+//    scale s[row][n/16], one scale per 16 columns (the group's largest |y| /
+//    32767; codes v/max as signed normalised 16-bit values), written by the
+//    tiled path, whose y is T*k rows: 2.25 bytes per value through HBM
+//    instead of 4. The rounding error is at most about 2^-16 of the group's
+//    largest value, far below what the output's parity bound allows.
+constexpr int kYGroup = 16;
+constexpr float kYCodeMax = 32767.0f;
+struct YRows {
+  float *f;    // [rows][H] fp32, or NULL
+  int16_t *q;  // [rows][H] codes (when f is NULL)
+  float *s;    // [rows][H / 16] scales (when f is NULL)
+};
+
 // Router logits as the routing kernels read them: the logit of (t, e) is
 // the sum, in order s = 0..nparts-1, of p[s * stride + t * E + e] (one plane
 // when the caller gives the logits, one per part of the router projection).
@@ -91,6 +108,17 @@ __device__ __forceinline__ uint32_t codes4(const float *v, float rr, bool fp8) {
   if (fp8) return f8x4(v[0], v[1], v[2], v[3], rr);
   return (uint32_t)(q8(v[0], rr) & 0xff) | ((uint32_t)(q8(v[1], rr) & 0xff) << 8) |
          ((uint32_t)(q8(v[2], rr) & 0xff) << 16) | ((uint32_t)(q8(v[3], rr) & 0xff) << 24);
+}
+// y codes: v / gm as signed normalised 16-bit values (v_cvt_pknorm_i16_f32:
+// clamp to [-1, 1], times 32767, rounded), two per 32-bit word, for a group
+// whose largest |y| is gm; the group's scale is gm / 32767. Groups whose
+// largest value is below 1e-30 get codes 0 and scale 0.
+__device__ __forceinline__ float y16_inv(float gm) { return gm > 1e-30f ? 1.0f / gm : 0.0f; }
+__device__ __forceinline__ int y16x2(float a, float b, float inv) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(a * inv, b * inv));
+}
+__device__ __forceinline__ float y16_scale(float gm) {
+  return gm > 1e-30f ? gm / kYCodeMax : 0.0f;
 }
 // Byte offset of the 1 KB fragment tile (n_tile, k_tile) of a fragment-tiled
 // [N][K] INT8 matrix.
@@ -206,14 +234,14 @@ hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *
                               Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
                               const int32_t *offsets, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_d, const float *s_d, int H, int F, int E, float *y,
+                              const int8_t *w_d, const float *s_d, int H, int F, int E, YRows y,
                               bool fp8, hipStream_t st, Timing tm);
-hipError_t launch_combine(const float *y, const float *wts, const int32_t *row_of, int64_t T,
+hipError_t launch_combine(YRows y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm);
 // stage outputs in dense rows (debug only)
 hipError_t launch_debug_rows(const int32_t *offsets, const int32_t *poffsets, int E, int64_t A,
                              const int32_t *sorted_p, const float *h_p, const int8_t *qh_t,
-                             const float *sh_p, const float *y_p, int F, int H, int32_t *sorted,
+                             const float *sh_p, YRows y_p, int F, int H, int32_t *sorted,
                              float *h, int8_t *qh, float *sh, float *y, hipStream_t st);
 hipError_t launch_debug_row_of(const int32_t *row_of_p, const int32_t *ids, const int32_t *offsets,
                                const int32_t *poffsets, int64_t A, int32_t *row_of,
