@@ -383,6 +383,37 @@ def copy_probe(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+def dense_int8_reference(torch, steps=10):
+    """The vendor library's dense INT8 GEMM (hipBLASLt through torch._int_mm,
+    int32 output) on the prefill GEMMs' shapes: all 131072 rows against one
+    expert's weights, with no gather, grouping or epilogue. Context for the
+    grouped kernels' INT8 fractions, timed with events on the same stream."""
+    dev = torch.device("cuda")
+    out = {}
+    for name, (M, K, N) in (("gemm1_shape", (131072, 4096, 3072)),
+                            ("gemm2_shape", (131072, 1536, 4096))):
+        a = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev).t()
+        for _ in range(2):
+            torch._int_mm(a, b)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record()
+            torch._int_mm(a, b)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[steps // 2]
+        tops = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+        out[name] = {"M": M, "K": K, "N": N, "ms_median": round(ms, 4), "TOPs": round(tops, 1),
+                     "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+        del a, b
+        torch.cuda.empty_cache()
+    out["library"] = "hipBLASLt via torch._int_mm (dense, int32 output)"
+    return out
+
+
 def make_layer_for(name):
     """(the layer's workload, the layer): prefill runs on the decode layer."""
     import synth
@@ -449,6 +480,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the vendor dense INT8 GEMM reference point")
     ap.add_argument("--alpha-sweep", action="store_true",
                     help="only the quantisation-error sweep over alpha and the clip variants")
     ap.add_argument("--copy-probe", action="store_true")
@@ -575,6 +608,9 @@ def main():
         "configs": configs,
     }
     res.update(extra)
+    if not args.workload and not args.no_reference:
+        log("vendor dense INT8 GEMM reference (hipBLASLt) on the prefill GEMM shapes")
+        res["dense_int8_reference"] = dense_int8_reference(torch)
     res["cpu_baseline"] = None
     if head in cpu:
         res["cpu_baseline"] = dict(cpu[head], **host_info())

@@ -227,8 +227,6 @@ def fp8_full_parity(wl, gemm_path):
     """Every stage of the FP8 layer on workload wl against the oracle, to the
     bars fp8_bounds derives."""
     import w8a8_int8_expert_amd as m
-    from moe_testlib import bf16_step
-    from synth import bf16_bits_to_f32
     layer = synth.make_layer(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
@@ -243,35 +241,47 @@ def fp8_full_parity(wl, gemm_path):
     kept = o["kept"]
     if kept == 0:
         return
-    y16 = tiled_path(wl, gemm_path)
+    t = res["gpu_tensors"]
+    gpu = dict(acc1=t["acc1"].view(-1, 2 * wl.F)[:kept].cpu().numpy().view(np.float32),
+               h=t["h"].view(-1, wl.F)[:kept].cpu().numpy(),
+               qh=t["qh"].view(-1, wl.F)[:kept].cpu().numpy(),
+               sh=t["sh"][:kept].cpu().numpy(), out=res["out"])
+    fp8_check(gpu, o, cal, wl, tiled_path(wl, gemm_path))
+
+
+def fp8_check(gpu, o, cal, wl, y16):
+    """The FP8 bars on the kept rows of o (in o's order) and the tokens of o
+    (wl.T of them): gpu holds the GPU's acc1 (fp32), h, qh, sh of those rows
+    and its bf16 output bits of those tokens."""
+    from moe_testlib import bf16_step
+    from synth import bf16_bits_to_f32
+    kept = o["kept"]
     b = fp8_bounds(o, cal, wl, y16)
     # GEMM1: fp32 sums against the exact ones
-    acc1 = res["gpu_tensors"]["acc1"].view(-1, 2 * wl.F)[:kept].cpu().numpy().view(np.float32)
-    err = np.abs(acc1.astype(np.float64) - o["acc1"])
+    err = np.abs(gpu["acc1"].astype(np.float64) - o["acc1"])
     rel = err / np.maximum(b["acc_tol"], 1e-300)
     _say("[fp8] GEMM1 error / bound: median %.3g, 99.9%% %.3g, max %.3g" % (
         np.median(rel), np.quantile(rel, 0.999), rel.max()))
     assert np.all(err <= b["acc_tol"] + 1e-30), "GEMM1 sums: max %.3g of the bound" % rel.max()
-    h = res["gpu_tensors"]["h"].view(-1, wl.F)[:kept].cpu().numpy().astype(np.float64)
-    herr = np.abs(h - o["h"].astype(np.float64))
+    herr = np.abs(gpu["h"].astype(np.float64) - o["h"].astype(np.float64))
     assert np.all(herr <= b["h_tol"] + 1e-30), "SwiGLU output: max %.3g of the bound" % (
         np.max(herr / np.maximum(b["h_tol"], 1e-300)))
     # Requantised codes: equal to the oracle's, or one e4m3 gap away where the
     # oracle's value lies within the bound of a rounding midpoint
-    qh = res["gpu_tensors"]["qh"].view(-1, wl.F)[:kept].cpu().numpy()
+    qh = gpu["qh"]
     tg, to = LUT[qh.view(np.uint8)], LUT[o["qh"].view(np.uint8)]
     dist = np.abs(tg - to)
     n_diff = int(np.count_nonzero(dist))
     _say("[fp8] requantised codes differing: %d (%.4f %%); may flip by the bound: %d" % (
         n_diff, 100.0 * n_diff / dist.size, b["n_may_flip"]))
     assert np.all(dist <= b["code_gap"]), "a code differs where no flip is possible"
-    sh = res["gpu_tensors"]["sh"][:kept].cpu().numpy().astype(np.float64)
+    sh = gpu["sh"].astype(np.float64)
     sh_o = o["sh"].astype(np.float64)
     assert np.all(np.abs(sh - sh_o) <= b["sh_rtol"] * sh_o + 1e-30), "requant scales"
     # Output, given the GPU's own codes and scales (checked against the oracle's
     # just above): the exact down projection and combine of those, within the
     # GEMM2 accumulation bound, the fp32 roundings and half a bf16 step.
-    got = bf16_bits_to_f32(res["out"]).astype(np.float64)
+    got = bf16_bits_to_f32(gpu["out"]).astype(np.float64)
     half = 0.5 * bf16_step(got)
     qv = LUT[qh.view(np.uint8)]
     exp_id = o["ids"].reshape(-1)[o["sorted"]]
@@ -309,3 +319,55 @@ def fp8_full_parity(wl, gemm_path):
          "largest error / bound %.3g" % (diff.max() / rms, np.median(lim) / rms, lim.max() / rms,
                                          np.max(diff / lim)))
     assert np.all(diff <= lim), "output past the bound by %.4g" % np.max(diff - lim)
+
+
+@pytest.mark.timeout(900)
+def test_fp8_prefill_sampled_parity(torch_cuda):
+    """The FP8 layer at the prefill shape (16384 tokens, tiled kernels): routing,
+    grouping and activation codes in full; every other stage on the kept rows
+    of the tokens that own the first and last row of each expert group and of
+    each 256-row M tile, plus 32 seeded random tokens."""
+    import w8a8_int8_expert_amd as m
+    from dataclasses import replace
+    from moe_testlib import rows_of
+    wl = synth.workload("prefill")
+    _say("[fp8] prefill sampled T=%d" % wl.T)
+    layer = synth.make_layer(synth.workload("decode"))
+    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
+                           fmt=oracle.FMT_FP8)
+    inputs = synth.make_inputs(wl, layer)
+    g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k, fp8=True)
+    upload_weights(g, cal)
+    res = run_gpu(g, inputs, wl.k, 0.0, 0)
+    ids, w = oracle.route(inputs.logits, wl.k)
+    p = oracle.permute(ids, wl.E, 0)
+    qx, sx = oracle.act_quant(inputs.x, cal["inv_s"], fmt=oracle.FMT_FP8)
+    check_routing_and_grouping(res, dict(ids=ids, w=w, **p))
+    check_act_quant(res, qx, sx)
+    edges = []
+    for e in range(wl.E):
+        lo, hi = int(p["offsets"][e]), int(p["offsets"][e + 1])
+        for r0 in range(lo, hi, 256):
+            edges += [r0, min(r0 + 255, hi - 1)]
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([p["sorted"][np.array(edges, np.int64)] // wl.k,
+                                     rng.choice(wl.T, 32, replace=False)]))
+    rows = np.sort(p["row_of"][toks].ravel())
+    rows = rows[rows >= 0].astype(np.int32)
+    _say("[fp8] prefill sampled: %d tokens, %d rows" % (toks.size, rows.size))
+    r = oracle.expert_rows(rows, ids, p["sorted"], qx, sx, cal, fmt=oracle.FMT_FP8)
+    # the sampled rows and tokens as a layer of their own: row i of the sample is
+    # permuted row rows[i]; a token's slots point into the sample
+    idx = np.full(max(p["kept"], 1), -1, np.int64)
+    idx[rows] = np.arange(rows.size)
+    ro = p["row_of"][toks]
+    row_of = np.where(ro >= 0, idx[np.maximum(ro, 0)], -1).astype(np.int32)
+    _, exact = oracle.combine(None, w[toks], row_of, r["y"], want_exact=True)
+    o = dict(kept=int(rows.size), sorted=p["sorted"][rows], ids=ids, qx=qx, sx=sx,
+             acc1=r["acc1"], h=r["h"], qh=r["qh"], sh=r["sh"], w=w[toks], row_of=row_of,
+             out_exact=exact)
+    t = res["gpu_tensors"]
+    gpu = dict(acc1=rows_of(res, rows, "acc1", 2 * wl.F).view(np.float32),
+               h=rows_of(res, rows, "h", wl.F), qh=rows_of(res, rows, "qh", wl.F),
+               sh=t["sh"].cpu().numpy()[rows], out=res["out"][toks])
+    fp8_check(gpu, o, cal, replace(wl, T=int(toks.size)), True)

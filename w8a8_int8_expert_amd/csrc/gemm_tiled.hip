@@ -520,7 +520,9 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             gm = __builtin_fmaxf(gm, __builtin_fmaxf(__builtin_fabsf(ya[q]), __builtin_fabsf(yb[q])));
-          gm = __builtin_fmaxf(gm, __shfl_xor(gm, 1, 64));
+          // the neighbour lane's maximum by a DPP quad permutation (1,0,3,2)
+          gm = __builtin_fmaxf(gm, __int_as_float(__builtin_amdgcn_update_dpp(
+                                       0, __float_as_int(gm), 0xB1, 0xF, 0xF, false)));
           if (m0 + m < R && nc + c8 < H) {
             const size_t row = (size_t)(row0 + m0 + m);
             const float inv = y16_inv(gm);

@@ -173,7 +173,12 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
   const int lane = threadIdx.x & 63;
   const int nchunk = H >> 3;
   const bool cached = nchunk <= 64 * MAXC;
+  // Up to 8 chunks per lane the scaled values themselves stay in registers
+  // (64 floats), so inv_s is read and multiplied once; more chunks keep the
+  // raw bf16 words and scale them again when the codes are made.
+  constexpr bool kKeepScaled = MAXC <= 8;
   v4i raw[MAXC];
+  float sv[kKeepScaled ? MAXC : 1][8];
   float amax = 0.0f;
   auto scale8 = [&](v4i r, int c, float *o) {
     const v4f s0 = *reinterpret_cast<const v4f *>(inv_s + c * 8);
@@ -200,7 +205,10 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
         float v[8];
         scale8(raw[i], c, v);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+        for (int j = 0; j < 8; ++j) {
+          amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+          if constexpr (kKeepScaled) sv[i][j] = v[j];
+        }
       }
     }
   } else {
@@ -231,7 +239,15 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = lane + 64 * i;
-        if (c < nchunk) add8(raw[i], c);
+        if (c < nchunk) {
+          if constexpr (kKeepScaled) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              top_insert(top, __float_as_uint(__builtin_fabsf(sv[i][j])));
+          } else {
+            add8(raw[i], c);
+          }
+        }
       }
     } else {
       for (int c = lane; c < nchunk; c += 64) add8(*reinterpret_cast<const v4i *>(xr + c * 8), c);
@@ -251,7 +267,13 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = lane + 64 * i;
-      if (c < nchunk) emit(raw[i], c);
+      if (c < nchunk) {
+        if constexpr (kKeepScaled)
+          *reinterpret_cast<uint2 *>(qr + c * 8) =
+              make_uint2(codes4(sv[i], rr, fp8), codes4(sv[i] + 4, rr, fp8));
+        else
+          emit(raw[i], c);
+      }
     }
   } else {
     for (int c = lane; c < nchunk; c += 64) emit(*reinterpret_cast<const v4i *>(xr + c * 8), c);
