@@ -80,6 +80,14 @@ static_assert(kALoads * kWaves == kATiles && kBLoads * kWaves == kBTiles, "load 
 constexpr int kEpiPitch = 96 + 8;
 constexpr int kSlice = 32 * kEpiPitch * 4;    // per-wavefront epilogue staging
 constexpr int kRowScaleAt = kWaves * kSlice;  // then 256 row scales
+// GEMM2 stages 16 rows x 192 columns per pass (the same pitch rule).
+constexpr int kEpiPitch2 = 192 + 8;
+constexpr int kSlice2 = 16 * kEpiPitch2 * 4;
+static_assert(kSlice2 <= kSlice, "GEMM2 epilogue staging");
+// After the row scales: per wavefront, GEMM2's 16 x 12 group scales of a
+// pass, stored by one instruction (16 bytes per lane).
+constexpr int kScaleStageAt = kRowScaleAt + BM * 4;
+static_assert(kScaleStageAt + kWaves * 16 * 12 * 4 <= kStages * kStageBytes, "epilogue staging");
 static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "epilogue staging");
 
 struct TiledArgs {
@@ -432,11 +440,19 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      // The scales of the lane's 16 rows (four runs of 4 consecutive rows),
+      // read before the pass's staging writes: a read issued after them
+      // cannot be moved ahead (the compiler cannot rule out aliasing) and
+      // waits for every write before it.
+      v4f rsc[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        rsc[g] = *reinterpret_cast<const v4f *>(row_scale + mw + 32 * i + 8 * g + rl);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + rl + (v & 3);
         const int m = mw + 32 * i + r;
-        const float sxv = row_scale[m];
+        const float sxv = rsc[v >> 2][v & 3];
         float mx = 0.0f;
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
@@ -469,17 +485,22 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
           }
         }
       }
-      // 32 rows x 96 columns: 24 lanes per row, 4 floats each.
+      // 32 rows x 96 columns: 24 lanes per row, 4 floats each; all reads
+      // are issued before the first store.
+      v4f hq[12];
+#pragma unroll
+      for (int j = 0; j < 12; ++j) {
+        const int c = j * 64 + lane;
+        hq[j] = *reinterpret_cast<const v4f *>(slice + (c / 24) * kEpiPitch + (c % 24) * 4);
+      }
 #pragma unroll
       for (int j = 0; j < 12; ++j) {
         const int c = j * 64 + lane;
         const int r = c / 24, c4 = (c % 24) * 4;
         const int m = mw + 32 * i + r;
-        if (m0 + m < R && f0 + c4 < F) {
-          const v4f hv = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c4);
+        if (m0 + m < R && f0 + c4 < F)
           __builtin_nontemporal_store(
-              hv, reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * F + f0 + c4));
-        }
+              hq[j], reinterpret_cast<v4f *>(a.out + (size_t)(row0 + m0 + m) * F + f0 + c4));
       }
     }
   } else {
@@ -490,32 +511,51 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
       const int n = n0 + 32 * c + (lane & 31);
       sd[c] = n < H ? a.wscale[(size_t)e * H + n] : 0.0f;
     }
+    // this wavefront's 12 column groups (16 columns each) start at group g0
+    // of a row; a pass's 16 x 12 scales are staged in LDS
+    const int hg = H / kYGroup, g0 = n0 / kYGroup;
+    float *sstage = reinterpret_cast<float *>(lds + kScaleStageAt) + 16 * 12 * wave;
+    float *slice2 = reinterpret_cast<float *>(lds + wave * kSlice2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      // the lane's 16 row scales, read ahead of the staging writes (as above)
+      v4f rsc[4];
 #pragma unroll
-      for (int hc = 0; hc < 2; ++hc) {
+      for (int g = 0; g < 4; ++g)
+        rsc[g] = *reinterpret_cast<const v4f *>(row_scale + mw + 32 * i + 8 * g + rl);
+      // Two passes of 16 rows x the wavefront's 192 columns: rows 16*vh..
+      // 16*vh+15 of row block i are the lane's v = 8*vh..8*vh+7, and each
+      // pass stores whole 384-byte runs of code rows.
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 8 * (v >> 2) + rl + (v & 3);
-          const float shv = row_scale[mw + 32 * i + r];
+      for (int vh = 0; vh < 2; ++vh) {
 #pragma unroll
-          for (int c = 0; c < 3; ++c)
-            slice[r * kEpiPitch + 32 * c + (lane & 31)] =
-                (float)acc[i][3 * hc + c][v] * shv * sd[3 * hc + c];
+        for (int vv = 0; vv < 8; ++vv) {
+          const int v = 8 * vh + vv;
+          const int r = 8 * (vv >> 2) + rl + (v & 3);  // row within the pass
+          const float shv = rsc[v >> 2][v & 3];
+#pragma unroll
+          for (int c = 0; c < 6; ++c)
+            slice2[r * kEpiPitch2 + 32 * c + (lane & 31)] = (float)acc[i][c][v] * shv * sd[c];
         }
-        // 32 rows x 96 columns: 12 lanes per row, 8 floats each, so that
+        // 16 rows x 192 columns: 24 lanes per row, 8 floats each, so that
         // every lane stores 16 bytes of codes; the two lanes 2g, 2g+1 of a
         // row hold one 16-column group (groups start on multiples of 16
-        // columns), which takes one scale.
-        const int nc = n0 + 96 * hc;
-        const int hg = H / kYGroup;
+        // columns), which takes one scale. All twelve staging reads come
+        // before the first store.
+        v4f yq[6][2];
 #pragma unroll
         for (int j = 0; j < 6; ++j) {
           const int c = j * 64 + lane;
-          const int r = c / 12, c8 = (c % 12) * 8;
-          const int m = mw + 32 * i + r;
-          const v4f ya = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c8);
-          const v4f yb = *reinterpret_cast<const v4f *>(slice + r * kEpiPitch + c8 + 4);
+          const float *src = slice2 + (c / 24) * kEpiPitch2 + (c % 24) * 8;
+          yq[j][0] = *reinterpret_cast<const v4f *>(src);
+          yq[j][1] = *reinterpret_cast<const v4f *>(src + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+          const int c = j * 64 + lane;
+          const int r = c / 24, c8 = (c % 24) * 8;
+          const int m = mw + 32 * i + 16 * vh + r;
+          const v4f ya = yq[j][0], yb = yq[j][1];
           float gm = 0.0f;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -523,15 +563,26 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
           // the neighbour lane's maximum by a DPP quad permutation (1,0,3,2)
           gm = __builtin_fmaxf(gm, __int_as_float(__builtin_amdgcn_update_dpp(
                                        0, __float_as_int(gm), 0xB1, 0xF, 0xF, false)));
-          if (m0 + m < R && nc + c8 < H) {
+          if (m0 + m < R && n0 + c8 < H) {
             const size_t row = (size_t)(row0 + m0 + m);
             const float inv = y16_inv(gm);
             const v4i q = {y16x2(ya[0], ya[1], inv), y16x2(ya[2], ya[3], inv),
                            y16x2(yb[0], yb[1], inv), y16x2(yb[2], yb[3], inv)};
-            __builtin_nontemporal_store(q, reinterpret_cast<v4i *>(a.y.q + row * H + nc + c8));
-            if ((lane & 1) == 0) a.y.s[row * hg + (nc + c8) / kYGroup] = y16_scale(gm);
+            __builtin_nontemporal_store(q, reinterpret_cast<v4i *>(a.y.q + row * H + n0 + c8));
           }
+          // every group's scale (0 for rows and columns that are not stored)
+          if ((lane & 1) == 0) sstage[r * 12 + c8 / kYGroup] = y16_scale(gm);
         }
+        // The pass's scales by one instruction: lane l < 48 stores groups
+        // 4(l%3)..4(l%3)+3 of row l/3 (16 bytes). The 16 rows are a 16-row
+        // block of the expert's padded group whenever the block starts
+        // before R (their padding rows get scale 0); groups at or past H/16
+        // (a partial last N tile) are not stored.
+        const int mb0 = m0 + mw + 32 * i + 16 * vh;
+        const int gq = g0 + 4 * (lane % 3);
+        if (lane < 48 && mb0 < R && gq < hg)
+          *reinterpret_cast<v4f *>(a.y.s + (size_t)(row0 + mb0 + lane / 3) * hg + gq) =
+              *reinterpret_cast<const v4f *>(sstage + 4 * lane);
       }
     }
   }
