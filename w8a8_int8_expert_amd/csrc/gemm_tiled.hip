@@ -89,6 +89,7 @@ static_assert(kSlice2 <= kSlice, "GEMM2 epilogue staging");
 constexpr int kScaleStageAt = kRowScaleAt + BM * 4;
 static_assert(kScaleStageAt + kWaves * 16 * 12 * 4 <= kStages * kStageBytes, "epilogue staging");
 static_assert(kRowScaleAt + BM * 4 <= kStages * kStageBytes, "epilogue staging");
+static_assert(kEpiPitch > 96, "GEMM1 keeps each staged row's maximum in column 96");
 
 struct TiledArgs {
   const int8_t *act;        // GEMM1: token-major codes [T][K]; GEMM2: fragment-tiled
@@ -451,7 +452,6 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = 8 * (v >> 2) + rl + (v & 3);
-        const int m = mw + 32 * i + r;
         const float sxv = rsc[v >> 2][v & 3];
         float mx = 0.0f;
 #pragma unroll
@@ -462,9 +462,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
           mx = __builtin_fmaxf(mx, __builtin_fabsf(hv));
         }
         // row maximum over the wavefront's 96 columns (the 32 lanes of a
-        // half), taken by lanes 31 and 63
+        // half), taken by lanes 31 and 63 into the slice's padding column
+        // 96 (the passes write columns 0..95 only)
         const uint32_t mb = half_wave_max(__float_as_uint(mx));
-        if ((lane & 31) == 31 && m0 + m < R) atomicMax(a.amax + row0 + m0 + m, mb);
+        if ((lane & 31) == 31) slice[r * kEpiPitch + 96] = __uint_as_float(mb);
       }
       if (a.acc1_dbg) {
 #pragma unroll
@@ -485,6 +486,10 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
           }
         }
       }
+      // the 32 row maxima by one atomic instruction (order independent)
+      if (lane < 32 && m0 + mw + 32 * i + lane < R)
+        atomicMax(a.amax + row0 + m0 + mw + 32 * i + lane,
+                  __float_as_uint(slice[lane * kEpiPitch + 96]));
       // 32 rows x 96 columns: 24 lanes per row, 4 floats each; all reads
       // are issued before the first store.
       v4f hq[12];

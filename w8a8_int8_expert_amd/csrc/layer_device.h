@@ -31,16 +31,6 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   const uint32_t o = (uint32_t)(key >> 32);
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, 64);
-    const uint64_t u = ((uint64_t)hi << 32) | lo;
-    v = u > v ? u : v;
-  }
-  return v;
-}
 
 // Renormalised softmax over the chosen k, from slot j's key on lane j:
 // exp(l_j - l_0) / sum over the k slots, summed in slot order.
@@ -148,8 +138,7 @@ __device__ __forceinline__ uint32_t wave_mth_largest(const uint32_t (&l)[kMaxSat
     int cnt = 0;
 #pragma unroll
     for (int s = 0; s < kMaxSatM; ++s) cnt += l[s] >= cand ? 1 : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) cnt += __shfl_xor(cnt, o, 64);
+    cnt = wave_sum(cnt);
     if (cnt >= m) ans = cand;
   }
   return ans;

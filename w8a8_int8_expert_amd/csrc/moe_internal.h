@@ -125,10 +125,73 @@ __device__ __forceinline__ float y16_scale(float gm) {
 __device__ __forceinline__ size_t frag_tile(int n_tile, int k_tile, int K) {
   return ((size_t)n_tile * (size_t)(K >> 6) + (size_t)k_tile) << 10;
 }
+// Maximum over the wavefront of a non-negative value (a |x| maximum), in
+// every lane. Non-negative floats order as their bit patterns. DPP moves
+// instead of LDS permutes: row_shr 1, 2, 4, 8 leave each 16-lane row's
+// maximum in its lane 15; row_bcast 15 into rows 1 and 3 and row_bcast 31
+// into rows 2 and 3 gather all four in lane 63, which is then read out.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, 64));
+  auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  uint32_t m = __float_as_uint(v);
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
+  m = step(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)m, 63));
+}
+// Inclusive prefix sum over the wavefront (every lane active), by the same
+// DPP steps: within each 16-lane row, lanes add the partial sums 1, 2, 4 and
+// 8 lanes below them (lanes with no such source add the 0 they are given);
+// then rows 1 and 3 add the total of the row below, and rows 2 and 3 the
+// total of rows 0 and 1.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
+}
+// Sum over the wavefront, in every lane.
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+// One DPP move of a 64-bit value (both halves from the same source lane;
+// lanes without a source get 0).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, kRowMask, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, kRowMask, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Inclusive prefix sum of 64-bit values over the wavefront (every lane active).
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v += dpp_u64<0x111, 0xF>(v);
+  v += dpp_u64<0x112, 0xF>(v);
+  v += dpp_u64<0x114, 0xF>(v);
+  v += dpp_u64<0x118, 0xF>(v);
+  v += dpp_u64<0x142, 0xA>(v);
+  v += dpp_u64<0x143, 0xC>(v);
+  return v;
+}
+// Maximum of 64-bit unsigned values over the wavefront, in every lane (every
+// lane active; 0 is the identity).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0x111, 0xF>(v));
+  v = mx(v, dpp_u64<0x112, 0xF>(v));
+  v = mx(v, dpp_u64<0x114, 0xF>(v));
+  v = mx(v, dpp_u64<0x118, 0xF>(v));
+  v = mx(v, dpp_u64<0x142, 0xA>(v));
+  v = mx(v, dpp_u64<0x143, 0xC>(v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ v4i mfma16(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);

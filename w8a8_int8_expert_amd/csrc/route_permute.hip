@@ -58,17 +58,6 @@ __device__ __forceinline__ void block_fill(uint32_t *p, int64_t n, uint32_t v) {
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = v;
 }
 
-// Inclusive wave scan of ints (64 lanes).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
 // Block-wide exclusive scan of one int per thread (blockDim.x == 1024);
 // returns the exclusive prefix, *total gets the sum. Uses wsum[16].
 __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int *total) {
@@ -138,13 +127,7 @@ __device__ __forceinline__ int finish_counts_small(int total, int E, int64_t cap
     v = (uint64_t)kept | ((uint64_t)((kept + 15) & ~15) << 21) |
         ((uint64_t)((kept + kTiledBM - 1) / kTiledBM) << 42);
   }
-  uint64_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)incl, o, 64);
-    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(incl >> 32), o, 64);
-    if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
-  }
+  const uint64_t incl = wave_incl_scan_u64(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint64_t base = 0, all = 0;
