@@ -45,6 +45,7 @@ FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.poffsets = take(sizeof(int32_t) * (E + 1));
   L.mtile_off = take(sizeof(int32_t) * (E + 1));
+  L.tile_order = take(sizeof(int32_t) * tile_order_ints(A, E, F, H));
   L.sorted = take(sizeof(int32_t) * (size_t)L.P);
   L.row_of = take(sizeof(int32_t) * A);
   L.qx = take((size_t)T * H);
@@ -230,6 +231,7 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
   int32_t *offsets = (int32_t *)(ws + L.offsets);
   int32_t *poffsets = (int32_t *)(ws + L.poffsets);
   int32_t *mtile_off = (int32_t *)(ws + L.mtile_off);
+  int32_t *tile_order = (int32_t *)(ws + L.tile_order);
   int32_t *sorted = (int32_t *)(ws + L.sorted);
   int32_t *row_of = (int32_t *)(ws + L.row_of);
   int8_t *qx = (int8_t *)(ws + L.qx);
@@ -272,6 +274,11 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
     lp = LogitPlanes{rpart, router_parts(H), T * (int64_t)E};
   }
 
+  // The tiled path's tile orders are built by extra blocks of the scatter
+  // launch (a small batch's fused prologue has no such launch: its tiles run
+  // in expert-major order).
+  const TileOrderArgs to = tile_order_args(A, E, F, H, counts, mtile_off,
+                                           path == 2 && !small ? tile_order : nullptr);
   if (small) {
     MOE_CHECK(launch_prologue_small(lp, topk_ids, topk_w, (int)T, E, k, capacity, ids,
                                     wts, counts, offsets, poffsets, mtile_off, sorted, row_of,
@@ -282,9 +289,10 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
                                 amax, sorted, L.P, st, tm(kRoute)));
     MOE_CHECK(launch_scan(blk_hist, L.nblk, E, capacity, counts, offsets, poffsets, mtile_off, st,
                           tm(kScan)));
-    MOE_CHECK(launch_scatter(ids, blk_hist, poffsets, T, E, k, capacity, sorted, row_of, st,
+    MOE_CHECK(launch_scatter(ids, blk_hist, poffsets, T, E, k, capacity, sorted, row_of, to, st,
                              tm(kScatter)));
   }
+  const int32_t *order1 = to.order[0], *order2 = to.order[1];
   if (path == 1) {
     if (!small)
       MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st, tm(kActQ)));
@@ -294,17 +302,17 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
     // GEMM1 gathers its activation rows from qx as it loads them.
     if (!small)
       MOE_CHECK(launch_act_quant(x, wt->inv_smooth, T, H, qx, sx, ac, fp8, st, tm(kActQ)));
-    MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, poffsets, offsets, mtile_off, A,
-                                 wt->w_gate_up, wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8, st,
-                                 tm(kG1)));
+    MOE_CHECK(launch_gemm1_tiled(qx, sx, sorted, k, counts, poffsets, offsets, mtile_off, order1,
+                                 A, wt->w_gate_up, wt->s_gate_up, H, F, E, h, amax, acc1_dbg, fp8,
+                                 st, tm(kG1)));
   }
   MOE_CHECK(launch_requant(h, amax, poffsets, E, L.P, F, qh, sh, fp8, st, tm(kReq)));
   if (path == 1)
     MOE_CHECK(launch_gemm2_stream(qh, sh, counts, poffsets, wt->w_down, wt->s_down, H, F, E, y.f,
                                   fp8, st, tm(kG2)));
   else
-    MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, poffsets, mtile_off, A, wt->w_down, wt->s_down,
-                                 H, F, E, y, fp8, st, tm(kG2)));
+    MOE_CHECK(launch_gemm2_tiled(qh, sh, counts, poffsets, mtile_off, order2, A, wt->w_down,
+                                 wt->s_down, H, F, E, y, fp8, st, tm(kG2)));
   MOE_CHECK(launch_combine(y, wts, row_of, T, H, k, out, st, tm(kComb)));
 
   if (dbg) {

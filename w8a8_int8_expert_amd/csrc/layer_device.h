@@ -269,6 +269,70 @@ __device__ __forceinline__ void quant_token_row(const uint16_t *__restrict__ xr,
   }
 }
 
+// ------------------------------------------------------------- tile order
+// Tile L of a tiled GEMM's expert-major order (expert, N group, M tile, N
+// tile in group) for the M-tile table mtile_off (M tiles of expert e:
+// mtile_off[e] .. mtile_off[e+1]-1), nt N tiles per expert in groups of gn.
+struct TileCoord {
+  int e, mtl, ntile;
+};
+__device__ __forceinline__ TileCoord tile_coord(const int32_t *__restrict__ mtile_off, int E,
+                                                int nt, int gn, int L) {
+  int lo = 0, hi = E;  // largest e with mtile_off[e] * nt <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (mtile_off[mid] * nt <= L) lo = mid; else hi = mid;
+  }
+  const int mtiles = mtile_off[lo + 1] - mtile_off[lo];
+  const int local = L - mtile_off[lo] * nt;
+  const int grp = local / (mtiles * gn), r_in = local - grp * (mtiles * gn);
+  const int mtl = r_in / gn;
+  return TileCoord{lo, mtl, grp * gn + (r_in - mtl * gn)};
+}
+
+// One 256-thread block's share of GEMM g's tile order: chunk x (the tiles
+// XCD x runs, places x*chunk .. x*chunk+len-1 of the expert-major order).
+// With at most kTileOrderMaxTiles tiles, the chunk's tiles are sorted stably
+// by the number of 64-row bands of the M tile that hold rows (4, 3, 2, 1):
+// a tile of a group's last, partial M tile skips the matrix work of its
+// empty bands, so the short tiles end the XCD's queue. Region: order[0] is
+// the flag (1: sorted), order[1 + place] the tile run at that place.
+__device__ __forceinline__ void tile_order_block(const TileOrderArgs &to, int x, int g) {
+  static_assert(kTileOrderMaxTiles <= 8 * 256, "one tile per thread and chunk");
+  __shared__ int wave_n[4][4];
+  int32_t *order = to.order[g];
+  const int nt = to.nt[g], gn = to.gn[g];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntiles = to.mtile_off[to.E] * nt;
+  const bool sort = ntiles > 0 && ntiles <= kTileOrderMaxTiles;
+  if (x == 0 && tid == 0) order[0] = sort ? 1 : 0;
+  if (!sort) return;
+  const int chunk = (ntiles + 7) >> 3;
+  const int lo = x * chunk;
+  const int len = ntiles - lo < chunk ? ntiles - lo : chunk;  // <= 256
+  int c = 4;  // no tile
+  if (tid < len) {
+    const TileCoord tc = tile_coord(to.mtile_off, to.E, nt, gn, lo + tid);
+    const int rows = to.counts[tc.e] - tc.mtl * kTiledBM;
+    c = rows >= kTiledBM ? 0 : 4 - (rows + 63) / 64;
+  }
+  int rank = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t m = __ballot(c == q);
+    if (c == q) rank = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_n[wave][q] = __builtin_popcountll(m);
+  }
+  __syncthreads();
+  if (c < 4) {
+    int pos = rank;
+    for (int q = 0; q < c; ++q)
+      for (int w = 0; w < 4; ++w) pos += wave_n[w][q];
+    for (int w = 0; w < wave; ++w) pos += wave_n[w][c];
+    order[1 + lo + pos] = lo + tid;
+  }
+}
+
 // ------------------------------------------------------------------ combine
 // "超大规模模型推理的Day0适配实践" §四: un-sort and gate-weighted sum of token t:
 //   out[t][n] = bf16( sum over slots j < k with row_of[t*k+j] >= 0 of

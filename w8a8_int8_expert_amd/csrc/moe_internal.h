@@ -25,6 +25,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 inline int route_tokens(int64_t T) { return T <= 4096 ? 16 : (T <= 8192 ? 32 : 64); }
 // Rows per M tile of the tiled grouped GEMMs.
 constexpr int kTiledBM = 256;
+// A tiled GEMM with at most this many tiles (three rounds of the 256
+// compute units) runs each XCD's tiles longest first.
+constexpr int kTileOrderMaxTiles = 3 * 256;
+// What the blocks that build the tile orders need: per GEMM g, its N tiles
+// per expert nt[g], N tiles per group gn[g] and its region order[g] (NULL:
+// none built).
+struct TileOrderArgs {
+  const int32_t *counts, *mtile_off;
+  int E;
+  int nt[2], gn[2];
+  int32_t *order[2];
+};
 // Maximum experts (LDS histograms are sized for it).
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
@@ -239,8 +251,8 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // Permuted rows inside the layer are "padded": every expert's group starts on
 // a 16-row boundary, so P <= A + 15*min(E, A) rows for A = T*k assignments.
 struct FwdLayout {
-  size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, sorted, row_of, qx, sx, h,
-      amax, qh, sh, y, rpart, total;
+  size_t ids, wts, blk_hist, counts, offsets, poffsets, mtile_off, tile_order, sorted, row_of,
+      qx, sx, h, amax, qh, sh, y, rpart, total;
   int64_t nblk;  // routing blocks
   int64_t P;     // padded permuted rows (upper bound)
 };
@@ -273,9 +285,10 @@ hipError_t launch_router_sum(const float *part, int nparts, int64_t T, int E, fl
 hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity, int32_t *counts,
                        int32_t *offsets, int32_t *poffsets, int32_t *mtile_off, hipStream_t st,
                        Timing tm);
+// (with to.order[g] set, 8 more blocks per GEMM g build its tile order)
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *poffsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
-                          int32_t *row_of, hipStream_t st, Timing tm);
+                          int32_t *row_of, const TileOrderArgs &to, hipStream_t st, Timing tm);
 hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, int H, int8_t *qx,
                             float *sx, ActClip ac, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
@@ -289,16 +302,24 @@ hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
                                int F, int E, float *y, bool fp8, hipStream_t st, Timing tm);
+// Tile orders of the two tiled GEMMs (gemm_tiled.hip): each GEMM's region is
+// a flag, then one tile index per place; with the flag 0 (or no region) a
+// GEMM runs its tiles in expert-major order. The regions are written by
+// extra blocks of the scatter launch. tile_order_ints: both regions' size
+// for A assignments.
+size_t tile_order_ints(int64_t A, int E, int F, int H);
+TileOrderArgs tile_order_args(int64_t A, int E, int F, int H, const int32_t *counts,
+                              const int32_t *mtile_off, int32_t *region);
 hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *sorted, int k,
                               const int32_t *counts, const int32_t *offsets,
-                              const int32_t *dense_off, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_gu, const float *s_gu, int H, int F, int E, float *h,
-                              uint32_t *amax, int32_t *acc1_dbg, bool fp8, hipStream_t st,
-                              Timing tm);
+                              const int32_t *dense_off, const int32_t *mtile_off,
+                              const int32_t *order, int64_t A, const int8_t *w_gu,
+                              const float *s_gu, int H, int F, int E, float *h, uint32_t *amax,
+                              int32_t *acc1_dbg, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *counts,
-                              const int32_t *offsets, const int32_t *mtile_off, int64_t A,
-                              const int8_t *w_d, const float *s_d, int H, int F, int E, YRows y,
-                              bool fp8, hipStream_t st, Timing tm);
+                              const int32_t *offsets, const int32_t *mtile_off,
+                              const int32_t *order, int64_t A, const int8_t *w_d, const float *s_d,
+                              int H, int F, int E, YRows y, bool fp8, hipStream_t st, Timing tm);
 hipError_t launch_combine(YRows y, const float *wts, const int32_t *row_of, int64_t T,
                           int H, int k, uint16_t *out, hipStream_t st, Timing tm);
 // stage outputs in dense rows (debug only)

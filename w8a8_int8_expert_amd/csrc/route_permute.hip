@@ -375,15 +375,24 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ blk_hi
 // (4 waves x 64 lanes, wave order = assignment order). A lane's rank among
 // equal experts of its wave comes from ballots over the id bits; earlier
 // waves of the round and earlier rounds are added through LDS counters.
+// Blocks past the nblk routing blocks build the tiled GEMMs' tile orders
+// (8 per GEMM whose region is given), which need only the M-tile table.
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t *__restrict__ ids, const int32_t *__restrict__ blk_base,
     const int32_t *__restrict__ offsets, int64_t T, int E, int k, int64_t capacity,
-    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, int tpb) {
+    int32_t *__restrict__ sorted, int32_t *__restrict__ row_of, int tpb, int nblk,
+    const TileOrderArgs to) {
+  if ((int)blockIdx.x >= nblk) {
+    const int b = (int)blockIdx.x - nblk;
+    const int g = to.order[0] ? b >> 3 : 1;  // the blocks of GEMM 1's order come first
+    tile_order_block(to, b & 7, g);
+    return;
+  }
   __shared__ int32_t running[kMaxExperts];
   __shared__ int32_t wcnt[4][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int e = tid; e < E; e += 256) {
-    running[e] = blk_base[(int64_t)e * gridDim.x + blockIdx.x];
+    running[e] = blk_base[(int64_t)e * nblk + blockIdx.x];
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
   }
   __syncthreads();
@@ -485,11 +494,12 @@ hipError_t launch_scan(int32_t *blk_hist, int64_t nblk, int E, int64_t capacity,
 
 hipError_t launch_scatter(const int32_t *ids, const int32_t *blk_hist, const int32_t *offsets,
                           int64_t T, int E, int k, int64_t capacity, int32_t *sorted,
-                          int32_t *row_of, hipStream_t st, Timing tm) {
+                          int32_t *row_of, const TileOrderArgs &to, hipStream_t st, Timing tm) {
   const int tpb = route_tokens(T);
   const int64_t nblk = (T + tpb - 1) / tpb;
-  return launch_kernel(scatter_kernel, dim3((unsigned)nblk), dim3(256), st, tm, ids, blk_hist,
-                       offsets, T, E, k, capacity, sorted, row_of, tpb);
+  const int extra = 8 * ((to.order[0] ? 1 : 0) + (to.order[1] ? 1 : 0));
+  return launch_kernel(scatter_kernel, dim3((unsigned)(nblk + extra)), dim3(256), st, tm, ids,
+                       blk_hist, offsets, T, E, k, capacity, sorted, row_of, tpb, (int)nblk, to);
 }
 
 }  // namespace moe
