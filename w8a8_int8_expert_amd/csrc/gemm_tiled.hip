@@ -50,15 +50,16 @@
 // N tile in group), so that the blocks that run together on one XCD (one L2)
 // share a few weight panels and reuse each activation tile across the group;
 // each XCD takes one contiguous eighth of that order. When a GEMM has at
-// most three rounds of tiles, each XCD runs its eighth longest first (the
-// order built by tile_order_block in the scatter launch): a tile of a
-// group's last, partial M tile skips the matrix work of its empty 64-row
-// bands and takes up to ~40 % less time, so these end the XCD's queue
-// instead of a few long tiles holding up a mostly idle last round. With
-// more rounds the blocks that finish at different times already keep the
-// compute units busy, and the expert-major order keeps a partial M tile's
-// weight panels in the caches. The grid is sized by an upper bound on the
-// tile count; surplus blocks exit at once.
+// most three rounds of tiles, the order built by tile_order_block (in the
+// scatter launch) is used instead: contiguous ranges of equal estimated
+// time per XCD, each run longest first. A tile of a group's last, partial
+// M tile skips the matrix work of its empty 64-row bands and takes up to
+// ~40 % less time, so these end the XCD's queue instead of a few long tiles
+// holding up a mostly idle last round. With more rounds the blocks that
+// finish at different times already keep the compute units busy, and the
+// expert-major order keeps a partial M tile's weight panels in the caches.
+// The grid gives each XCD as many places as either order can need; surplus
+// blocks exit at once.
 #include <type_traits>
 
 #include "layer_device.h"
@@ -108,10 +109,10 @@ struct TiledArgs {
   const int32_t *counts, *offsets, *mtile_off;  // offsets: 16-aligned group starts
   const int32_t *dense_off;                     // GEMM1: dense group starts (debug rows)
   int E;
-  int mt_max;               // upper bound on the number of M tiles
   int nt;                   // N tiles per expert
   int gn;                   // N tiles per group (divides nt)
-  const int32_t *order;     // tile order region (flag, then a tile per place), or NULL
+  const int32_t *order;     // tile order region (see tile_order_block), or NULL
+  int places;               // places per XCD in the grid (the region's stride)
   const int8_t *w;          // fragment-tiled weights
   const float *wscale;
   int K, F, H;
@@ -178,16 +179,19 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   // an expert's N groups back to back: the expert's weights are read once
   // and its activation tiles are re-read while still in the caches.
   const int E = a.E;
-  const int ntiles = a.mtile_off[E] * a.nt;
-  const int chunk = (ntiles + 7) >> 3;
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int place = xcd * chunk + idx;
-  if (idx >= chunk || place >= ntiles) return;
-  // A tile order, when one was built, permutes each XCD's chunk: its
-  // longest tiles first.
-  const bool sorted_order = a.order && a.order[0];
-  const TileCoord tc = tile_coord(a.mtile_off, E, a.nt, a.gn,
-                                  sorted_order ? a.order[1 + place] : place);
+  int L;
+  if (a.order && a.order[0]) {
+    // the XCD's range of the tile order (equal estimated time, longest first)
+    if (idx >= a.order[1 + xcd]) return;
+    L = a.order[9 + xcd * a.places + idx];
+  } else {
+    const int ntiles = a.mtile_off[E] * a.nt;
+    const int chunk = (ntiles + 7) >> 3;
+    if (idx >= chunk || xcd * chunk + idx >= ntiles) return;
+    L = xcd * chunk + idx;
+  }
+  const TileCoord tc = tile_coord(a.mtile_off, E, a.nt, a.gn, L);
   const int e = tc.e, mtl = tc.mtl, ntile = tc.ntile;
   const int R = a.counts[e];
   const int row0 = a.offsets[e];  // multiple of 16
@@ -606,24 +610,30 @@ int group_n(int nt) {
 int gemm1_ntiles(int F) { return (F + 191) / 192; }
 int gemm2_ntiles(int H) { return (H + BN - 1) / BN; }
 int64_t mtile_bound(int64_t A, int E) { return (A + BM - 1) / BM + E; }
+// places per XCD in a tiled GEMM's grid
+int xcd_places(int64_t A, int E, int nt) {
+  const int64_t p = (mtile_bound(A, E) * nt + 7) / 8;
+  return (int)(p > kTileOrderPlaces ? p : kTileOrderPlaces);
+}
 
 }  // namespace
 
 size_t tile_order_ints(int64_t A, int E, int F, int H) {
-  const size_t mt = (size_t)mtile_bound(A, E);
-  return 2 + mt * (size_t)(gemm1_ntiles(F) + gemm2_ntiles(H));
+  return 18 + 8 * (size_t)(xcd_places(A, E, gemm1_ntiles(F)) + xcd_places(A, E, gemm2_ntiles(H)));
 }
 
-// GEMM1's region first (flag + one place per tile slot), then GEMM2's.
+// GEMM1's region first (flag, 8 counts, 8 x places tiles), then GEMM2's.
 TileOrderArgs tile_order_args(int64_t A, int E, int F, int H, const int32_t *counts,
                               const int32_t *mtile_off, int32_t *region) {
   TileOrderArgs to{};
   to.counts = counts; to.mtile_off = mtile_off; to.E = E;
   to.nt[0] = gemm1_ntiles(F); to.gn[0] = group_n(to.nt[0]);
   to.nt[1] = gemm2_ntiles(H); to.gn[1] = group_n(to.nt[1]);
+  to.cap[0] = xcd_places(A, E, to.nt[0]);
+  to.cap[1] = xcd_places(A, E, to.nt[1]);
   if (region) {
     to.order[0] = region;
-    to.order[1] = region + 1 + (size_t)mtile_bound(A, E) * to.nt[0];
+    to.order[1] = region + 9 + 8 * (size_t)to.cap[0];
   }
   return to;
 }
@@ -638,11 +648,11 @@ hipError_t launch_gemm1_tiled(const int8_t *qx, const float *sx, const int32_t *
   a.act = qx; a.row_scale = sx; a.gather = sorted; a.topk = k; a.counts = counts;
   a.offsets = offsets; a.dense_off = dense_off; a.mtile_off = mtile_off; a.E = E;
   a.order = order;
-  a.mt_max = (int)mtile_bound(A, E);
   a.nt = gemm1_ntiles(F); a.gn = group_n(a.nt);
+  a.places = xcd_places(A, E, a.nt);
   a.w = w_gu; a.wscale = s_gu; a.K = H; a.F = F; a.H = H; a.out = h; a.amax = amax;
   a.acc1_dbg = acc1_dbg;
-  const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
+  const dim3 grid((unsigned)(8 * a.places));
   if (fp8) return launch_kernel(gemm_tiled_kernel<true, true>, grid, dim3(512), st, tm, a);
   return launch_kernel(gemm_tiled_kernel<true, false>, grid, dim3(512), st, tm, a);
 }
@@ -655,10 +665,10 @@ hipError_t launch_gemm2_tiled(const int8_t *qh, const float *sh, const int32_t *
   a.act = qh; a.row_scale = sh; a.counts = counts; a.offsets = offsets;
   a.mtile_off = mtile_off; a.E = E;
   a.order = order;
-  a.mt_max = (int)mtile_bound(A, E);
   a.nt = gemm2_ntiles(H); a.gn = group_n(a.nt);
+  a.places = xcd_places(A, E, a.nt);
   a.w = w_d; a.wscale = s_d; a.K = F; a.F = F; a.H = H; a.y = y;
-  const dim3 grid((unsigned)(((int64_t)a.mt_max * a.nt + 7) / 8 * 8));  // >= 8 * chunk
+  const dim3 grid((unsigned)(8 * a.places));
   if (fp8) return launch_kernel(gemm_tiled_kernel<false, true>, grid, dim3(512), st, tm, a);
   return launch_kernel(gemm_tiled_kernel<false, false>, grid, dim3(512), st, tm, a);
 }

@@ -290,32 +290,81 @@ __device__ __forceinline__ TileCoord tile_coord(const int32_t *__restrict__ mtil
   return TileCoord{lo, mtl, grp * gn + (r_in - mtl * gn)};
 }
 
-// One 256-thread block's share of GEMM g's tile order: chunk x (the tiles
-// XCD x runs, places x*chunk .. x*chunk+len-1 of the expert-major order).
-// With at most kTileOrderMaxTiles tiles, the chunk's tiles are sorted stably
-// by the number of 64-row bands of the M tile that hold rows (4, 3, 2, 1):
-// a tile of a group's last, partial M tile skips the matrix work of its
-// empty bands, so the short tiles end the XCD's queue. Region: order[0] is
-// the flag (1: sorted), order[1 + place] the tile run at that place.
+// One 256-thread block's share of GEMM g's tile order, for XCD x. With at
+// most kTileOrderMaxTiles tiles:
+//  - the expert-major order is cut into 8 contiguous ranges of about equal
+//    estimated time (a tile of an M tile with b 64-row bands of rows costs
+//    3 + b: a partial tile skips the empty bands' matrix work but still
+//    streams its whole weight panel), tile j going to the XCD that holds the
+//    midpoint of its cost; and
+//  - XCD x runs its range sorted stably by bands (4, 3, 2, 1), so that the
+//    short tiles end its queue.
+// Region: order[0] flag (1: built), order[1 + x] the number of tiles of XCD
+// x, order[9 + x * cap + i] its i-th tile (cap = to.cap[g], the places the
+// GEMM's grid gives each XCD). Every block derives the same ranges, so the
+// ones that do not fit cap (or too many tiles) leave the flag 0 everywhere.
 __device__ __forceinline__ void tile_order_block(const TileOrderArgs &to, int x, int g) {
-  static_assert(kTileOrderMaxTiles <= 8 * 256, "one tile per thread and chunk");
+  static_assert(kTileOrderMaxTiles <= 3 * 256, "three tiles per thread");
+  __shared__ int wsum[4], first[8], cnt[8];
   __shared__ int wave_n[4][4];
   int32_t *order = to.order[g];
-  const int nt = to.nt[g], gn = to.gn[g];
+  const int nt = to.nt[g], gn = to.gn[g], cap = to.cap[g];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = to.mtile_off[to.E] * nt;
-  const bool sort = ntiles > 0 && ntiles <= kTileOrderMaxTiles;
-  if (x == 0 && tid == 0) order[0] = sort ? 1 : 0;
-  if (!sort) return;
-  const int chunk = (ntiles + 7) >> 3;
-  const int lo = x * chunk;
-  const int len = ntiles - lo < chunk ? ntiles - lo : chunk;  // <= 256
-  int c = 4;  // no tile
-  if (tid < len) {
-    const TileCoord tc = tile_coord(to.mtile_off, to.E, nt, gn, lo + tid);
-    const int rows = to.counts[tc.e] - tc.mtl * kTiledBM;
-    c = rows >= kTiledBM ? 0 : 4 - (rows + 63) / 64;
+  if (ntiles <= 0 || ntiles > kTileOrderMaxTiles) {
+    if (x == 0 && tid == 0) order[0] = 0;
+    return;
   }
+  auto bands = [&](int L) {
+    const TileCoord tc = tile_coord(to.mtile_off, to.E, nt, gn, L);
+    const int rows = to.counts[tc.e] - tc.mtl * kTiledBM;
+    return rows >= kTiledBM ? 4 : (rows + 63) / 64;
+  };
+  // costs of tiles 3t .. 3t+2 and their block-wide prefix
+  int cost[3], tsum = 0;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int j = 3 * tid + s;
+    cost[s] = j < ntiles ? 3 + bands(j) : 0;
+    tsum += cost[s];
+  }
+  const int incl = wave_incl_scan(tsum);
+  if (lane == 63) wsum[wave] = incl;
+  if (tid < 8) {
+    first[tid] = ntiles;
+    cnt[tid] = 0;
+  }
+  __syncthreads();
+  int before = incl - tsum, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  // XCD of tile j: floor(8 * (its cost midpoint) / total), monotone in j
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int j = 3 * tid + s;
+    if (j < ntiles) {
+      int xj = (int)((8ll * (2ll * before + cost[s])) / (2ll * total));
+      xj = xj < 7 ? xj : 7;
+      atomicMin(&first[xj], j);
+      atomicAdd(&cnt[xj], 1);
+    }
+    before += cost[s];
+  }
+  __syncthreads();
+  bool fits = true;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) fits = fits && cnt[q] <= cap && cnt[q] <= 256;
+  if (!fits) {
+    if (x == 0 && tid == 0) order[0] = 0;
+    return;
+  }
+  const int lo = first[x], len = cnt[x];
+  // XCD x's tiles lo .. lo+len-1, stably by bands, most first
+  int c = 4;  // no tile
+  if (tid < len) c = 4 - bands(lo + tid);
   int rank = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -329,7 +378,11 @@ __device__ __forceinline__ void tile_order_block(const TileOrderArgs &to, int x,
     for (int q = 0; q < c; ++q)
       for (int w = 0; w < 4; ++w) pos += wave_n[w][q];
     for (int w = 0; w < wave; ++w) pos += wave_n[w][c];
-    order[1 + lo + pos] = lo + tid;
+    order[9 + x * cap + pos] = lo + tid;
+  }
+  if (tid == 0) {
+    order[1 + x] = len;
+    if (x == 0) order[0] = 1;
   }
 }
 

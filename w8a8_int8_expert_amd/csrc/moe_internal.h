@@ -26,15 +26,18 @@ inline int route_tokens(int64_t T) { return T <= 4096 ? 16 : (T <= 8192 ? 32 : 6
 // Rows per M tile of the tiled grouped GEMMs.
 constexpr int kTiledBM = 256;
 // A tiled GEMM with at most this many tiles (three rounds of the 256
-// compute units) runs each XCD's tiles longest first.
+// compute units) gets a tile order: ranges of equal estimated time per XCD,
+// each run longest first. Its grid then gives each XCD at least
+// kTileOrderPlaces places (a range holds at most ~0.22 of the tiles).
 constexpr int kTileOrderMaxTiles = 3 * 256;
+constexpr int kTileOrderPlaces = 192;
 // What the blocks that build the tile orders need: per GEMM g, its N tiles
-// per expert nt[g], N tiles per group gn[g] and its region order[g] (NULL:
-// none built).
+// per expert nt[g], N tiles per group gn[g], the places per XCD of its grid
+// cap[g] and its region order[g] (NULL: none built).
 struct TileOrderArgs {
   const int32_t *counts, *mtile_off;
   int E;
-  int nt[2], gn[2];
+  int nt[2], gn[2], cap[2];
   int32_t *order[2];
 };
 // Maximum experts (LDS histograms are sized for it).
@@ -302,11 +305,11 @@ hipError_t launch_gemm1_stream(const int8_t *qx, const float *sx, const int32_t 
 hipError_t launch_gemm2_stream(const int8_t *qh, const float *sh, const int32_t *counts,
                                const int32_t *poffsets, const int8_t *w_d, const float *s_d, int H,
                                int F, int E, float *y, bool fp8, hipStream_t st, Timing tm);
-// Tile orders of the two tiled GEMMs (gemm_tiled.hip): each GEMM's region is
-// a flag, then one tile index per place; with the flag 0 (or no region) a
-// GEMM runs its tiles in expert-major order. The regions are written by
-// extra blocks of the scatter launch. tile_order_ints: both regions' size
-// for A assignments.
+// Tile orders of the two tiled GEMMs (gemm_tiled.hip, tile_order_block in
+// layer_device.h): each GEMM's region is a flag, the tile count of each XCD
+// and its tiles; with the flag 0 (or no region) a GEMM runs its tiles in
+// expert-major order. The regions are written by extra blocks of the
+// scatter launch. tile_order_ints: both regions' size for A assignments.
 size_t tile_order_ints(int64_t A, int E, int F, int H);
 TileOrderArgs tile_order_args(int64_t A, int E, int F, int H, const int32_t *counts,
                               const int32_t *mtile_off, int32_t *region);
