@@ -14,16 +14,27 @@ namespace {
 
 // x bf16 [T][H] -> qx int8 [T][H], sx fp32 [T]. One wavefront per token;
 // the row stays in registers (MAXC chunks of 8 values per lane) between its
-// maximum and its codes.
-template <bool kF8, int MAXC>
+// maximum and its codes. Rows of 4097..8192 channels keep the raw words and
+// scale them twice, so there (kStage) the block first copies inv_s (32 KB
+// at most) into LDS for its four tokens, instead of every token reading it
+// twice through the caches.
+constexpr int kInvStage = 8192;
+template <bool kF8, int MAXC, bool kStage>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t *__restrict__ x,
                                                         const float *__restrict__ inv_s,
                                                         int64_t T, int H,
                                                         int8_t *__restrict__ qx,
                                                         float *__restrict__ sx, ActClip ac) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  quant_token_row<MAXC>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, kF8);
+  if constexpr (kStage) {
+    __shared__ __attribute__((aligned(16))) float sinv[kInvStage];
+    for (int i = threadIdx.x; i < (H >> 2); i += 256)
+      reinterpret_cast<v4f *>(sinv)[i] = reinterpret_cast<const v4f *>(inv_s)[i];
+    __syncthreads();
+    if (t < T) quant_token_row<MAXC>(x + t * H, sinv, H, qx + t * H, sx + t, ac, kF8);
+  } else {
+    if (t < T) quant_token_row<MAXC>(x + t * H, inv_s, H, qx + t * H, sx + t, ac, kF8);
+  }
 }
 
 // h fp32 [rows][F] with row max |h| in amax (float bits) -> qh int8 stored
@@ -71,15 +82,21 @@ hipError_t launch_act_quant(const uint16_t *x, const float *inv_s, int64_t T, in
   // rows up to 4096 channels fit eight 16-byte chunks per lane: half the
   // registers, twice the wavefronts in flight
   if (H <= 4096) {
-    if (fp8) return launch_kernel(act_quant_kernel<true, 8>, grid, dim3(256), st, tm, x, inv_s, T, H,
-                                  qx, sx, ac);
-    return launch_kernel(act_quant_kernel<false, 8>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx,
-                         ac);
+    if (fp8) return launch_kernel(act_quant_kernel<true, 8, false>, grid, dim3(256), st, tm, x,
+                                  inv_s, T, H, qx, sx, ac);
+    return launch_kernel(act_quant_kernel<false, 8, false>, grid, dim3(256), st, tm, x, inv_s, T,
+                         H, qx, sx, ac);
   }
-  if (fp8) return launch_kernel(act_quant_kernel<true, 16>, grid, dim3(256), st, tm, x, inv_s, T, H,
-                                qx, sx, ac);
-  return launch_kernel(act_quant_kernel<false, 16>, grid, dim3(256), st, tm, x, inv_s, T, H, qx, sx,
-                       ac);
+  if (H <= kInvStage) {
+    if (fp8) return launch_kernel(act_quant_kernel<true, 16, true>, grid, dim3(256), st, tm, x,
+                                  inv_s, T, H, qx, sx, ac);
+    return launch_kernel(act_quant_kernel<false, 16, true>, grid, dim3(256), st, tm, x, inv_s, T,
+                         H, qx, sx, ac);
+  }
+  if (fp8) return launch_kernel(act_quant_kernel<true, 16, false>, grid, dim3(256), st, tm, x,
+                                inv_s, T, H, qx, sx, ac);
+  return launch_kernel(act_quant_kernel<false, 16, false>, grid, dim3(256), st, tm, x, inv_s, T, H,
+                       qx, sx, ac);
 }
 
 hipError_t launch_requant(const float *h, const uint32_t *amax, const int32_t *poffsets, int E,
