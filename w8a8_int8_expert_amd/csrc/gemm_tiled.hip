@@ -180,17 +180,18 @@ __global__ __launch_bounds__(512, 1) void gemm_tiled_kernel(const TiledArgs a) {
   // and its activation tiles are re-read while still in the caches.
   const int E = a.E;
   const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int ntiles = a.mtile_off[E] * a.nt;
   int L;
   if (a.order && a.order[0]) {
     // the XCD's range of the tile order (equal estimated time, longest first)
     if (idx >= a.order[1 + xcd]) return;
     L = a.order[9 + xcd * a.places + idx];
   } else {
-    const int ntiles = a.mtile_off[E] * a.nt;
     const int chunk = (ntiles + 7) >> 3;
-    if (idx >= chunk || xcd * chunk + idx >= ntiles) return;
+    if (idx >= chunk) return;
     L = xcd * chunk + idx;
   }
+  if (L < 0 || L >= ntiles) return;
   const TileCoord tc = tile_coord(a.mtile_off, E, a.nt, a.gn, L);
   const int e = tc.e, mtl = tc.mtl, ntile = tc.ntile;
   const int R = a.counts[e];
