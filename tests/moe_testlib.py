@@ -170,12 +170,21 @@ class OutCheck:
         self.diff.append(np.abs(g - x))
         self.half.append(0.5 * bf16_step(g))
 
-    def finish(self, label=""):
+    def finish(self, label="", allow=None):
+        """allow (one chunk only): a function of flat element indices giving
+        the largest output change that requantised codes which may flip can
+        cause there (flip_allowance); it is added for elements over the bar."""
         rms = np.sqrt(self.sumsq / self.n) if self.n else 0.0
         diff = np.concatenate(self.diff) if self.diff else np.zeros(0)
         half = np.concatenate(self.half) if self.half else np.zeros(0)
         bar = OUT_RMS_FRAC * rms
         excess = diff - (bar + half + 1e-30)
+        n_flip = 0
+        if allow is not None:
+            over = np.nonzero(excess > 0)[0]
+            if over.size:
+                excess[over] -= allow(over)
+                n_flip = int(over.size)
         worst = float(np.max(excess, initial=-1.0))
         err = float(np.max(diff, initial=0.0))
         n_step = int(np.count_nonzero(diff > bar))
@@ -183,14 +192,70 @@ class OutCheck:
         past = float(np.max(diff - half, initial=0.0)) / rms if rms else 0.0
         print("[out] %s %d elements: max |gpu - exact| = %.4g x RMS, %.4g x RMS beyond half a "
               "bf16 step at |gpu| (bar %.3g x RMS); %d elements past 2e-2 x RMS, within half a "
-              "bf16 step" % (label, diff.size, rel, past, OUT_RMS_FRAC, n_step), flush=True)
+              "bf16 step; %d within the effect of codes that may flip"
+              % (label, diff.size, rel, past, OUT_RMS_FRAC, n_step, n_flip), flush=True)
         assert worst <= 0, ("output over the bar by %.4g (max err %.4g, 2e-2 x rms %.4g)"
                             % (worst, err, bar))
         return rel
 
 
-def check_out(out_g_bits, exact, label=""):
+def check_out(out_g_bits, exact, label="", allow=None):
     """The output bar on one batch: exact is the oracle's fp64 sum (out_exact)."""
     c = OutCheck()
     c.add(out_g_bits, exact)
-    return c.finish(label)
+    return c.finish(label, allow)
+
+
+def flip_allowance(o, cal, k):
+    """For an INT8 oracle forward o (with acc1 and h): a function of flat
+    output indices t*H + n giving sum over the token's kept slots of |w| times
+    the largest change of y[row][n] that the row's requantised codes which may
+    flip can cause, sh * sw_d[e][n] * sum over those codes of |q_d[e][n][f]|,
+    plus the scale's tolerance SH_RTOL * |y[row][n]|.
+
+    A code may flip where the GPU's fp32 SwiGLU, whose h differs from the
+    oracle's fl32 of the fp64 value by at most 2^-20 + |g| * 2^-21 relative
+    (g the gate pre-activation: the exponential's argument carries its
+    relative rounding into exp), and its row maximum by the largest such
+    bound, can move the code-space value c = fl32(h * fl32(127 / max|h|))
+    across a rounding midpoint: |c| within |c| * (eps_h + eps_max + 2^-22) +
+    2^-24 of n + 1/2."""
+    H = cal["q_d"].shape[1]
+    F = cal["q_d"].shape[2]
+    ids = o["ids"].reshape(-1)
+    cache = {}
+
+    def row_effect(r):
+        if r in cache:
+            return cache[r]
+        a = int(o["sorted"][r])
+        t, e = a // k, int(ids[a])
+        g = o["acc1"][r, :F].astype(np.float64) * float(o["sx"][t]) * \
+            cal["sw_gu"][e, :F].astype(np.float64)
+        eps_h = 2.0 ** -20 + np.abs(g) * 2.0 ** -21
+        h = o["h"][r].astype(np.float32)
+        amax = np.float32(np.max(np.abs(h)))
+        if amax == 0:
+            eff = np.zeros(H)
+        else:
+            rr = np.float32(127.0) / amax
+            c = np.abs((h * rr).astype(np.float32).astype(np.float64))
+            dc = c * (eps_h + eps_h.max() + 2.0 ** -22) + 2.0 ** -24
+            may = np.abs(c - np.floor(c) - 0.5) <= dc
+            qd = np.abs(cal["q_d"][e][:, may].astype(np.float64)).sum(axis=1)
+            eff = float(o["sh"][r]) * cal["sw_d"][e].astype(np.float64) * qd
+        eff = eff + SH_RTOL * np.abs(o["y"][r])
+        cache[r] = eff
+        return eff
+
+    def allow(flat):
+        out = np.zeros(flat.size)
+        for i, f in enumerate(flat):
+            t, n = divmod(int(f), H)
+            for j in range(k):
+                r = int(o["row_of"][t, j])
+                if r >= 0:
+                    out[i] += abs(float(o["w"][t, j])) * row_effect(r)[n]
+        return out
+
+    return allow

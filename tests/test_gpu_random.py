@@ -16,7 +16,7 @@ from test_gpu_parity import _full_parity, _layer_and_cal, _say, torch_cuda  # no
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 96
 
 
 def _draw(i):
