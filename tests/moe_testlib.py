@@ -206,44 +206,50 @@ def check_out(out_g_bits, exact, label="", allow=None):
     return c.finish(label, allow)
 
 
+def may_flip(o, cal, k, r):
+    """Mask over the F requantised codes of kept row r of an INT8 oracle
+    forward o (with acc1 and h): the codes that an fp32 SwiGLU may round
+    differently from the oracle.
+
+    The GPU's h differs from the oracle's fl32 of the fp64 value by at most
+    2^-20 + |g| * 2^-21 relative (g the gate pre-activation: the exponential's
+    argument carries its relative rounding into exp), and its row maximum by
+    the largest such bound. The code-space value c = fl32(h * fl32(127 /
+    max|h|)) then moves by at most |c| * (eps_h + eps_max + 2^-22) + 2^-24, and
+    a code can flip only where c lies that close to a rounding midpoint."""
+    F = cal["q_d"].shape[2]
+    a = int(o["sorted"][r])
+    t, e = a // k, int(o["ids"].reshape(-1)[a])
+    g = o["acc1"][r, :F].astype(np.float64) * float(o["sx"][t]) * \
+        cal["sw_gu"][e, :F].astype(np.float64)
+    eps_h = 2.0 ** -20 + np.abs(g) * 2.0 ** -21
+    h = o["h"][r].astype(np.float32)
+    amax = np.float32(np.max(np.abs(h)))
+    if amax == 0:
+        return np.zeros(F, bool)
+    rr = np.float32(127.0) / amax
+    c = np.abs((h * rr).astype(np.float32).astype(np.float64))
+    dc = c * (eps_h + eps_h.max() + 2.0 ** -22) + 2.0 ** -24
+    return np.abs(c - np.floor(c) - 0.5) <= dc
+
+
 def flip_allowance(o, cal, k):
     """For an INT8 oracle forward o (with acc1 and h): a function of flat
-    output indices t*H + n giving sum over the token's kept slots of |w| times
-    the largest change of y[row][n] that the row's requantised codes which may
-    flip can cause, sh * sw_d[e][n] * sum over those codes of |q_d[e][n][f]|,
-    plus the scale's tolerance SH_RTOL * |y[row][n]|.
-
-    A code may flip where the GPU's fp32 SwiGLU, whose h differs from the
-    oracle's fl32 of the fp64 value by at most 2^-20 + |g| * 2^-21 relative
-    (g the gate pre-activation: the exponential's argument carries its
-    relative rounding into exp), and its row maximum by the largest such
-    bound, can move the code-space value c = fl32(h * fl32(127 / max|h|))
-    across a rounding midpoint: |c| within |c| * (eps_h + eps_max + 2^-22) +
-    2^-24 of n + 1/2."""
+    output indices t*H + n giving the sum over the token's kept slots of |w|
+    times the largest change of y[row][n] that the row's codes which may flip
+    (may_flip) can cause, sh * sw_d[e][n] * sum over those codes of
+    |q_d[e][n][f]|, plus the scale's tolerance SH_RTOL * |y[row][n]|."""
     H = cal["q_d"].shape[1]
-    F = cal["q_d"].shape[2]
     ids = o["ids"].reshape(-1)
     cache = {}
 
     def row_effect(r):
         if r in cache:
             return cache[r]
-        a = int(o["sorted"][r])
-        t, e = a // k, int(ids[a])
-        g = o["acc1"][r, :F].astype(np.float64) * float(o["sx"][t]) * \
-            cal["sw_gu"][e, :F].astype(np.float64)
-        eps_h = 2.0 ** -20 + np.abs(g) * 2.0 ** -21
-        h = o["h"][r].astype(np.float32)
-        amax = np.float32(np.max(np.abs(h)))
-        if amax == 0:
-            eff = np.zeros(H)
-        else:
-            rr = np.float32(127.0) / amax
-            c = np.abs((h * rr).astype(np.float32).astype(np.float64))
-            dc = c * (eps_h + eps_h.max() + 2.0 ** -22) + 2.0 ** -24
-            may = np.abs(c - np.floor(c) - 0.5) <= dc
-            qd = np.abs(cal["q_d"][e][:, may].astype(np.float64)).sum(axis=1)
-            eff = float(o["sh"][r]) * cal["sw_d"][e].astype(np.float64) * qd
+        e = int(ids[int(o["sorted"][r])])
+        may = may_flip(o, cal, k, r)
+        qd = np.abs(cal["q_d"][e][:, may].astype(np.float64)).sum(axis=1)
+        eff = float(o["sh"][r]) * cal["sw_d"][e].astype(np.float64) * qd
         eff = eff + SH_RTOL * np.abs(o["y"][r])
         cache[r] = eff
         return eff

@@ -1,0 +1,143 @@
+"""The output bar's allowance for requantised codes that may flip, checked on
+the CPU against an independent fp32 implementation of the SwiGLU and the
+requantisation (numpy float32, each operation rounded to fp32 in the order a
+GPU kernel takes them: dequantise as (acc * sx) * sw, exp, reciprocal,
+g * sigmoid * u).
+
+Intermediate requantised codes may differ from the oracle's by one step in a
+small share of entries; on an outlier row one such flip, times a large down
+weight, can move an output element past 2e-2 x RMS by itself. The allowance
+(moe_testlib.may_flip / flip_allowance) claims, from oracle quantities alone,
+which codes an fp32 SwiGLU may round differently and how far that can move the
+output. Here every code the fp32 implementation rounds differently must be one
+it names, and the output built from the fp32 codes must pass the bar with it.
+No GPU is needed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import moe_testlib
+from moe_testlib import check_out, flip_allowance, may_flip
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+f32 = np.float32
+
+# The seeded random configuration whose GPU run showed the effect (3 of 2.6 M
+# codes flipped by one step, output 0.034 x RMS from the exact sum), and the
+# small outlier case.
+CASES = {
+    "random_case90": dict(T=2521, H=256, F=128, E=128, k=8, layer_seed=7090, input_seed=8090,
+                          logit_step=0.25, outlier_frac=0.02, outlier_mult=50.0,
+                          lognormal_tokens=True),
+    "tiny_outliers": dict(outlier_frac=0.02, outlier_mult=50.0, lognormal_tokens=True, T=33),
+}
+
+
+def _fp32_requant(o, cal, k):
+    """Codes and scales of the kept rows from an fp32 SwiGLU of the oracle's
+    INT32 accumulators."""
+    kept = o["kept"]
+    F = cal["q_d"].shape[2]
+    a = o["sorted"][:kept].astype(np.int64)
+    t, e = a // k, o["ids"].reshape(-1)[a]
+    sx = o["sx"][t].astype(f32)[:, None]
+    acc = o["acc1"][:kept]
+    sw = cal["sw_gu"][e].astype(f32)
+    g = (acc[:, :F].astype(f32) * sx) * sw[:, :F]
+    u = (acc[:, F:].astype(f32) * sx) * sw[:, F:]
+    sig = f32(1.0) / (f32(1.0) + np.exp(-g))
+    h = (g * sig) * u
+    assert h.dtype == f32
+    amax = np.max(np.abs(h), axis=1)
+    safe = np.where(amax > 0, amax, f32(1.0))
+    rr = (f32(127.0) / safe).astype(f32)
+    q = np.clip(np.rint((h * rr[:, None]).astype(f32)), -127, 127).astype(np.int8)
+    q[amax == 0] = 0
+    sh = (amax / f32(127.0)).astype(f32)
+    return q, sh, e
+
+
+def _output(o, cal, k, q, sh, e):
+    """fp64 combine of y from the given codes, rounded once to bf16 bits."""
+    T = o["row_of"].shape[0]
+    H = cal["q_d"].shape[1]
+    y = np.zeros((q.shape[0], H))
+    for ex in np.unique(e):
+        rows = np.nonzero(e == ex)[0]
+        acc2 = q[rows].astype(np.float64) @ cal["q_d"][ex].astype(np.float64).T
+        y[rows] = acc2 * sh[rows, None].astype(np.float64) * \
+            cal["sw_d"][ex].astype(np.float64)[None, :]
+    out = np.zeros((T, H))
+    for j in range(k):
+        r = o["row_of"][:, j]
+        ok = r >= 0
+        out[ok] += o["w"][ok, j].astype(np.float64)[:, None] * y[r[ok]]
+    return synth.f32_to_bf16_bits(out.astype(f32))
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fp32_flips_within_allowance(name):
+    wl = synth.workload("tiny", **CASES[name])
+    layer = synth.make_layer(wl)
+    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
+    inputs = synth.make_inputs(wl, layer)
+    o = oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits, ids=inputs.ids, w=inputs.w,
+                       capacity_factor=wl.capacity_factor)
+    q, sh, e = _fp32_requant(o, cal, wl.k)
+    qo = o["qh"][:o["kept"]]
+    d = q.astype(np.int32) - qo.astype(np.int32)
+    assert np.abs(d).max(initial=0) <= 1
+    rows = np.unique(np.nonzero(d)[0])
+    for r in rows:
+        flipped = d[r] != 0
+        named = may_flip(o, cal, wl.k, int(r))
+        assert not np.any(flipped & ~named), "row %d: a flip the allowance does not name" % r
+    np.testing.assert_allclose(sh, o["sh"][:o["kept"]], rtol=1e-5, atol=0)
+    print("[flip] %s: %d of %d codes differ from the oracle's, in %d rows"
+          % (name, int(np.count_nonzero(d)), d.size, rows.size))
+    check_out(_output(o, cal, wl.k, q, sh, e), o["out_exact"], name,
+              allow=flip_allowance(o, cal, wl.k))
+
+
+def test_allowance_magnitude(monkeypatch):
+    """With exactly one code named as may-flip (code f of kept row r), the
+    allowance at every output of r's token equals the sum over its kept slots
+    of |w| * SH_RTOL * |y|, plus, for r's slot, |w| * sh[r] * |sw_d[e][n] *
+    q_d[e][n][f]|: the exact effect of flipping that code by one step."""
+    wl = synth.workload("tiny", **CASES["tiny_outliers"])
+    layer = synth.make_layer(wl)
+    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
+    inputs = synth.make_inputs(wl, layer)
+    o = oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits, ids=inputs.ids, w=inputs.w,
+                       capacity_factor=wl.capacity_factor)
+    H, F = cal["q_d"].shape[1], cal["q_d"].shape[2]
+    assert H != F  # a transposed q_d would not even broadcast
+    r, f = o["kept"] // 2, 5
+
+    def only(o_, cal_, k_, row):
+        m = np.zeros(F, bool)
+        m[f] = row == r
+        return m
+
+    monkeypatch.setattr(moe_testlib, "may_flip", only)
+    allow = moe_testlib.flip_allowance(o, cal, wl.k)
+    a = int(o["sorted"][r])
+    t, ex = a // wl.k, int(o["ids"].reshape(-1)[a])
+    scale_only = np.zeros(H)
+    flip = np.zeros(H)
+    for j in range(wl.k):
+        rj = int(o["row_of"][t, j])
+        if rj < 0:
+            continue
+        wj = abs(float(o["w"][t, j]))
+        scale_only += wj * moe_testlib.SH_RTOL * np.abs(o["y"][rj])
+        if rj == r:
+            flip += wj * float(o["sh"][r]) * np.abs(
+                cal["sw_d"][ex].astype(np.float64) * cal["q_d"][ex][:, f].astype(np.float64))
+    got = allow(t * H + np.arange(H))
+    np.testing.assert_allclose(got, scale_only + flip, rtol=1e-12, atol=0)
+    # the flip's term dominates wherever its weight code is not small
+    assert np.count_nonzero(flip > 10 * scale_only) > H // 2
