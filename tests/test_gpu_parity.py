@@ -234,6 +234,53 @@ def test_calibrate_parity(torch_cuda, name):
     assert np.array_equal(q_d, cal["q_d"])
 
 
+NONFINITE = {
+    # the fused small-batch prologue (8 experts: one rank per lane)
+    "tiny": dict(T=40),
+    # the routing launches of a larger batch, 128 experts (two per lane)
+    "E128_k8": dict(T=400, E=128, k=8, H=256, F=128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NONFINITE))
+def test_nonfinite_logits(torch_cuda, name):
+    """Router logits with NaN and infinite entries. Reading: a NaN ranks below
+    every number, -inf below every finite one, so a row with at least k
+    finite logits routes as if its NaNs were -inf: that oracle's ids and
+    weights, and its output. A row with no finite logit takes experts
+    0..k-1 (equal keys: the lower index wins), its weights and output are
+    NaN and are not compared."""
+    wl = synth.workload("tiny", **NONFINITE[name])
+    _say("[nonfinite] %s %s" % (name, NONFINITE[name]))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    lg = inputs.logits.copy()
+    T, E, k = wl.T, wl.E, wl.k
+    nan, inf = np.float32(np.nan), np.float32(np.inf)
+    lg[0, 3] = nan                      # one NaN
+    lg[1, : E - k] = nan                # exactly k finite logits left
+    lg[2, ::2] = -inf                   # masked experts
+    lg[3, :] = nan                      # no finite logit
+    lg[4, 1], lg[4, E - 1] = nan, -inf
+    lg[5, E // 2] = inf                 # one +inf: chosen first, with weight NaN
+    g = run_gpu(_gpu_layer(wl, cal), synth.Inputs(x=inputs.x, logits=lg), k)
+    ids = g["ids"]
+    assert ids.min() >= 0 and ids.max() < E
+    assert all(len(set(r)) == k for r in ids.tolist()), "repeated expert in a row"
+    assert ids[3].tolist() == list(range(k))
+    assert ids[5, 0] == E // 2
+    o = oracle.forward(inputs.x, cal, k, logits=np.where(np.isnan(lg), -inf, lg))
+    assert np.array_equal(ids, o["ids"]), "routing ids differ"
+    cmp_rows = np.ones(T, bool)
+    cmp_rows[[3, 5]] = False
+    assert np.max(np.abs(g["w"][cmp_rows].astype(np.float64) - o["w"][cmp_rows]),
+                  initial=0.0) <= 1e-6
+    H = wl.H
+    c = OutCheck()
+    c.add(g["out"].reshape(T, H)[cmp_rows], o["out_exact"].reshape(T, H)[cmp_rows])
+    c.finish(name)
+
+
 def test_deterministic_and_t0(torch_cuda):
     """Two runs give identical bits; T = 0 is a no-op."""
     import torch
