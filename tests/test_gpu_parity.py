@@ -109,6 +109,10 @@ SMALL = {
     # top-32 of 40 experts held one per lane (rank-based top-k), and top-16 batched
     "k32_E40": dict(E=40, k=32, H=256, F=128, T=50),
     "route_k16_E64": dict(E=64, k=16, H=256, F=128, T=300),
+    # capacity 1 (ceil(cf * T * k / E) for the smallest cf): each expert keeps its first
+    # assignment, most tokens lose every slot and come out zero; fused and batched routing
+    "tiny_cap1": dict(capacity_factor=1e-4, T=50),
+    "route_cap1": dict(capacity_factor=1e-4, T=3000, E=16, k=2, H=256, F=128),
 }
 
 
@@ -232,6 +236,27 @@ def test_calibrate_parity(torch_cuda, name):
     assert np.array_equal(q_gu, cal["q_gu"])
     q_d = unpack_tiled(g.w_down.cpu().numpy(), wl.E, wl.H, wl.F)
     assert np.array_equal(q_d, cal["q_d"])
+
+
+@pytest.mark.parametrize("gemm_path", [1, 2])
+def test_zero_token_rows(torch_cuda, gemm_path):
+    """Tokens whose activations are all +0 or all -0: scale 0 and codes 0, so
+    their expert rows have GEMM1 sums 0, h 0 and a row maximum of 0 (scale 0,
+    codes 0 in the requantisation), and their output is 0; the other tokens
+    are unaffected."""
+    wl = synth.workload("tiny", T=30)
+    _say("[parity] zero rows path=%d" % gemm_path)
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    x = inputs.x.copy()
+    x[[0, 7, 8]] = 0
+    x[[12, 29]] = 0x8000
+    inputs = synth.Inputs(x=x, logits=inputs.logits)
+    _full_parity(wl, inputs, cal, gemm_path)
+    g = run_gpu(_gpu_layer(wl, cal), inputs, wl.k, wl.capacity_factor, gemm_path)
+    out = synth.bf16_bits_to_f32(g["out"]).reshape(wl.T, wl.H)
+    assert not np.any(out[[0, 7, 8, 12, 29]]), "a zero token's output is not zero"
+    assert not np.any(g["sx"][[0, 7, 8, 12, 29]])
 
 
 NONFINITE = {
