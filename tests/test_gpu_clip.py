@@ -9,7 +9,7 @@ import pytest
 import oracle
 import synth
 from moe_testlib import (bf16_tensor, check_act_quant, check_out, check_requant,
-                         check_routing_and_grouping, run_gpu, upload_weights)
+                         check_routing_and_grouping, flip_allowance, run_gpu, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,7 @@ def clip_full_parity(torch, wl, gemm_path, static, sat_p):
         qh = res["gpu_tensors"]["qh"].view(-1, wl.F)[:kept].cpu().numpy()
         sh = res["gpu_tensors"]["sh"][:kept].cpu().numpy()
         check_requant(qh, sh, o["qh"], o["sh"])
-    check_out(res["out"], o["out_exact"])
+    check_out(res["out"], o["out_exact"], allow=flip_allowance(o, cal, wl.k))
 
 
 def test_saturation_rank_limit(torch_cuda):

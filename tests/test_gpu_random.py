@@ -16,7 +16,7 @@ from test_gpu_parity import _full_parity, _layer_and_cal, _say, torch_cuda  # no
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = 160
 
 
 def _draw(i):
@@ -57,10 +57,10 @@ def test_random_config_parity(torch_cuda, i):  # noqa: F811
 
 
 
-# Six draws over the widest routing the library accepts: 129 to 1024 experts
+# Draws over the widest routing the library accepts: 129 to 1024 experts
 # (two to sixteen experts per router lane) and top-k up to 32, small hidden and
 # FFN sizes, with or without capacity and tied logits.
-N_WIDE = 6
+N_WIDE = 24
 
 
 def _draw_wide(i):
@@ -92,10 +92,10 @@ def test_random_config_wide_routing_parity(torch_cuda, i):  # noqa: F811
     _full_parity(wl, inputs, cal, path)
 
 
-# The FP8 (e4m3) expert path on twelve further draws, to its own bars (activation
+# The FP8 (e4m3) expert path on further draws, to its own bars (activation
 # codes and scales bit-exact; every other bar derived from the oracle's
 # quantities and the accumulation assumption, test_gpu_fp8.fp8_bounds).
-N_FP8 = 12
+N_FP8 = 36
 CASES_FP8 = [_draw(100 + i) for i in range(N_FP8)]
 
 
@@ -108,8 +108,8 @@ def test_random_config_fp8_parity(torch_cuda, i):  # noqa: F811
     fp8_full_parity(wl, path)
 
 
-# Router-projection mode (logits = x . W_r^T on the GPU) on eight further draws.
-N_ROUTER = 8
+# Router-projection mode (logits = x . W_r^T on the GPU) on further draws.
+N_ROUTER = 24
 CASES_ROUTER = [_draw(200 + i) for i in range(N_ROUTER)]
 
 
@@ -123,10 +123,10 @@ def test_random_config_router_parity(torch_cuda, i):  # noqa: F811
     router_full_parity(torch_cuda, wl, path)
 
 
-# Activation clips on eight further draws: dynamic saturation at a percentile
+# Activation clips on further draws: dynamic saturation at a percentile
 # that leaves 2-12 values of a token above the level, with or without the static
 # clip from the calibration tokens.
-N_CLIP = 8
+N_CLIP = 24
 
 
 def _draw_clip(i):
