@@ -150,3 +150,41 @@ def test_random_config_clip_parity(torch_cuda, i):  # noqa: F811
     wl = synth.workload("tiny", **over)
     _say("[random clip] case=%d path=%d static=%s sat=%.6g %s" % (i, path, static, sat_p, over))
     clip_full_parity(torch_cuda, wl, path, static, sat_p)
+
+
+# Medium shapes: hidden 1536-4096, FFN 512-2048, up to 64 experts, so that the
+# K loops run 24-64 stages and GEMM2 has up to 11 N tiles (weights capped at
+# 1.2 GB, oracle work at 1.5e10 multiply-adds per draw).
+N_MEDIUM = 12
+
+
+def _draw_medium(i):
+    rng = np.random.default_rng(np.random.SeedSequence([2030, i]))
+    H = int(rng.choice([1536, 2048, 2560, 3072, 4096]))
+    F = int(rng.choice([512, 768, 1024, 1536, 2048]))
+    E = int(rng.choice([4, 8, 16, 33, 64]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    if E * 3 * H * F > 1.2e9:
+        E = max(1, int(1.2e9 // (3 * H * F)))
+        k = min(k, E)
+    t_max = max(1, min(1500, int(1.5e10 // (k * 3 * H * F))))
+    T = int(rng.integers(1, t_max + 1))
+    over = dict(T=T, H=H, F=F, E=E, k=k, layer_seed=11000 + i, input_seed=12000 + i)
+    if rng.random() < 0.3:
+        over["capacity_factor"] = float(np.round(rng.uniform(0.5, 1.5), 2))
+    if rng.random() < 0.3:
+        over.update(outlier_frac=0.02, outlier_mult=50.0, lognormal_tokens=True)
+    return over, int(rng.integers(1, 3))
+
+
+CASES_MEDIUM = [_draw_medium(i) for i in range(N_MEDIUM)]
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_random_config_medium_parity(torch_cuda, i):  # noqa: F811
+    over, path = CASES_MEDIUM[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random medium] case=%d path=%d %s" % (i, path, over))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    _full_parity(wl, inputs, cal, path)
