@@ -237,3 +237,21 @@ def test_pack_validation(lib):
     assert lib.moe_w8a8_pack(1, 24, 64, A, B, None) == UNS            # N % 16
     assert lib.moe_w8a8_pack(1, 16, 96, A, B, None) == UNS            # K % 64
     assert lib.moe_w8a8_pack(1 << 20, 1 << 14, 1 << 14, A, B, None) == INV   # > 2^40 bytes
+
+
+def test_library_shares_torch_hip_runtime():
+    """Loading the library before torch is imported still leaves one HIP runtime
+    in the process, torch's: the binding's device memory and streams belong to
+    it. (A second runtime, initialised after torch's, finds no device.)"""
+    import subprocess
+    import sys
+    code = ("import w8a8_int8_expert_amd as m\n"
+            "m.load_library()\n"
+            "import torch\n"
+            "print(sorted(set(l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l)))\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    maps = eval(r.stdout.strip().splitlines()[-1])
+    assert len(maps) == 1 and "/torch/lib/" in maps[0], maps

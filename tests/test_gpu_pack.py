@@ -38,3 +38,40 @@ def test_pack_matches_layout(torch_cuda, count, N, K):
     got = d.cpu().numpy()
     assert np.array_equal(got, pack_tiled(src))
     assert np.array_equal(unpack_tiled(got, count, N, K), src)
+
+
+def test_stale_hip_error_not_reported(torch_cuda):
+    """An error that another HIP user in the process left pending (here a
+    hipSetDevice to a device that does not exist, which changes nothing else)
+    is not reported as the failure of the library's next launch: the pack and
+    a whole forward after it still succeed and give their results."""
+    import ctypes
+    torch = torch_cuda
+    import synth
+    import w8a8_int8_expert_amd as m
+    hip = ctypes.CDLL("libamdhip64.so")
+    dev = torch.device("cuda")
+    src = torch.randint(-127, 128, (2, 32, 128), dtype=torch.int8, device=dev)
+    dst = torch.empty(2 * 32 * 128, dtype=torch.int8, device=dev)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    assert m.moe_w8a8_pack(2, 32, 128, src, dst) == m.MOE_W8A8_OK
+    torch.cuda.synchronize()
+    want = pack_tiled(src.cpu().numpy())
+    assert np.array_equal(dst.cpu().numpy(), want)
+    # a forward of the tiny layer after another pending error
+    wl = synth.workload("tiny")
+    layer = synth.make_layer(wl)
+    g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
+    g.calibrate(torch.from_numpy(layer.calib_x.view("int16")).to(dev).view(torch.bfloat16),
+                torch.from_numpy(layer.w_gate).to(dev), torch.from_numpy(layer.w_up).to(dev),
+                torch.from_numpy(layer.w_down).to(dev), wl.alpha)
+    inputs = synth.make_inputs(wl, layer)
+    x = torch.from_numpy(inputs.x.view("int16")).to(dev).view(torch.bfloat16)
+    lg = torch.from_numpy(inputs.logits).to(dev)
+    ref = g.forward(x, lg).clone()
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    out = g.forward(x, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

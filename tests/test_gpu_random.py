@@ -188,3 +188,17 @@ def test_random_config_medium_parity(torch_cuda, i):  # noqa: F811
     layer, cal = _layer_and_cal(wl)
     inputs = synth.make_inputs(wl, layer)
     _full_parity(wl, inputs, cal, path)
+
+
+# FP8 experts on four further medium-size draws, to the FP8 bars.
+N_MEDIUM_FP8 = 4
+CASES_MEDIUM_FP8 = [_draw_medium(100 + i) for i in range(N_MEDIUM_FP8)]
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM_FP8))
+def test_random_config_medium_fp8_parity(torch_cuda, i):  # noqa: F811
+    from test_gpu_fp8 import fp8_full_parity
+    over, path = CASES_MEDIUM_FP8[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random medium fp8] case=%d path=%d %s" % (i, path, over))
+    fp8_full_parity(wl, path)

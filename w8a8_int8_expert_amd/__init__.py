@@ -59,13 +59,20 @@ _lib = None
 
 
 def load_library(path: str = LIB_PATH):
-    """Load libmoe_w8a8.so; raises if it has not been built."""
+    """Load libmoe_w8a8.so; raises if it has not been built.
+
+    torch is imported first: the binding hands the library torch's device
+    memory and streams, so the library must run on torch's HIP runtime. Its
+    dependency on libamdhip64.so.7 then resolves to the runtime torch already
+    loaded (same soname); loaded the other way round, the process would hold
+    two HIP runtimes, and the one initialised second finds no device."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError("libmoe_w8a8.so is not built (%s); run "
                            "`python -m w8a8_int8_expert_amd.build`" % path)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     D, W, G = ctypes.POINTER(moe_w8a8_dims), ctypes.POINTER(moe_w8a8_weights), \
         ctypes.POINTER(moe_w8a8_debug)

@@ -134,15 +134,14 @@ hipError_t launch_calib_colmax(const uint16_t *calib_x, int64_t n_calib, const f
                                const float *w_up, int H, int F, int E, uint32_t *ax, uint32_t *aw,
                                hipStream_t st) {
   const unsigned cb = (unsigned)((H + 255) / 256);
-  colmax_x_kernel<<<dim3(cb), dim3(256), 0, st>>>(calib_x, n_calib, H, ax, aw);
-  hipError_t err = hipGetLastError();
+  const hipError_t err =
+      launch_kernel(colmax_x_kernel, dim3(cb), dim3(256), st, Timing{}, calib_x, n_calib, H, ax, aw);
   if (err != hipSuccess) return err;
   const int64_t rows = (int64_t)E * F;
   const int64_t chunks = rows < 512 ? rows : 512;
   const int64_t per = (rows + chunks - 1) / chunks;
-  colmax_w_kernel<<<dim3(cb, (unsigned)((rows + per - 1) / per)), dim3(256), 0, st>>>(
-      w_gate, w_up, rows, per, H, aw);
-  return hipGetLastError();
+  return launch_kernel(colmax_w_kernel, dim3(cb, (unsigned)((rows + per - 1) / per)), dim3(256),
+                       st, Timing{}, w_gate, w_up, rows, per, H, aw);
 }
 
 // Static clipping threshold ("一晚上完成MoE模型推理优化…" §3.2: calibration
@@ -184,24 +183,22 @@ __global__ __launch_bounds__(1024) void clip_threshold_kernel(const uint16_t *__
 
 hipError_t launch_calib_clip(const uint16_t *calib_x, int64_t n_calib, int H, const float *inv_s,
                              int64_t m, float *out, hipStream_t st) {
-  clip_threshold_kernel<<<dim3(1), dim3(1024), 0, st>>>(calib_x, n_calib, H, inv_s, m, out);
-  return hipGetLastError();
+  return launch_kernel(clip_threshold_kernel, dim3(1), dim3(1024), st, Timing{}, calib_x, n_calib,
+                       H, inv_s, m, out);
 }
 
 hipError_t launch_calib_smooth(const uint32_t *ax, const uint32_t *aw, float alpha, int H,
                                float *s, float *inv_s, hipStream_t st) {
-  smooth_kernel<<<dim3((unsigned)((H + 255) / 256)), dim3(256), 0, st>>>(ax, aw, alpha, H, s,
-                                                                        inv_s);
-  return hipGetLastError();
+  return launch_kernel(smooth_kernel, dim3((unsigned)((H + 255) / 256)), dim3(256), st, Timing{},
+                       ax, aw, alpha, H, s, inv_s);
 }
 
 hipError_t launch_calib_quant(const float *w_gate, const float *w_up, const float *w_down,
                               const float *s, int H, int F, int E, int8_t *w_gu, float *s_gu,
                               int8_t *w_d, float *s_d, bool fp8, hipStream_t st) {
   const int64_t rows = (int64_t)E * 2 * F + (int64_t)E * H;
-  quant_rows_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st>>>(
-      w_gate, w_up, w_down, s, H, F, E, w_gu, s_gu, w_d, s_d, fp8);
-  return hipGetLastError();
+  return launch_kernel(quant_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), st, Timing{},
+                       w_gate, w_up, w_down, s, H, F, E, w_gu, s_gu, w_d, s_d, fp8);
 }
 
 }  // namespace moe

@@ -239,9 +239,13 @@ __device__ __forceinline__ v16f mfma32f8(v4i a0, v4i a1, v4i b0, v4i b1, v16f c)
 struct Timing {
   hipEvent_t start = nullptr, stop = nullptr;
 };
+// The launch's own error: hipGetLastError also returns an error that an
+// earlier call in the process (another library's included) left behind, so
+// that one is cleared first.
 template <typename... KArgs, typename... Args>
 inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
                                 Timing tm, Args... args) {
+  (void)hipGetLastError();
   if (tm.start || tm.stop)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, args...);
   else
