@@ -259,6 +259,40 @@ def test_zero_token_rows(torch_cuda, gemm_path):
     assert not np.any(g["sx"][[0, 7, 8, 12, 29]])
 
 
+def test_two_streams_concurrent(torch_cuda):
+    """Two layers (their own weights and workspaces) run on two side streams at
+    once, forwards interleaved: every output equals the one each layer gives
+    alone on the default stream, bit for bit (the kernels are deterministic
+    and the library keeps no state between calls outside the workspace)."""
+    torch = torch_cuda
+    dev = torch.device("cuda")
+    _say("[streams] tiny E=8 k=2 and mid E=16 k=4 on two side streams")
+    layers = []
+    for over in (dict(T=40), dict(T=300, E=16, k=4, H=512, F=384)):
+        wl = synth.workload("tiny", **over)
+        layer, cal = _layer_and_cal(wl)
+        inputs = synth.make_inputs(wl, layer)
+        g = _gpu_layer(wl, cal)
+        x = torch.from_numpy(inputs.x.view("int16")).to(dev).view(torch.bfloat16)
+        lg = torch.from_numpy(inputs.logits).to(dev)
+        ref = g.forward(x, lg).clone()
+        g.workspace(wl.T)
+        layers.append((g, x, lg, ref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [[], []]
+    for it in range(12):
+        for j, (g, x, lg, _) in enumerate(layers):
+            with torch.cuda.stream(streams[j]):
+                outs[j].append(g.forward(x, lg))
+    torch.cuda.synchronize()
+    for j, (_, _, _, ref) in enumerate(layers):
+        for o in outs[j]:
+            assert torch.equal(o, ref), "layer %d differs when run concurrently" % j
+
+
 NONFINITE = {
     # the fused small-batch prologue (8 experts: one rank per lane)
     "tiny": dict(T=40),
