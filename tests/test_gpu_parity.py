@@ -259,6 +259,28 @@ def test_zero_token_rows(torch_cuda, gemm_path):
     assert not np.any(g["sx"][[0, 7, 8, 12, 29]])
 
 
+@pytest.mark.parametrize("gemm_path", [1, 2])
+@pytest.mark.parametrize("T", [40, 3000])
+def test_invalid_expert_ids(torch_cuda, T, gemm_path):
+    """Pre-routed ids outside [0, E) (-1, E, E + 5, the int32 extremes) are
+    dropped like capacity overflow: no row, no share of the output. Checked
+    against the oracle, which drops them too, through the fused prologue
+    (T = 40) and the batched routing (T * k = 6000)."""
+    wl = synth.workload("tiny", T=T, pre_routed=True, zipf_s=1.1)
+    _say("[parity] invalid ids T=%d path=%d" % (T, gemm_path))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    ids = inputs.ids.copy()
+    E = wl.E
+    bad = [-1, E, E + 5, np.iinfo(np.int32).min, np.iinfo(np.int32).max]
+    rng = np.random.default_rng(5)
+    where = rng.choice(ids.size, size=max(5, ids.size // 7), replace=False)
+    ids.reshape(-1)[where] = np.resize(np.array(bad, np.int32), where.size)
+    ids[0, :] = -1  # a token with every slot dropped
+    inputs = synth.Inputs(x=inputs.x, ids=ids, w=inputs.w)
+    _full_parity(wl, inputs, cal, gemm_path)
+
+
 def test_two_streams_concurrent(torch_cuda):
     """Two layers (their own weights and workspaces) run on two side streams at
     once, forwards interleaved: every output equals the one each layer gives
