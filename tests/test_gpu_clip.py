@@ -115,3 +115,39 @@ def test_saturation_rank_limit(torch_cuda):
     lg = torch.zeros(4, wl.E, dtype=torch.float32, device="cuda")
     with pytest.raises(m.MoEW8A8Error):
         g.forward(x, router_logits=lg)
+
+
+def fp8_clip_full_parity(torch, wl, gemm_path, static, sat_p):
+    """FP8 experts with the static clip and/or dynamic saturation: activation
+    codes and scales bit-exact against the oracle in the FP8 format, every
+    later stage to the FP8 bars (test_gpu_fp8.fp8_check)."""
+    import w8a8_int8_expert_amd as m
+    from test_gpu_fp8 import fp8_check, tiled_path
+    dev = torch.device("cuda")
+    layer = synth.make_layer(wl)
+    cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
+                           fmt=oracle.FMT_FP8)
+    inputs = synth.make_inputs(wl, layer)
+    g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k, fp8=True)
+    upload_weights(g, cal)
+    clip = 0.0
+    if static:
+        g.calibrate_clip(bf16_tensor(layer.calib_x, dev), 99.0)
+        clip = oracle.clip_threshold(layer.calib_x, cal["inv_s"], 99.0)
+    g.set_clip(static=static, sat_percentile=sat_p)
+    res = run_gpu(g, inputs, wl.k, wl.capacity_factor, gemm_path)
+    o = oracle.forward(inputs.x, cal, wl.k, logits=inputs.logits, ids=inputs.ids, w=inputs.w,
+                       capacity_factor=wl.capacity_factor, clip=clip, sat_percentile=sat_p,
+                       fmt=oracle.FMT_FP8)
+    plain_sx = oracle.act_quant(inputs.x, cal["inv_s"], fmt=oracle.FMT_FP8)[1]
+    assert np.any(o["sx"] < plain_sx), "the clip changes no token"
+    check_routing_and_grouping(res, o)
+    check_act_quant(res, o["qx"], o["sx"])
+    kept = o["kept"]
+    if kept:
+        t = res["gpu_tensors"]
+        gpu = dict(acc1=t["acc1"].view(-1, 2 * wl.F)[:kept].cpu().numpy().view(np.float32),
+                   h=t["h"].view(-1, wl.F)[:kept].cpu().numpy(),
+                   qh=t["qh"].view(-1, wl.F)[:kept].cpu().numpy(),
+                   sh=t["sh"][:kept].cpu().numpy(), out=res["out"])
+        fp8_check(gpu, o, cal, wl, tiled_path(wl, gemm_path))

@@ -202,3 +202,17 @@ def test_random_config_medium_fp8_parity(torch_cuda, i):  # noqa: F811
     wl = synth.workload("tiny", **over)
     _say("[random medium fp8] case=%d path=%d %s" % (i, path, over))
     fp8_full_parity(wl, path)
+
+
+# FP8 experts with activation clips, on the clip family's first eight draws.
+N_FP8_CLIP = 8
+
+
+@pytest.mark.parametrize("i", range(N_FP8_CLIP))
+def test_random_config_fp8_clip_parity(torch_cuda, i):  # noqa: F811
+    from test_gpu_clip import fp8_clip_full_parity
+    over, path, static, sat_p = CASES_CLIP[i]
+    wl = synth.workload("tiny", **over)
+    _say("[random fp8 clip] case=%d path=%d static=%s sat=%.6g %s"
+         % (i, path, static, sat_p, over))
+    fp8_clip_full_parity(torch_cuda, wl, path, static, sat_p)
