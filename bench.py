@@ -340,7 +340,7 @@ def host_info():
 
 
 # Bounded samples of each workload for the CPU oracle: (tokens, minimum seconds).
-ORACLE_SAMPLE = {"tiny": (None, 2.0), "decode": (None, 8.0), "prefill": (512, 0.0),
+ORACLE_SAMPLE = {"tiny": (None, 2.0), "decode": (None, 10.0), "prefill": (512, 0.0),
                  "ep_share": (1024, 0.0), "stress": (256, 0.0)}
 
 
