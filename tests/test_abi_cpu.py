@@ -255,3 +255,31 @@ def test_library_shares_torch_hip_runtime():
     assert r.returncode == 0, r.stderr[-2000:]
     maps = eval(r.stdout.strip().splitlines()[-1])
     assert len(maps) == 1 and "/torch/lib/" in maps[0], maps
+
+
+def test_header_is_c99_and_links_from_c(tmp_path):
+    """include/moe_w8a8.h compiles as strict C99, and a C program links the
+    library and calls its host-side entry points (workspace size, error
+    strings), with the answers the Python binding gets."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(m.LIB_PATH)
+    src = tmp_path / "client.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"moe_w8a8.h\"\n"
+        "int main(void) {\n"
+        "  moe_w8a8_dims d = {4096, 1536, 64, 8};\n"
+        "  printf(\"%zu\\n%s\\n\", moe_w8a8_workspace_size(&d, 32),\n"
+        "         moe_w8a8_strerror(MOE_W8A8_ERR_WORKSPACE));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "client"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(root, "include"), str(src), "-L", libdir, "-lmoe_w8a8",
+                    "-Wl,-rpath," + libdir, "-o", str(exe)], check=True, timeout=120)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, check=True, timeout=60)
+    ws, msg = r.stdout.splitlines()
+    assert int(ws) == m.moe_w8a8_workspace_size(m.dims(4096, 1536, 64, 8), 32) > 0
+    assert msg == m.moe_w8a8_strerror(m.MOE_W8A8_ERR_WORKSPACE)
