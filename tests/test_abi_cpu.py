@@ -283,3 +283,45 @@ def test_header_is_c99_and_links_from_c(tmp_path):
     ws, msg = r.stdout.splitlines()
     assert int(ws) == m.moe_w8a8_workspace_size(m.dims(4096, 1536, 64, 8), 32) > 0
     assert msg == m.moe_w8a8_strerror(m.MOE_W8A8_ERR_WORKSPACE)
+
+
+def test_misaligned_pointers_refused(lib):
+    """Each entry point refuses a device pointer below the alignment its kernels
+    rely on (the header's rule) with MOE_W8A8_ERR_INVALID, before any launch."""
+    d = m.dims(256, 512, 8, 2)
+    for kw in (dict(x=FAKE + 8), dict(out=FAKE + 4), dict(logits=FAKE + 2),
+               dict(ws=FAKE + 128)):
+        assert _fwd(d, **kw) == m.MOE_W8A8_ERR_INVALID, kw
+    assert _fwd(d, logits=None, ids=FAKE + 2, w=FAKE) == m.MOE_W8A8_ERR_INVALID
+    assert _fwd(d, logits=None, ids=FAKE, w=FAKE + 1) == m.MOE_W8A8_ERR_INVALID
+    for field, off in (("w_gate_up", 8), ("w_down", 4), ("inv_smooth", 8), ("s_gate_up", 2),
+                       ("s_down", 1), ("act_clip", 2), ("w_router", 8)):
+        wt = _weights()
+        setattr(wt, field, FAKE + off)
+        assert _fwd(d, weights=wt) == m.MOE_W8A8_ERR_INVALID, field
+    # the same checks come before the no-allocation forward touches the GPU
+    assert lib.moe_w8a8_forward_noalloc(ctypes.byref(d), ctypes.byref(_weights()), FAKE + 8, 4,
+                                        FAKE, None, None, 0.0, FAKE, None,
+                                        None) == m.MOE_W8A8_ERR_INVALID
+    # calibrate, its clip and the router projection
+    w = _weights()
+    assert lib.moe_w8a8_calibrate(ctypes.byref(d), 0.6, FAKE + 1, 4, FAKE, FAKE, FAKE,
+                                  ctypes.byref(w), FAKE, 1 << 40, None) == m.MOE_W8A8_ERR_INVALID
+    assert lib.moe_w8a8_calibrate(ctypes.byref(d), 0.6, FAKE, 4, FAKE + 2, FAKE, FAKE,
+                                  ctypes.byref(w), FAKE, 1 << 40, None) == m.MOE_W8A8_ERR_INVALID
+    assert lib.moe_w8a8_calibrate(ctypes.byref(d), 0.6, FAKE, 4, FAKE, FAKE, FAKE,
+                                  ctypes.byref(w), FAKE + 64, 1 << 40,
+                                  None) == m.MOE_W8A8_ERR_INVALID
+    wq = _weights()
+    wq.w_gate_up = FAKE + 4
+    assert lib.moe_w8a8_calibrate(ctypes.byref(d), 0.6, FAKE, 4, FAKE, FAKE, FAKE,
+                                  ctypes.byref(wq), FAKE, 1 << 40, None) == m.MOE_W8A8_ERR_INVALID
+    assert lib.moe_w8a8_calibrate_clip(ctypes.byref(d), 99.0, FAKE + 1, 4, FAKE, FAKE,
+                                       None) == m.MOE_W8A8_ERR_INVALID
+    assert lib.moe_w8a8_calibrate_clip(ctypes.byref(d), 99.0, FAKE, 4, FAKE, FAKE + 2,
+                                       None) == m.MOE_W8A8_ERR_INVALID
+    dr = m.dims(1024, 512, 8, 2)
+    assert lib.moe_w8a8_router_logits(ctypes.byref(dr), FAKE + 8, 4, FAKE, FAKE, FAKE, 1 << 40,
+                                      None) == m.MOE_W8A8_ERR_INVALID
+    assert lib.moe_w8a8_router_logits(ctypes.byref(dr), FAKE, 4, FAKE + 8, FAKE, FAKE, 1 << 40,
+                                      None) == m.MOE_W8A8_ERR_INVALID

@@ -26,6 +26,20 @@ bool dims_supported(const moe_w8a8_dims *d) {
   return d->hidden % 256 == 0 && d->hidden <= 65536 && d->ffn % 128 == 0 && d->ffn <= 65536 &&
          d->num_experts <= kMaxExperts && d->top_k <= kMaxTopK;
 }
+// p is NULL or a multiple of a bytes.
+bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+// Alignment the kernels rely on (the header's rule): 16 bytes for the arrays
+// they move 16 bytes at a time (tokens, weight codes, inv_smooth, the router
+// matrix), 8 for the output, 4 for the other fp32/int32 arrays, 256 for a
+// workspace (its regions are laid out in 256-byte steps).
+bool fwd_aligned(const moe_w8a8_weights *wt, const uint16_t *x, const float *router_logits,
+                 const int32_t *topk_ids, const float *topk_w, const uint16_t *out,
+                 const void *workspace) {
+  return al(x, 16) && al(out, 8) && al(wt->w_gate_up, 16) && al(wt->w_down, 16) &&
+         al(wt->inv_smooth, 16) && al(wt->w_router, 16) && al(wt->s_gate_up, 4) &&
+         al(wt->s_down, 4) && al(wt->act_clip, 4) && al(router_logits, 4) && al(topk_ids, 4) &&
+         al(topk_w, 4) && al(workspace, 256);
+}
 }  // namespace
 
 FwdLayout fwd_layout(int64_t T, int H, int F, int E, int k) {
@@ -122,6 +136,8 @@ extern "C" int moe_w8a8_router_logits(const moe_w8a8_dims *d, const uint16_t *x,
   if (!dims_valid(d) || T < 0) return MOE_W8A8_ERR_INVALID;
   if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
   if (!x || !w_router || !logits) return MOE_W8A8_ERR_INVALID;
+  if (!al(x, 16) || !al(w_router, 16) || !al(logits, 4) || !al(workspace, 256))
+    return MOE_W8A8_ERR_INVALID;
   if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, E = d->num_experts;
@@ -145,6 +161,7 @@ extern "C" int moe_w8a8_calibrate_clip(const moe_w8a8_dims *d, float percentile,
   if (!dims_valid(d) || !inv_smooth || !act_clip || n_calib < 0 || (n_calib > 0 && !calib_x) ||
       !(percentile > 0.0f && percentile <= 100.0f))
     return MOE_W8A8_ERR_INVALID;
+  if (!al(calib_x, 2) || !al(inv_smooth, 4) || !al(act_clip, 4)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden;
   const int64_t N = n_calib * (int64_t)H;
@@ -164,6 +181,11 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
       !out->inv_smooth)
     return MOE_W8A8_ERR_INVALID;
   if (out->format != MOE_W8A8_FORMAT_INT8 && out->format != MOE_W8A8_FORMAT_FP8)
+    return MOE_W8A8_ERR_INVALID;
+  if (!al(calib_x, 2) || !al(w_gate, 4) || !al(w_up, 4) || !al(w_down, 4) ||
+      !al(out->w_gate_up, 16) || !al(out->w_down, 16) || !al(out->s_gate_up, 4) ||
+      !al(out->s_down, 4) || !al(out->smooth, 4) || !al(out->inv_smooth, 4) ||
+      !al(workspace, 256))
     return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts;
@@ -195,6 +217,8 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
   if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
   if (!x || !out || !wt->w_gate_up || !wt->w_down || !wt->s_gate_up || !wt->s_down ||
       !wt->inv_smooth)
+    return MOE_W8A8_ERR_INVALID;
+  if (!fwd_aligned(wt, x, router_logits, topk_ids, topk_w, out, workspace))
     return MOE_W8A8_ERR_INVALID;
   if (isnan(capacity_factor)) return MOE_W8A8_ERR_INVALID;
   const float sat_p = wt->act_sat_percentile;
@@ -392,6 +416,8 @@ extern "C" int moe_w8a8_forward_noalloc(const moe_w8a8_dims *d, const moe_w8a8_w
   if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   if (moe_w8a8_workspace_size(d, T) > MOE_W8A8_SCRATCH_BYTES) return MOE_W8A8_ERR_SCRATCH;
+  if (!fwd_aligned(wt, x, router_logits, topk_ids, topk_w, out, nullptr))
+    return MOE_W8A8_ERR_INVALID;
   void *ws = nullptr;
   MOE_CHECK(scratch_on_current_device(&ws));
   return forward_impl(d, wt, x, T, router_logits, topk_ids, topk_w, capacity_factor, out, ws,
