@@ -281,6 +281,23 @@ def test_invalid_expert_ids(torch_cuda, T, gemm_path):
     _full_parity(wl, inputs, cal, gemm_path)
 
 
+def test_weights_past_2gib(torch_cuda):
+    """A layer whose gate/up codes pass 2^31 bytes (33 experts, H 8192,
+    F 4096: 2.2 GB, the down codes 1.1 GB), so that every weight and row
+    offset must be 64-bit: every stage against the oracle on both GEMM paths.
+    (A 64-expert layer, 4.3 GB, passed as well.)"""
+    wl = synth.workload("tiny", T=24, E=33, k=8, H=8192, F=4096, layer_seed=31337,
+                        input_seed=31338)
+    _say("[parity] weights past 2 GiB: E=33 H=8192 F=4096 T=24 k=8")
+    layer, cal = _layer_and_cal(wl)
+    assert cal["q_gu"].nbytes > (1 << 31)
+    inputs = synth.make_inputs(wl, layer)
+    del layer
+    for path in (1, 2):
+        _say("[parity] weights past 2 GiB path=%d" % path)
+        _full_parity(wl, inputs, cal, path)
+
+
 def test_two_streams_concurrent(torch_cuda):
     """Two layers (their own weights and workspaces) run on two side streams at
     once, forwards interleaved: every output equals the one each layer gives
