@@ -109,6 +109,10 @@ FORWARD_CASES = {
     "tiny": dict(),                                          # fused small-batch routing
     "mid_route_hist": dict(T=1000, E=8, k=4, H=1024, F=256),  # block routing, 2 parts
     "decode": None,
+    # the largest hidden size (128 partial-sum planes of 512 channels)
+    "max_hidden": dict(H=65536, F=128, E=8, k=2, T=300),
+    # 1024 experts (sixteen per router lane), top-32, block routing
+    "E1024_k32": dict(E=1024, k=32, H=1024, F=128, T=700),
 }
 
 
