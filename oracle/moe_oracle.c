@@ -161,9 +161,17 @@ static void quant_row_fmt(const float *v, int64_t n, int32_t fmt, int8_t *q, flo
   quant_row_fmt_at(v, n, row_absmax(v, n), fmt, q, scale);
 }
 
+/* Decoded value of every FP8 code (oracle_e4m3_value of it), filled once
+ * when the library is loaded, so that a product's operands are looked up
+ * rather than decoded again for every product. */
+static double e4m3_values[256];
+__attribute__((constructor)) static void fill_e4m3_values(void) {
+  for (int c = 0; c < 256; ++c) e4m3_values[c] = oracle_e4m3_value((uint8_t)c);
+}
+
 /* Code value: INT8 codes as integers, FP8 codes decoded. */
 static double code_value(int8_t c, int32_t fmt) {
-  return fmt == 0 ? (double)c : oracle_e4m3_value((uint8_t)c);
+  return fmt == 0 ? (double)c : e4m3_values[(uint8_t)c];
 }
 
 /* Exported forms used by the pins: rows of either format. */
