@@ -17,12 +17,22 @@ Parity bar (what the benchmark spec of the layer fixes):
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 QH_MISMATCH_FRAC = 1e-3
 SH_RTOL = 1e-5
 W_ATOL = 1e-6
 OUT_RMS_FRAC = 2e-2
+
+
+@functools.lru_cache(maxsize=2)
+def layer_of(wl):
+    """synth.make_layer(wl), kept for the next test that draws the same seeded
+    layer (the full-size layers take ~15 s to draw). Callers only read it."""
+    import synth
+    return synth.make_layer(wl)
 
 
 def pack_tiled(w: np.ndarray) -> np.ndarray:

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import synth
-from moe_testlib import check_out, flip_allowance
+from moe_testlib import check_out, flip_allowance, layer_of
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -51,7 +51,7 @@ def test_c_client_matches_binding(tmp_path, over):
     wl = synth.workload("tiny", **over)
     print("[c client] %s" % over, flush=True)
     sys.stdout.flush()
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     inputs = synth.make_inputs(wl, layer)
     d = tmp_path / "io"
     d.mkdir()

@@ -9,7 +9,8 @@ import pytest
 import oracle
 import synth
 from moe_testlib import (bf16_tensor, check_act_quant, check_out, check_requant,
-                         check_routing_and_grouping, flip_allowance, run_gpu, upload_weights)
+                         check_routing_and_grouping, flip_allowance, layer_of, run_gpu,
+                         upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +36,7 @@ def test_clip_threshold_parity(torch_cuda, name):
     import w8a8_int8_expert_amd as m
     wl = synth.workload(name)
     _say("[clip] threshold case=%s n_calib=%d H=%d" % (name, wl.n_calib, wl.H))
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     dev = torch.device("cuda")
     g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
@@ -74,7 +75,7 @@ def clip_full_parity(torch, wl, gemm_path, static, sat_p):
     """The layer with the static clip (at the calibration tokens' 99th percentile)
     and/or dynamic saturation at percentile sat_p, every stage against the oracle."""
     import w8a8_int8_expert_amd as m
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     inputs = synth.make_inputs(wl, layer)
     g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
@@ -124,7 +125,7 @@ def fp8_clip_full_parity(torch, wl, gemm_path, static, sat_p):
     import w8a8_int8_expert_amd as m
     from test_gpu_fp8 import fp8_check, tiled_path
     dev = torch.device("cuda")
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
     inputs = synth.make_inputs(wl, layer)

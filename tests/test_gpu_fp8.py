@@ -39,8 +39,8 @@ import pytest
 
 import oracle
 import synth
-from moe_testlib import (check_act_quant, check_routing_and_grouping, run_gpu, unpack_tiled,
-                         upload_weights)
+from moe_testlib import (check_act_quant, check_routing_and_grouping, layer_of, run_gpu,
+                         unpack_tiled, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +84,7 @@ def test_fp8_calibrate_parity(torch_cuda, name):
     from moe_testlib import bf16_tensor
     wl = synth.workload(name)
     _say("[fp8] calibrate case=%s H=%d F=%d E=%d" % (name, wl.H, wl.F, wl.E))
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
     dev = torch.device("cuda")
@@ -227,7 +227,7 @@ def fp8_full_parity(wl, gemm_path):
     """Every stage of the FP8 layer on workload wl against the oracle, to the
     bars fp8_bounds derives."""
     import w8a8_int8_expert_amd as m
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
     inputs = synth.make_inputs(wl, layer)
@@ -332,7 +332,7 @@ def test_fp8_prefill_sampled_parity(torch_cuda):
     from moe_testlib import rows_of
     wl = synth.workload("prefill")
     _say("[fp8] prefill sampled T=%d" % wl.T)
-    layer = synth.make_layer(synth.workload("decode"))
+    layer = layer_of(synth.workload("decode"))
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha,
                            fmt=oracle.FMT_FP8)
     inputs = synth.make_inputs(wl, layer)

@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import pytest
 
-from moe_testlib import pack_tiled, unpack_tiled
+from moe_testlib import layer_of, pack_tiled, unpack_tiled
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +61,7 @@ def test_stale_hip_error_not_reported(torch_cuda):
     assert np.array_equal(dst.cpu().numpy(), want)
     # a forward of the tiny layer after another pending error
     wl = synth.workload("tiny")
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
     g.calibrate(torch.from_numpy(layer.calib_x.view("int16")).to(dev).view(torch.bfloat16),
                 torch.from_numpy(layer.w_gate).to(dev), torch.from_numpy(layer.w_up).to(dev),

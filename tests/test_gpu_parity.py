@@ -15,8 +15,8 @@ import pytest
 import oracle
 import synth
 from moe_testlib import (OutCheck, QH_MISMATCH_FRAC, SH_RTOL, check_act_quant, check_out,
-                         check_requant, check_routing_and_grouping, flip_allowance, rows_of,
-                         run_gpu, unpack_tiled, upload_weights)
+                         check_requant, check_routing_and_grouping, flip_allowance, layer_of,
+                         rows_of, run_gpu, unpack_tiled, upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +37,11 @@ def torch_cuda():
 
 
 @functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=2)
 def _layer_and_cal(wl: synth.Workload):
-    layer = synth.make_layer(wl)
+    """The seeded layer and its oracle calibration, kept for the next test on
+    the same workload (both only read)."""
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     return layer, cal
 

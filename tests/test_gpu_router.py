@@ -17,7 +17,8 @@ import pytest
 import oracle
 import synth
 from moe_testlib import (bf16_tensor, check_act_quant, check_out, check_requant,
-                         check_routing_and_grouping, flip_allowance, run_gpu, upload_weights)
+                         check_routing_and_grouping, flip_allowance, layer_of, run_gpu,
+                         upload_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +68,7 @@ def test_router_logits_parity(torch_cuda, case):
     wl = synth.workload("decode") if ROUTER_CASES[case] is None else \
         synth.workload("tiny", **ROUTER_CASES[case])
     _say("[router] logits case=%s T=%d H=%d E=%d" % (case, wl.T, wl.H, wl.E))
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     x = synth.make_inputs(wl, layer).x
     w = synth.make_router(wl)
     got = _gpu_logits(torch_cuda, wl, x, w)
@@ -80,7 +81,7 @@ def test_router_logits_independent_of_batch(torch_cuda):
     """A token's logits do not depend on the batch it comes in."""
     wl = synth.workload("decode", T=1000)
     _say("[router] batch independence T=1000 vs 1 and 37")
-    layer = synth.make_layer(synth.workload("decode"))
+    layer = layer_of(synth.workload("decode"))
     x = synth.make_inputs(wl, layer).x
     w = synth.make_router(wl)
     full = _gpu_logits(torch_cuda, wl, x, w)
@@ -132,7 +133,7 @@ def router_full_parity(torch, wl, gemm_path):
     exact ones, the routing decision bit-exact on the GPU's logits, every later stage
     against the oracle routed from them."""
     import w8a8_int8_expert_amd as m
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     inputs = synth.make_inputs(wl, layer)
     w = synth.make_router(wl)

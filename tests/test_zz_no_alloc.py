@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from moe_testlib import bf16_tensor, tensor_bits, upload_weights
+from moe_testlib import bf16_tensor, tensor_bits, upload_weights, layer_of
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def torch_cuda():
 
 def _layer(wl):
     import w8a8_int8_expert_amd as m
-    layer = synth.make_layer(wl)
+    layer = layer_of(wl)
     cal = oracle.calibrate(layer.calib_x, layer.w_gate, layer.w_up, layer.w_down, wl.alpha)
     g = m.MoEW8A8(wl.H, wl.F, wl.E, wl.k)
     upload_weights(g, cal)
