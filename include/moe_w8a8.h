@@ -67,10 +67,10 @@ extern "C" {
  * MOE_W8A8_ERR_INVALID, before anything is enqueued): 16 bytes for arrays the
  * kernels move 16 bytes at a time (the tokens x, the packed weight codes
  * w_gate_up and w_down, inv_smooth when the forward reads it, the router
- * matrix, pack's src and dst), 8 bytes for the forward's output, the natural
- * alignment of the element type for every other array, and 256 bytes for a
- * workspace (its regions are laid out in 256-byte steps). hipMalloc and
- * torch allocations satisfy all of them. */
+ * matrix, pack's src and dst, the debug accumulators acc1), 8 bytes for the
+ * forward's output, the natural alignment of the element type for every other
+ * array, and 256 bytes for a workspace (its regions are laid out in 256-byte
+ * steps). hipMalloc and torch allocations satisfy all of them. */
 
 /* Layer dimensions. Supported set: hidden H a multiple of 256 in [256, 65536];
  * ffn F a multiple of 128 in [128, 65536]; 1 <= num_experts E <= 1024;

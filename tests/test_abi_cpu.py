@@ -299,6 +299,12 @@ def test_misaligned_pointers_refused(lib):
         wt = _weights()
         setattr(wt, field, FAKE + off)
         assert _fwd(d, weights=wt) == m.MOE_W8A8_ERR_INVALID, field
+    dbg = m.moe_w8a8_debug()
+    dbg.acc1 = FAKE + 4
+    assert _fwd(d, dbg=dbg) == m.MOE_W8A8_ERR_INVALID
+    dbg = m.moe_w8a8_debug()
+    dbg.row_of = FAKE + 2
+    assert _fwd(d, dbg=dbg) == m.MOE_W8A8_ERR_INVALID
     # the same checks come before the no-allocation forward touches the GPU
     assert lib.moe_w8a8_forward_noalloc(ctypes.byref(d), ctypes.byref(_weights()), FAKE + 8, 4,
                                         FAKE, None, None, 0.0, FAKE, None,

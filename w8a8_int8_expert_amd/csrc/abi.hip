@@ -227,6 +227,12 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
     return MOE_W8A8_ERR_INVALID;
   const bool fp8 = wt->format == MOE_W8A8_FORMAT_FP8;
   if (dbg && (dbg->gemm_path < 0 || dbg->gemm_path > 2)) return MOE_W8A8_ERR_INVALID;
+  // the streaming GEMM1 writes the debug accumulators 16 bytes at a time
+  if (dbg && (!al(dbg->acc1, 16) || !al(dbg->topk_ids, 4) || !al(dbg->topk_w, 4) ||
+              !al(dbg->expert_counts, 4) || !al(dbg->expert_offsets, 4) ||
+              !al(dbg->sorted_assign, 4) || !al(dbg->row_of, 4) || !al(dbg->sx, 4) ||
+              !al(dbg->h, 4) || !al(dbg->sh, 4) || !al(dbg->y, 4) || !al(dbg->router_logits, 4)))
+    return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts, k = d->top_k;
   ActClip ac{wt->act_clip, 0};
