@@ -200,7 +200,8 @@ typedef struct {
  * pool instead of allocating per call); the library allocates nothing.
  * A pure function of the arguments, nondecreasing in T (a workspace sized for
  * the largest batch serves every smaller one); returns 0 for invalid or
- * unsupported dimensions or T < 0. */
+ * unsupported dimensions, T < 0, or a batch past the row limit of
+ * moe_w8a8_forward. */
 size_t moe_w8a8_workspace_size(const moe_w8a8_dims *dims, int64_t T);
 
 /* Calibrate and quantise the layer weights ("MiniMax-M3 W8A8 inference on
@@ -264,7 +265,8 @@ int moe_w8a8_calibrate_clip(const moe_w8a8_dims *dims, float percentile,
  *   debug       NULL, or a host struct of optional device outputs (above).
  * T == 0 is a successful no-op whatever the other pointers are (empty
  * tensors may carry NULL addresses). Errors: MOE_W8A8_ERR_INVALID (NULL required
- * pointer, T < 0, T*k >= 2^31, routing inputs as above, act_sat_percentile
+ * pointer, T < 0, T*k >= 2^31 or T*k + 15*min(T*k, E) >= 2^31 (the permuted
+ * rows with every expert group padded to 16), routing inputs as above, act_sat_percentile
  * outside {0} and (0, 100]), MOE_W8A8_ERR_UNSUPPORTED (also a saturation
  * rank m > 16), MOE_W8A8_ERR_WORKSPACE, MOE_W8A8_ERR_HIP. */
 int moe_w8a8_forward(const moe_w8a8_dims *dims, const moe_w8a8_weights *weights,

@@ -74,6 +74,31 @@ def test_workspace_size_pure(lib):
     assert m.moe_w8a8_workspace_size(m.dims(4096, 1536, 2048, 8), 1) == 0   # E > 1024
 
 
+def test_row_limit_without_overflow(lib):
+    """A batch is refused once T*k or the padded row count T*k + 15*min(T*k, E)
+    reaches 2^31, exactly at that boundary, and a T whose T*k overflows int64
+    is refused too (workspace size 0, forward and router INVALID, nothing
+    launched)."""
+    lim = (1 << 31) - 1
+    d = m.dims(256, 128, 1, 1)          # E = 1: padding adds at most 15 rows
+    assert m.moe_w8a8_workspace_size(d, lim - 15) > 0
+    assert m.moe_w8a8_workspace_size(d, lim - 14) == 0
+    d = m.dims(256, 128, 1024, 1)       # E = 1024: up to 15360 padding rows
+    assert m.moe_w8a8_workspace_size(d, lim - 15 * 1024) > 0
+    assert m.moe_w8a8_workspace_size(d, lim - 15 * 1024 + 1) == 0
+    d = m.dims(256, 128, 64, 32)
+    t = (lim - 15 * 64) // 32
+    assert m.moe_w8a8_workspace_size(d, t) > 0
+    assert m.moe_w8a8_workspace_size(d, t + 1) == 0
+    for T in ((1 << 62), (1 << 63) - 1, (1 << 63) // 32 + 1):
+        assert m.moe_w8a8_workspace_size(d, T) == 0
+        assert _fwd(d, T=T, ws_bytes=(1 << 63) - 1) == m.MOE_W8A8_ERR_INVALID
+        assert m.moe_w8a8_router_logits(d, FAKE, T, FAKE, FAKE, FAKE, 1 << 62,
+                                        stream=0) == m.MOE_W8A8_ERR_INVALID
+        assert m.moe_w8a8_forward_noalloc(d, _weights(), FAKE, T, FAKE, None, None, 0.0, FAKE,
+                                          None, stream=0) == m.MOE_W8A8_ERR_INVALID
+
+
 def _weights():
     return m.moe_w8a8_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
 

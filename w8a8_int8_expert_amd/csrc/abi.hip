@@ -26,6 +26,16 @@ bool dims_supported(const moe_w8a8_dims *d) {
   return d->hidden % 256 == 0 && d->hidden <= 65536 && d->ffn % 128 == 0 && d->ffn <= 65536 &&
          d->num_experts <= kMaxExperts && d->top_k <= kMaxTopK;
 }
+// The kernels index assignments and permuted rows in int32: refuse a batch
+// whose T*k, or whose padded row count T*k + 15*min(T*k, E) (each expert group
+// rounded up to 16 rows), reaches 2^31. T*k is bounded by a division first, so
+// no product can overflow int64 for a huge T.
+bool too_many_rows(int64_t T, int k, int E) {
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  if (T > lim / k) return true;
+  const int64_t A = T * k;
+  return A + 15 * (A < E ? A : (int64_t)E) > lim;
+}
 // p is NULL or a multiple of a bytes.
 bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 // Alignment the kernels rely on (the header's rule): 16 bytes for the arrays
@@ -93,7 +103,7 @@ using namespace moe;
 
 extern "C" size_t moe_w8a8_workspace_size(const moe_w8a8_dims *d, int64_t T) {
   if (!dims_valid(d) || !dims_supported(d) || T < 0) return 0;
-  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return 0;
+  if (too_many_rows(T, d->top_k, d->num_experts)) return 0;
   const size_t f = fwd_layout(T, d->hidden, d->ffn, d->num_experts, d->top_k).total;
   const size_t c = calib_ws_bytes(d->hidden);
   return f > c ? f : c;
@@ -138,7 +148,7 @@ extern "C" int moe_w8a8_router_logits(const moe_w8a8_dims *d, const uint16_t *x,
   if (!x || !w_router || !logits) return MOE_W8A8_ERR_INVALID;
   if (!al(x, 16) || !al(w_router, 16) || !al(logits, 4) || !al(workspace, 256))
     return MOE_W8A8_ERR_INVALID;
-  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (too_many_rows(T, d->top_k, d->num_experts)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, E = d->num_experts;
   const int parts = router_parts(H);
@@ -214,7 +224,7 @@ int forward_impl(const moe_w8a8_dims *d, const moe_w8a8_weights *wt, const uint1
   const bool project = !routed && !pre;
   if ((routed && pre) || (pre && (!topk_ids || !topk_w)) || (project && !wt->w_router))
     return MOE_W8A8_ERR_INVALID;
-  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (too_many_rows(T, d->top_k, d->num_experts)) return MOE_W8A8_ERR_INVALID;
   if (!x || !out || !wt->w_gate_up || !wt->w_down || !wt->s_gate_up || !wt->s_down ||
       !wt->inv_smooth)
     return MOE_W8A8_ERR_INVALID;
@@ -419,7 +429,7 @@ extern "C" int moe_w8a8_forward_noalloc(const moe_w8a8_dims *d, const moe_w8a8_w
                                         const moe_w8a8_debug *dbg, void *stream) {
   if (!dims_valid(d) || !wt || T < 0) return MOE_W8A8_ERR_INVALID;
   if (T == 0) return dims_supported(d) ? MOE_W8A8_OK : MOE_W8A8_ERR_UNSUPPORTED;
-  if (T * (int64_t)d->top_k >= (int64_t)1 << 31) return MOE_W8A8_ERR_INVALID;
+  if (too_many_rows(T, d->top_k, d->num_experts)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   if (moe_w8a8_workspace_size(d, T) > MOE_W8A8_SCRATCH_BYTES) return MOE_W8A8_ERR_SCRATCH;
   if (!fwd_aligned(wt, x, router_logits, topk_ids, topk_w, out, nullptr))
