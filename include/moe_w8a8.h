@@ -220,7 +220,7 @@ size_t moe_w8a8_workspace_size(const moe_w8a8_dims *dims, int64_t T);
  * scale = a/127 (an all-zero row gets scale 0 and codes 0).
  * Workspace: at least moe_w8a8_workspace_size(dims, 0) bytes.
  * Errors: MOE_W8A8_ERR_INVALID (NULL pointer, alpha outside [0,1],
- * n_calib < 0), MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE,
+ * n_calib < 0 or n_calib * H >= 2^61), MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_WORKSPACE,
  * MOE_W8A8_ERR_HIP. */
 int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
                        const uint16_t *calib_x, int64_t n_calib,
@@ -236,7 +236,8 @@ int moe_w8a8_calibrate(const moe_w8a8_dims *dims, float alpha,
  * [1, N]) in ascending order; 0 when n_calib = 0.
  *   percentile in (0, 100]; calib_x bf16 [n_calib][H]; inv_smooth fp32 [H]
  *   (from moe_w8a8_calibrate); act_clip fp32 [1]. All device memory.
- * Errors: MOE_W8A8_ERR_INVALID, MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_HIP. */
+ * Errors: MOE_W8A8_ERR_INVALID (also n_calib * H >= 2^61),
+ * MOE_W8A8_ERR_UNSUPPORTED, MOE_W8A8_ERR_HIP. */
 int moe_w8a8_calibrate_clip(const moe_w8a8_dims *dims, float percentile,
                             const uint16_t *calib_x, int64_t n_calib,
                             const float *inv_smooth, float *act_clip, void *stream);

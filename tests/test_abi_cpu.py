@@ -173,6 +173,8 @@ def test_calibrate_validation(lib):
     assert cal(alpha=1.5) == m.MOE_W8A8_ERR_INVALID
     assert cal(alpha=float("nan")) == m.MOE_W8A8_ERR_INVALID
     assert cal(n=-1) == m.MOE_W8A8_ERR_INVALID
+    for n in ((1 << 61) // 256, (1 << 62), (1 << 63) - 1):       # n_calib * H >= 2^61
+        assert cal(n=n) == m.MOE_W8A8_ERR_INVALID
     assert cal(cx=None) == m.MOE_W8A8_ERR_INVALID
     bad = _weights()
     bad.smooth = None
@@ -196,6 +198,9 @@ def test_calibrate_clip_validation(lib):
     assert cc(inv=None) == m.MOE_W8A8_ERR_INVALID
     assert cc(out=None) == m.MOE_W8A8_ERR_INVALID
     assert cc(d=m.dims(320, 512, 8, 2)) == m.MOE_W8A8_ERR_UNSUPPORTED
+    # n_calib * H >= 2^61, including counts whose product overflows int64
+    for n in ((1 << 61) // 256, (1 << 62), (1 << 63) - 1):
+        assert cc(n=n) == m.MOE_W8A8_ERR_INVALID
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -36,6 +36,9 @@ bool too_many_rows(int64_t T, int k, int E) {
   const int64_t A = T * k;
   return A + 15 * (A < E ? A : (int64_t)E) > lim;
 }
+// More calibration tokens than any device holds: n_calib * H >= 2^61 values
+// (2^62 bytes of bf16), decided without forming the product.
+bool too_many_calib(int64_t n_calib, int H) { return n_calib > ((int64_t)1 << 61) / H - 1; }
 // p is NULL or a multiple of a bytes.
 bool al(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 // Alignment the kernels rely on (the header's rule): 16 bytes for the arrays
@@ -172,6 +175,7 @@ extern "C" int moe_w8a8_calibrate_clip(const moe_w8a8_dims *d, float percentile,
       !(percentile > 0.0f && percentile <= 100.0f))
     return MOE_W8A8_ERR_INVALID;
   if (!al(calib_x, 2) || !al(inv_smooth, 4) || !al(act_clip, 4)) return MOE_W8A8_ERR_INVALID;
+  if (too_many_calib(n_calib, d->hidden)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden;
   const int64_t N = n_calib * (int64_t)H;
@@ -197,6 +201,7 @@ extern "C" int moe_w8a8_calibrate(const moe_w8a8_dims *d, float alpha, const uin
       !al(out->s_down, 4) || !al(out->smooth, 4) || !al(out->inv_smooth, 4) ||
       !al(workspace, 256))
     return MOE_W8A8_ERR_INVALID;
+  if (too_many_calib(n_calib, d->hidden)) return MOE_W8A8_ERR_INVALID;
   if (!dims_supported(d)) return MOE_W8A8_ERR_UNSUPPORTED;
   const int H = d->hidden, F = d->ffn, E = d->num_experts;
   if (!workspace || workspace_bytes < calib_ws_bytes(H)) return MOE_W8A8_ERR_WORKSPACE;
