@@ -251,6 +251,49 @@ def test_binding_rejects_mismatched_tensors(lib):
             g.forward(x.cuda(), router_logits=lg)
 
 
+def test_binding_calls_on_the_layers_device(lib, monkeypatch):
+    """Every method of the binding calls into the library inside the layer's
+    device context (the library launches on the current device and torch's
+    current stream of it). The library entry points and the context are
+    replaced by recorders: nothing runs on a device."""
+    import contextlib
+    import torch
+    H, F, E, k, T = 256, 128, 8, 2, 5
+    g = m.MoEW8A8(H, F, E, k, device="cpu")
+    depth = [0]
+    seen = []
+
+    @contextlib.contextmanager
+    def on_device():
+        depth[0] += 1
+        try:
+            yield
+        finally:
+            depth[0] -= 1
+    monkeypatch.setattr(g, "_on_device", on_device)
+    for name in ("moe_w8a8_forward", "moe_w8a8_forward_noalloc", "moe_w8a8_calibrate",
+                 "moe_w8a8_calibrate_clip", "moe_w8a8_router_logits", "moe_w8a8_pack"):
+        def rec(*a, _name=name, **kw):
+            seen.append((_name, depth[0]))
+            return m.MOE_W8A8_OK
+        monkeypatch.setattr(m, name, rec)
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    lg = torch.zeros(T, E, dtype=torch.float32)
+    g.forward(x, router_logits=lg)
+    g.forward_noalloc(x, torch.empty(T, H, dtype=torch.bfloat16), router_logits=lg)
+    g.calibrate(x, torch.zeros(E, F, H), torch.zeros(E, F, H), torch.zeros(E, H, F), 0.6)
+    g.calibrate_clip(x, 99.9)
+    g.set_router(torch.zeros(E, H, dtype=torch.bfloat16))
+    g.router_logits(x)
+    g.load_quantized(torch.zeros(E, 2 * F, H, dtype=torch.int8), torch.ones(E, 2 * F),
+                     torch.zeros(E, H, F, dtype=torch.int8), torch.ones(E, H), torch.ones(H),
+                     torch.ones(H))
+    assert [n for n, _ in seen] == ["moe_w8a8_forward", "moe_w8a8_forward_noalloc",
+                                    "moe_w8a8_calibrate", "moe_w8a8_calibrate_clip",
+                                    "moe_w8a8_router_logits", "moe_w8a8_pack", "moe_w8a8_pack"]
+    assert all(d == 1 for _, d in seen), seen
+
+
 def test_pack_validation(lib):
     """moe_w8a8_pack refuses bad sizes, NULL, misaligned or overlapping buffers
     before anything is enqueued."""

@@ -185,7 +185,13 @@ def _check(rc: int, what: str):
 
 
 class MoEW8A8:
-    """Quantised layer on one device (torch tensors for memory and streams)."""
+    """Quantised layer on one device (torch tensors for memory and streams).
+    Every library call is made with the layer's device current, on torch's
+    current stream of that device, whichever device was current before.
+    The layer owns one workspace, allocated on the stream current at its first
+    use and replaced when a larger batch needs more: calls on one layer must
+    not overlap on different streams (give each stream a layer of its own, as
+    the weights may be shared, or synchronise between the streams)."""
 
     def __init__(self, hidden: int, ffn: int, num_experts: int, top_k: int, device="cuda",
                  fp8: bool = False):
@@ -211,6 +217,12 @@ class MoEW8A8:
         self.act_clip = torch.zeros(1, dtype=torch.float32, **kw)
         self._ws = None
 
+    def _on_device(self):
+        """Context in which the layer's device is current: the library launches
+        on the current device, on torch's current stream of that device."""
+        import torch
+        return torch.cuda.device(self.device)
+
     def _expect(self, t, name, dtype, shape):
         """Raise MoEW8A8Error unless t is a contiguous tensor of this dtype and
         shape on the layer's device (the C ABI reads raw pointers)."""
@@ -232,8 +244,10 @@ class MoEW8A8:
         smoothed values (after calibrate); forward then uses it."""
         import torch
         self._expect(calib_x, "calib_x", torch.bfloat16, (calib_x.shape[0], self.d.hidden))
-        _check(moe_w8a8_calibrate_clip(self.d, percentile, calib_x, calib_x.shape[0],
-                                       self.inv_smooth, self.act_clip), "moe_w8a8_calibrate_clip")
+        with self._on_device():
+            _check(moe_w8a8_calibrate_clip(self.d, percentile, calib_x, calib_x.shape[0],
+                                           self.inv_smooth, self.act_clip),
+                   "moe_w8a8_calibrate_clip")
         self.weights.act_clip = self.act_clip.data_ptr()
 
     def set_clip(self, static: bool = False, sat_percentile: float = 0.0):
@@ -266,8 +280,9 @@ class MoEW8A8:
             out = torch.empty(T, self.d.num_experts, dtype=torch.float32, device=self.device)
         self._expect(out, "out", torch.float32, (T, self.d.num_experts))
         ws = self.workspace(T)
-        _check(moe_w8a8_router_logits(self.d, x, T, self.w_router, out, ws, ws.numel()),
-               "moe_w8a8_router_logits")
+        with self._on_device():
+            _check(moe_w8a8_router_logits(self.d, x, T, self.w_router, out, ws, ws.numel()),
+                   "moe_w8a8_router_logits")
         return out
 
     def load_quantized(self, q_gate_up, s_gate_up, q_down, s_down, smooth, inv_smooth):
@@ -284,8 +299,9 @@ class MoEW8A8:
         self._expect(s_down, "s_down", torch.float32, (E, H))
         self._expect(smooth, "smooth", torch.float32, (H,))
         self._expect(inv_smooth, "inv_smooth", torch.float32, (H,))
-        _check(moe_w8a8_pack(E, 2 * F, H, q_gate_up, self.w_gate_up), "moe_w8a8_pack")
-        _check(moe_w8a8_pack(E, H, F, q_down, self.w_down), "moe_w8a8_pack")
+        with self._on_device():
+            _check(moe_w8a8_pack(E, 2 * F, H, q_gate_up, self.w_gate_up), "moe_w8a8_pack")
+            _check(moe_w8a8_pack(E, H, F, q_down, self.w_down), "moe_w8a8_pack")
         self.s_gate_up.copy_(s_gate_up)
         self.s_down.copy_(s_down)
         self.smooth.copy_(smooth)
@@ -309,8 +325,9 @@ class MoEW8A8:
         self._expect(w_up, "w_up", torch.float32, (E, F, H))
         self._expect(w_down, "w_down", torch.float32, (E, H, F))
         ws = self.workspace(0)
-        _check(moe_w8a8_calibrate(self.d, alpha, calib_x, calib_x.shape[0], w_gate, w_up, w_down,
-                                  self.weights, ws, ws.numel()), "moe_w8a8_calibrate")
+        with self._on_device():
+            _check(moe_w8a8_calibrate(self.d, alpha, calib_x, calib_x.shape[0], w_gate, w_up,
+                                      w_down, self.weights, ws, ws.numel()), "moe_w8a8_calibrate")
 
     def forward(self, x, router_logits=None, topk_ids=None, topk_w=None,
                 capacity_factor: float = 0.0, out=None, debug: Optional[moe_w8a8_debug] = None):
@@ -320,8 +337,10 @@ class MoEW8A8:
         T = x.shape[0]
         out = self._check_forward_args(x, router_logits, topk_ids, topk_w, out)
         ws = self.workspace(T)
-        _check(moe_w8a8_forward(self.d, self.weights, x, T, router_logits, topk_ids, topk_w,
-                                capacity_factor, out, ws, ws.numel(), debug), "moe_w8a8_forward")
+        with self._on_device():
+            _check(moe_w8a8_forward(self.d, self.weights, x, T, router_logits, topk_ids, topk_w,
+                                    capacity_factor, out, ws, ws.numel(), debug),
+                   "moe_w8a8_forward")
         return out
 
     def forward_noalloc(self, x, out, router_logits=None, topk_ids=None, topk_w=None,
@@ -332,9 +351,10 @@ class MoEW8A8:
         if out is None:
             raise MoEW8A8Error("forward_noalloc needs a caller-given out tensor")
         out = self._check_forward_args(x, router_logits, topk_ids, topk_w, out)
-        _check(moe_w8a8_forward_noalloc(self.d, self.weights, x, T, router_logits, topk_ids,
-                                        topk_w, capacity_factor, out, debug),
-               "moe_w8a8_forward_noalloc")
+        with self._on_device():
+            _check(moe_w8a8_forward_noalloc(self.d, self.weights, x, T, router_logits, topk_ids,
+                                            topk_w, capacity_factor, out, debug),
+                   "moe_w8a8_forward_noalloc")
         return out
 
     def _check_forward_args(self, x, router_logits, topk_ids, topk_w, out):
