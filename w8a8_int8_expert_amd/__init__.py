@@ -190,8 +190,8 @@ class MoEW8A8:
     current stream of that device, whichever device was current before.
     The layer owns one workspace, allocated on the stream current at its first
     use and replaced when a larger batch needs more: calls on one layer must
-    not overlap on different streams (give each stream a layer of its own, as
-    the weights may be shared, or synchronise between the streams)."""
+    not overlap on different streams (give each stream a layer of its own, or
+    synchronise between the streams)."""
 
     def __init__(self, hidden: int, ffn: int, num_experts: int, top_k: int, device="cuda",
                  fp8: bool = False):
