@@ -1,0 +1,240 @@
+"""End-to-end pin of the oracle: on inputs that every quantiser of the layer
+represents exactly, the W8A8 layer must equal the plain dense MoE FFN in fp64,
+to the last bit of its fp64 sum and of its bf16 output.
+
+The inputs are built so that no step of the quantised path loses anything:
+  - SmoothQuant ("MiniMax-M3 W8A8 inference on K100AI" §3.2, alpha = 0.5):
+    per-channel activation and weight ranges are powers of 4, so every s_j is
+    an exact power of 2 and smoothing only moves exponents;
+  - the per-token and per-output-channel quantisers ("... K100AI" §1.2,
+    §3.2): every row's largest magnitude is 127 * 2^p, so 127/amax and the
+    scale are exact and the row's codes are its integer values;
+  - SwiGLU: every gate value is at least 40, where 1 + exp(-g) rounds to 1
+    in fp64 and silu(g) = g exactly;
+  - the requantisation of h ("... K100AI" §4.3): the up projection of each
+    expert reads the token through one anchor channel that is 127 in every
+    token, so h_f = g * 127 * n_f * 2^e with integer n_f and some |n_f| = 127:
+    the row maximum is 127 * (g * 127 * 2^e) and the codes are the n_f;
+  - every product and sum stays within 24 (fp32) and 53 (fp64) significant
+    bits.
+Channels 6 and 7 are zero in every token and carry the 127 of the gate and up
+rows, so those rows have their maximum where it does not touch the sums. A
+fifth expert is never routed; it holds each channel's weight range, which
+fixes s.
+
+The reference uses nothing of the oracle: top-k by (logit descending, index
+ascending) with softmax weights renormalised over the chosen experts
+("超大规模模型推理的Day0适配实践" §四), the first C = ceil(cf*T*k/E)
+assignments of each expert in (token, slot) order (§二.2), and
+out[t] = sum_j w[t][j] * W_down[e] (silu(W_gate[e] x_t) * (W_up[e] x_t)) in
+fp64 from the unquantised tensors. A wrong scale, a weight on the wrong slot,
+a transposed operand, gate and up swapped, a lost capacity drop or a wrong
+permutation changes the result. The planted codes (qx, q_gu, q_d, qh) and the
+exact scales are checked stage by stage as well.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import f32_to_bf16_bits
+from test_oracle_pins import _bf16_nearest_bruteforce
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+H, F, E, K, T = 8, 4, 5, 2, 6
+ROUTED = 4          # experts 0..3; expert 4 only carries the weight ranges
+ALPHA = 0.5
+ANCHOR, GATE_PAD, UP_PAD = 0, 6, 7
+
+
+def _pow2(e):
+    return float(2.0 ** e)
+
+
+def _reference_route(logits):
+    """Top-k with ties to the lower index; softmax renormalised over the k."""
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:K]
+        ids[t] = order
+        ex = np.array([math.exp(float(logits[t, e]) - float(logits[t, order[0]]))
+                       for e in order])
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
+def _reference_keep(ids, cf):
+    """The first C assignments of each expert in (token, slot) order."""
+    keep = np.ones((T, K), bool)
+    if cf <= 0:
+        return keep
+    C = math.ceil(cf * T * K / E)
+    seen = np.zeros(E, int)
+    for t in range(T):
+        for j in range(K):
+            e = ids[t, j]
+            keep[t, j] = seen[e] < C
+            seen[e] += 1
+    return keep
+
+
+def _reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up=False):
+    """Dense MoE FFN in fp64 on the unquantised tensors."""
+    out = np.zeros((T, H))
+    for t in range(T):
+        for j in range(K):
+            if not keep[t, j]:
+                continue
+            e = ids[t, j]
+            g = wg[e].astype(np.float64) @ x[t]
+            u = wu[e].astype(np.float64) @ x[t]
+            if swap_gate_up:
+                g, u = u, g
+            h = g / (1.0 + np.exp(-g)) * u
+            wj = w[t, K - 1 - j] if swap_slots else w[t, j]
+            out[t] += float(wj) * (wd[e].astype(np.float64) @ h)
+    return out
+
+
+def _build(seed):
+    """One lossless case: tensors, the planted codes and exponents, logits."""
+    rng = np.random.default_rng([4242, seed])
+    b = rng.integers(-1, 3, size=H)                 # s_j = 2^b_j
+    a = rng.integers(5, 7, size=H)                  # weight range aw_j = 4^a_j
+    aw = np.array([4.0 ** int(v) for v in a])
+    ax = np.array([4.0 ** int(a[j] + b[j]) for j in range(H)])
+    calib = np.stack([ax * rng.choice([-1, 1], size=H), ax / 2 * rng.choice([-1, 1], size=H)])
+    s = np.array([_pow2(int(v)) for v in b])
+
+    # tokens: integer codes d with d[ANCHOR] = 127, zero padding channels
+    m = rng.integers(-1, 2, size=T)
+    d = rng.integers(-127, 128, size=(T, H))
+    d[:, ANCHOR] = 127
+    d[:, GATE_PAD] = 0
+    d[:, UP_PAD] = 0
+    x = (d * np.array([_pow2(int(v)) for v in m])[:, None]) * s[None, :]
+    x32 = x.astype(np.float32)
+    assert np.array_equal(x32.astype(np.float64), x)
+    x_bits = f32_to_bf16_bits(x32)
+    assert np.array_equal(x_bits.astype(np.uint32) << 16, x32.view(np.uint32)), "x not bf16"
+
+    # routing, fixed before the gate rows so that every pair used can be checked
+    logits = np.zeros((T, E), np.float32)
+    for t in range(T):
+        A, B = sorted(rng.choice(ROUTED, size=2, replace=False))
+        L = np.float32(rng.integers(-8, 9) / 4)
+        logits[t] = L - np.float32(1 + rng.integers(0, 4, size=E))
+        logits[t, A] = logits[t, B] = L
+        if rng.random() < 0.5:      # a higher index tied at the top: it must lose
+            logits[t, 4] = L
+    pre_ids = np.stack([rng.permutation(ROUTED)[:K] for _ in range(T)]).astype(np.int32)
+    pre_w = (rng.integers(1, 9, size=(T, K)) / 8).astype(np.float32)
+
+    r_ids, _ = _reference_route(logits)
+    pairs = {(t, int(e)) for t in range(T) for e in r_ids[t]} | \
+            {(t, int(e)) for t in range(T) for e in pre_ids[t]}
+
+    wg = np.zeros((E, F, H), np.float32)
+    wu = np.zeros((E, F, H), np.float32)
+    wd = np.zeros((E, H, F), np.float32)
+    plan = {}
+    for e in range(ROUTED):
+        pg, pu, pr = (int(v) for v in rng.integers(-1, 2, size=3))
+        for _ in range(1000):
+            cg = np.zeros(H, np.int64)
+            cg[ANCHOR] = rng.integers(2, 4)
+            live = rng.choice(np.arange(1, GATE_PAD), size=2, replace=False)
+            cg[live] = rng.choice([-1, 1], size=2)
+            cg[GATE_PAD] = 127
+            acc_g = {t: int(d[t] @ cg) for t in range(T) if (t, e) in pairs}
+            if all(v * _pow2(int(m[t]) + pg) >= 40 for t, v in acc_g.items()):
+                break
+        else:
+            raise AssertionError("no gate row with every gate value >= 40")
+        n = rng.integers(-127, 128, size=F)
+        n[rng.integers(F)] = 127 * rng.choice([-1, 1])
+        cu = np.zeros((F, H), np.int64)
+        cu[:, ANCHOR] = n
+        cu[:, UP_PAD] = 127
+        cd = rng.integers(-127, 128, size=(H, F))
+        cd[np.arange(H), rng.integers(0, F, size=H)] = 127 * rng.choice([-1, 1], size=H)
+        # smoothed rows are 2^p * codes; the stored weights divide by s
+        wg[e] = (_pow2(pg) * cg[None, :] / s[None, :]).astype(np.float32)
+        wu[e] = (_pow2(pu) * cu / s[None, :]).astype(np.float32)
+        wd[e] = (_pow2(pr) * cd).astype(np.float32)
+        plan[e] = dict(pg=pg, pu=pu, pr=pr, cg=cg, n=n, cu=cu, cd=cd, acc_g=acc_g)
+    # the never-routed expert attains each channel's weight range
+    wg[ROUTED, 0] = (aw * rng.choice([-1, 1], size=H)).astype(np.float32)
+    wu[ROUTED] = rng.uniform(-1, 1, size=(F, H)).astype(np.float32)
+    wd[ROUTED] = rng.uniform(-1, 1, size=(H, F)).astype(np.float32)
+    for j in range(H):
+        assert np.abs(np.concatenate([wg[:, :, j], wu[:, :, j]])).max() == aw[j]
+        assert np.abs(calib[:, j]).max() == ax[j]
+    calib_bits = f32_to_bf16_bits(calib.astype(np.float32))
+    return dict(x=x, x_bits=x_bits, d=d, m=m, s=s, calib_bits=calib_bits, wg=wg, wu=wu, wd=wd,
+                plan=plan, logits=logits, pre_ids=pre_ids, pre_w=pre_w)
+
+
+MODES = ["logits", "capacity", "pre_routed"]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("seed", range(6))
+def test_lossless_layer_equals_dense_ffn(seed, mode):
+    c = _build(seed)
+    cal = oracle.calibrate(c["calib_bits"], c["wg"], c["wu"], c["wd"], ALPHA)
+    # calibration: exact s, the planted codes and power-of-2 scales
+    assert np.array_equal(cal["s"].astype(np.float64), c["s"])
+    assert np.array_equal(cal["inv_s"].astype(np.float64), 1.0 / c["s"])
+    for e, p in c["plan"].items():
+        assert np.array_equal(cal["q_gu"][e, :F], np.tile(p["cg"], (F, 1)))
+        assert np.array_equal(cal["q_gu"][e, F:], p["cu"])
+        assert np.array_equal(cal["q_d"][e], p["cd"])
+        assert np.all(cal["sw_gu"][e, :F] == _pow2(p["pg"]))
+        assert np.all(cal["sw_gu"][e, F:] == _pow2(p["pu"]))
+        assert np.all(cal["sw_d"][e] == _pow2(p["pr"]))
+
+    cf = 0.75 if mode == "capacity" else 0.0     # C = ceil(0.75 * 12 / 5) = 2
+    if mode == "pre_routed":
+        ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
+        o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"])
+    else:
+        ids, w = _reference_route(c["logits"])
+        o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf)
+        assert np.array_equal(o["ids"], ids)
+        assert np.array_equal(o["w"].astype(np.float64), w)     # ties: exactly 1/2
+        assert np.all(w == 0.5) and np.all(ids < ROUTED)
+    keep = _reference_keep(ids, cf)
+    assert np.array_equal(o["row_of"] >= 0, keep)
+    if mode == "capacity":
+        assert not keep.all()
+
+    # token codes and scales are the planted ones
+    assert np.array_equal(o["qx"], c["d"])
+    assert np.array_equal(o["sx"].astype(np.float64), [_pow2(int(v)) for v in c["m"]])
+    # every kept row requantises to its expert's n_f, with the exact scale
+    for i in range(o["kept"]):
+        a = int(o["sorted"][i])
+        t, e = a // K, int(o["ids"].reshape(-1)[a])
+        p = c["plan"][e]
+        assert np.array_equal(o["qh"][i], p["n"])
+        expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
+        assert float(o["sh"][i]) == p["acc_g"][t] * 127 * _pow2(expo)
+
+    ref = _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids, w, keep)
+    assert np.array_equal(o["out_exact"], ref), np.abs(o["out_exact"] - ref).max()
+    want = np.array([[_bf16_nearest_bruteforce(float(v)) for v in row] for row in ref], np.uint16)
+    assert np.array_equal(o["out"], want)
+
+    # the pin has power: plausible slips in the layer change the result
+    assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids, w,
+                                                    keep, swap_gate_up=True))
+    if mode == "pre_routed":
+        assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids,
+                                                        w, keep, swap_slots=True))
+    if mode == "capacity":
+        assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids,
+                                                        w, np.ones_like(keep)))

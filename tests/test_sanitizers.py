@@ -38,7 +38,7 @@ def test_oracle_pins_under_asan_ubsan():
                         os.path.join(ROOT, "oracle", "moe_oracle.c"), "-o", lib, "-lm"],
                        check=True)
         out = _run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                    "tests/test_oracle_pins.py"],
+                    "tests/test_oracle_pins.py", "tests/test_oracle_exact_layer.py"],
                    {"LD_PRELOAD": libasan, "MOE_ORACLE_LIB": lib})
     assert " passed" in out
 
