@@ -248,7 +248,9 @@ int moe_w8a8_calibrate_clip(const moe_w8a8_dims *dims, float percentile,
  *   router_logits fp32 [T][E] given; or
  *   topk_ids    int32 [T][k] and topk_w fp32 [T][k] (pre-routed mode): the
  *               assignments and their weights (ids outside [0, E) are treated
- *               as dropped; the weights are used as given); or
+ *               as dropped; the weights are used as given; an expert named in
+ *               several slots of a token gets one row per slot, each weighted
+ *               by its own slot's weight and counted against the capacity); or
  *   neither (router-projection mode): the logits are x . w_router^T from
  *               weights->w_router, as moe_w8a8_router_logits computes them,
  *               and the routing of step 1 is taken on them.

@@ -284,6 +284,29 @@ def test_invalid_expert_ids(torch_cuda, T, gemm_path):
     _full_parity(wl, inputs, cal, gemm_path)
 
 
+@pytest.mark.parametrize("gemm_path", [1, 2])
+@pytest.mark.parametrize("T,cf", [(40, 0.0), (3000, 0.0), (3000, 1.0)],
+                         ids=["T40", "T3000", "T3000_cap"])
+def test_repeated_expert_ids(torch_cuda, T, cf, gemm_path):
+    """Pre-routed tokens that name one expert in several slots: each slot is
+    an assignment of its own (a row per slot, weighted by that slot's weight,
+    counted against the capacity in (token, slot) order), as in the oracle.
+    Through the fused prologue (T = 40) and the batched routing (T * k = 6000,
+    also with capacity drops)."""
+    wl = synth.workload("tiny", T=T, pre_routed=True, zipf_s=1.1, capacity_factor=cf)
+    _say("[parity] repeated ids T=%d cf=%g path=%d" % (T, cf, gemm_path))
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    ids = inputs.ids.copy()
+    rng = np.random.default_rng(7)
+    rows = rng.choice(wl.T, size=max(4, wl.T // 3), replace=False)
+    ids[rows, 1:] = ids[rows, :1]          # every slot of these tokens: one expert
+    ids[0, :] = 2                          # token 0 too, whatever it had
+    assert (ids[:, 0] == ids[:, 1]).sum() >= rows.size
+    inputs = synth.Inputs(x=inputs.x, ids=ids, w=inputs.w)
+    _full_parity(wl, inputs, cal, gemm_path)
+
+
 def test_weights_past_2gib(torch_cuda):
     """A layer whose gate/up codes pass 2^31 bytes (33 experts, H 8192,
     F 4096: 2.2 GB, the down codes 1.1 GB), so that every weight and row
