@@ -31,6 +31,13 @@ fp64 from the unquantised tensors. A wrong scale, a weight on the wrong slot,
 a transposed operand, gate and up swapped, a lost capacity drop or a wrong
 permutation changes the result. The planted codes (qx, q_gu, q_d, qh) and the
 exact scales are checked stage by stage as well.
+
+The FP8 experts ("超大规模模型推理的Day0适配实践" §二.1, §四) are pinned the
+same way with 448 in place of 127: every planted value is an integer that
+e4m3 represents (at most 4 significant bits), so codes and scales are again
+exact and the FP8 layer must equal the same dense FFN. The e4m3 bytes are
+decoded here from their bit fields (sign, 4 exponent bits with bias 7, 3
+mantissa bits), independently of the oracle's decoder.
 """
 import math
 
@@ -44,6 +51,7 @@ from test_oracle_pins import _bf16_nearest_bruteforce
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 H, F, E, K, T = 8, 4, 5, 2, 6
+FORMATS = {"int8": (oracle.FMT_INT8, 127), "fp8": (oracle.FMT_FP8, 448)}
 ROUTED = 4          # experts 0..3; expert 4 only carries the weight ranges
 ALPHA = 0.5
 ANCHOR, GATE_PAD, UP_PAD = 0, 6, 7
@@ -51,6 +59,33 @@ ANCHOR, GATE_PAD, UP_PAD = 0, 6, 7
 
 def _pow2(e):
     return float(2.0 ** e)
+
+
+def _e4m3_byte_value(c):
+    """Value of an OCP e4m3 byte from its bit fields."""
+    c = int(c) & 0xFF
+    sign = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 0xF, c & 7
+    assert not (e == 15 and m == 7), "NaN code"
+    return sign * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def _code_values(codes, fmt):
+    codes = np.asarray(codes)
+    if fmt == oracle.FMT_INT8:
+        return codes.astype(np.float64)
+    return np.vectorize(_e4m3_byte_value, otypes=[np.float64])(codes.view(np.uint8))
+
+
+def _grid(qmax):
+    """Signed integers the format represents exactly, up to qmax: all of
+    [-127, 127] for INT8; for e4m3 the integers with at most 4 significant
+    bits (1..15, then steps of 2 to 30, 4 to 60, 8 to 120, 16 to 240, 32 to
+    448)."""
+    if qmax == 127:
+        return np.arange(-127, 128)
+    pos = [v for v in range(1, 449) if v < 16 or (v >> (v.bit_length() - 4)) << (v.bit_length() - 4) == v]
+    return np.array(sorted([-v for v in pos] + [0] + pos))
 
 
 def _reference_route(logits):
@@ -99,20 +134,21 @@ def _reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up
     return out
 
 
-def _build(seed):
+def _build(seed, qmax=127):
     """One lossless case: tensors, the planted codes and exponents, logits."""
-    rng = np.random.default_rng([4242, seed])
+    rng = np.random.default_rng([4242, seed, qmax])
+    grid = _grid(qmax)
     b = rng.integers(-1, 3, size=H)                 # s_j = 2^b_j
-    a = rng.integers(5, 7, size=H)                  # weight range aw_j = 4^a_j
+    a = rng.integers(5, 7, size=H) + (qmax > 127)   # weight range aw_j = 4^a_j
     aw = np.array([4.0 ** int(v) for v in a])
     ax = np.array([4.0 ** int(a[j] + b[j]) for j in range(H)])
     calib = np.stack([ax * rng.choice([-1, 1], size=H), ax / 2 * rng.choice([-1, 1], size=H)])
     s = np.array([_pow2(int(v)) for v in b])
 
-    # tokens: integer codes d with d[ANCHOR] = 127, zero padding channels
+    # tokens: codes d on the grid with d[ANCHOR] = qmax, zero padding channels
     m = rng.integers(-1, 2, size=T)
-    d = rng.integers(-127, 128, size=(T, H))
-    d[:, ANCHOR] = 127
+    d = rng.choice(grid, size=(T, H))
+    d[:, ANCHOR] = qmax
     d[:, GATE_PAD] = 0
     d[:, UP_PAD] = 0
     x = (d * np.array([_pow2(int(v)) for v in m])[:, None]) * s[None, :]
@@ -148,19 +184,19 @@ def _build(seed):
             cg[ANCHOR] = rng.integers(2, 4)
             live = rng.choice(np.arange(1, GATE_PAD), size=2, replace=False)
             cg[live] = rng.choice([-1, 1], size=2)
-            cg[GATE_PAD] = 127
+            cg[GATE_PAD] = qmax
             acc_g = {t: int(d[t] @ cg) for t in range(T) if (t, e) in pairs}
             if all(v * _pow2(int(m[t]) + pg) >= 40 for t, v in acc_g.items()):
                 break
         else:
             raise AssertionError("no gate row with every gate value >= 40")
-        n = rng.integers(-127, 128, size=F)
-        n[rng.integers(F)] = 127 * rng.choice([-1, 1])
+        n = rng.choice(grid, size=F)
+        n[rng.integers(F)] = qmax * rng.choice([-1, 1])
         cu = np.zeros((F, H), np.int64)
         cu[:, ANCHOR] = n
-        cu[:, UP_PAD] = 127
-        cd = rng.integers(-127, 128, size=(H, F))
-        cd[np.arange(H), rng.integers(0, F, size=H)] = 127 * rng.choice([-1, 1], size=H)
+        cu[:, UP_PAD] = qmax
+        cd = rng.choice(grid, size=(H, F))
+        cd[np.arange(H), rng.integers(0, F, size=H)] = qmax * rng.choice([-1, 1], size=H)
         # smoothed rows are 2^p * codes; the stored weights divide by s
         wg[e] = (_pow2(pg) * cg[None, :] / s[None, :]).astype(np.float32)
         wu[e] = (_pow2(pu) * cu / s[None, :]).astype(np.float32)
@@ -183,16 +219,18 @@ MODES = ["logits", "capacity", "pre_routed"]
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("seed", range(6))
-def test_lossless_layer_equals_dense_ffn(seed, mode):
-    c = _build(seed)
-    cal = oracle.calibrate(c["calib_bits"], c["wg"], c["wu"], c["wd"], ALPHA)
+@pytest.mark.parametrize("fmt_name", sorted(FORMATS))
+def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
+    fmt, qmax = FORMATS[fmt_name]
+    c = _build(seed, qmax)
+    cal = oracle.calibrate(c["calib_bits"], c["wg"], c["wu"], c["wd"], ALPHA, fmt=fmt)
     # calibration: exact s, the planted codes and power-of-2 scales
     assert np.array_equal(cal["s"].astype(np.float64), c["s"])
     assert np.array_equal(cal["inv_s"].astype(np.float64), 1.0 / c["s"])
     for e, p in c["plan"].items():
-        assert np.array_equal(cal["q_gu"][e, :F], np.tile(p["cg"], (F, 1)))
-        assert np.array_equal(cal["q_gu"][e, F:], p["cu"])
-        assert np.array_equal(cal["q_d"][e], p["cd"])
+        assert np.array_equal(_code_values(cal["q_gu"][e, :F], fmt), np.tile(p["cg"], (F, 1)))
+        assert np.array_equal(_code_values(cal["q_gu"][e, F:], fmt), p["cu"])
+        assert np.array_equal(_code_values(cal["q_d"][e], fmt), p["cd"])
         assert np.all(cal["sw_gu"][e, :F] == _pow2(p["pg"]))
         assert np.all(cal["sw_gu"][e, F:] == _pow2(p["pu"]))
         assert np.all(cal["sw_d"][e] == _pow2(p["pr"]))
@@ -200,10 +238,10 @@ def test_lossless_layer_equals_dense_ffn(seed, mode):
     cf = 0.75 if mode == "capacity" else 0.0     # C = ceil(0.75 * 12 / 5) = 2
     if mode == "pre_routed":
         ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
-        o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"])
+        o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"], fmt=fmt)
     else:
         ids, w = _reference_route(c["logits"])
-        o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf)
+        o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf, fmt=fmt)
         assert np.array_equal(o["ids"], ids)
         assert np.array_equal(o["w"].astype(np.float64), w)     # ties: exactly 1/2
         assert np.all(w == 0.5) and np.all(ids < ROUTED)
@@ -213,16 +251,16 @@ def test_lossless_layer_equals_dense_ffn(seed, mode):
         assert not keep.all()
 
     # token codes and scales are the planted ones
-    assert np.array_equal(o["qx"], c["d"])
+    assert np.array_equal(_code_values(o["qx"], fmt), c["d"])
     assert np.array_equal(o["sx"].astype(np.float64), [_pow2(int(v)) for v in c["m"]])
     # every kept row requantises to its expert's n_f, with the exact scale
     for i in range(o["kept"]):
         a = int(o["sorted"][i])
         t, e = a // K, int(o["ids"].reshape(-1)[a])
         p = c["plan"][e]
-        assert np.array_equal(o["qh"][i], p["n"])
+        assert np.array_equal(_code_values(o["qh"][i], fmt), p["n"])
         expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
-        assert float(o["sh"][i]) == p["acc_g"][t] * 127 * _pow2(expo)
+        assert float(o["sh"][i]) == p["acc_g"][t] * qmax * _pow2(expo)
 
     ref = _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids, w, keep)
     assert np.array_equal(o["out_exact"], ref), np.abs(o["out_exact"] - ref).max()
