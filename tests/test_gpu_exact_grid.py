@@ -1,0 +1,154 @@
+"""The GPU path on inputs that every quantiser represents exactly: the
+construction of tests/test_oracle_exact_layer.py at the kernels' sizes
+(hidden 256, FFN 128, 8 routed experts and one that only carries the weight
+ranges, top-2), INT8, with the layer calibrated on the GPU from the
+unquantised weights ("MiniMax-M3 W8A8 inference on K100AI" §3.2).
+
+On these inputs nothing in the quantised path may round, so the checks are
+exact where the path is integer and tight where it is not:
+  - smoothing factors, weight codes and weight scales equal the planted ones;
+  - token codes and scales, the GEMM1 INT32 sums, the requantised codes (not
+    one may flip) and their scales equal the planted values;
+  - each dequantised expert row y differs from the exact fp64 row by at most
+    the GPU's fp32 roundings, 2^-22 |y|, plus on the tiled path y's int16
+    step: half the 16-column group's largest |y| / 32767, plus 2^-20 of it;
+  - the output differs from the dense fp64 MoE FFN by at most those errors
+    weighted by |w|, the fp32 combine (2^-22 of sum |w y|) and half a bf16
+    step at the output.
+The reference is the dense FFN of the CPU test, with routing (ties to the
+lower index, "超大规模模型推理的Day0适配实践" §四) and capacity (§二.2) by
+their definitions; it takes nothing from the oracle or the GPU.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from moe_testlib import bf16_step, bf16_tensor, run_gpu, unpack_tiled
+from test_oracle_exact_layer import ALPHA, build, reference_keep, reference_route, reference_y
+
+pytestmark = pytest.mark.gpu
+
+DIMS = dict(H=256, F=128, E=9, K=2)
+Y_GROUP = 16
+Y_CODE_MAX = 32767
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w8a8_int8_expert_amd as m
+    m.load_library()
+    return torch
+
+
+@functools.lru_cache(maxsize=1)
+def _case(T):
+    return build(7, 127, T=T, **DIMS)
+
+
+@functools.lru_cache(maxsize=1)
+def _gpu_layer(T):
+    """The case's layer, calibrated on the GPU, after checking that the
+    calibration reproduces the planted smoothing, codes and scales."""
+    import torch
+    import w8a8_int8_expert_amd as m
+    c = _case(T)
+    H, F, E, K = c["H"], c["F"], c["E"], c["K"]
+    dev = torch.device("cuda")
+    g = m.MoEW8A8(H, F, E, K)
+    g.calibrate(bf16_tensor(c["calib_bits"], dev), torch.from_numpy(c["wg"]).to(dev),
+                torch.from_numpy(c["wu"]).to(dev), torch.from_numpy(c["wd"]).to(dev), ALPHA)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.smooth.cpu().numpy().astype(np.float64), c["s"])
+    assert np.array_equal(g.inv_smooth.cpu().numpy().astype(np.float64), 1.0 / c["s"])
+    q_gu = unpack_tiled(g.w_gate_up.cpu().numpy(), E, 2 * F, H)
+    q_d = unpack_tiled(g.w_down.cpu().numpy(), E, H, F)
+    s_gu, s_d = g.s_gate_up.cpu().numpy(), g.s_down.cpu().numpy()
+    for e, p in c["plan"].items():
+        assert np.array_equal(q_gu[e, :F], np.tile(p["cg"], (F, 1)))
+        assert np.array_equal(q_gu[e, F:], p["cu"])
+        assert np.array_equal(q_d[e], p["cd"])
+        assert np.all(s_gu[e, :F] == 2.0 ** p["pg"]) and np.all(s_gu[e, F:] == 2.0 ** p["pu"])
+        assert np.all(s_d[e] == 2.0 ** p["pr"])
+    return g
+
+
+def _y_error_bound(y, tiled):
+    """Per-element bound on |y_gpu - y| for exact rows y [n][H]."""
+    b = 2.0 ** -22 * np.abs(y)
+    if tiled:
+        G = np.abs(y).reshape(y.shape[0], -1, Y_GROUP).max(axis=2)
+        b = b + np.repeat(G, Y_GROUP, axis=1) * (0.5 / Y_CODE_MAX + 2.0 ** -20)
+    return b
+
+
+@pytest.mark.parametrize("gemm_path", [1, 2])
+@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed"])
+@pytest.mark.parametrize("T", [40, 3000])
+def test_exact_grid_layer(torch_cuda, T, mode, gemm_path):
+    c = _case(T)
+    H, F, E, K = c["H"], c["F"], c["E"], c["K"]
+    _say("[exact grid] T=%d H=%d F=%d E=%d k=%d mode=%s path=%d" % (T, H, F, E, K, mode,
+                                                                   gemm_path))
+    g = _gpu_layer(T)
+    cf = 0.75 if mode == "capacity" else 0.0
+    if mode == "pre_routed":
+        ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
+        inputs = synth.Inputs(x=c["x_bits"], ids=c["pre_ids"], w=c["pre_w"])
+    else:
+        ids, w = reference_route(c["logits"], K)
+        inputs = synth.Inputs(x=c["x_bits"], logits=c["logits"])
+    r = run_gpu(g, inputs, K, cf, gemm_path)
+    if mode != "pre_routed":
+        assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 0.5)
+    keep = reference_keep(ids, cf, E)
+    assert np.array_equal(r["row_of"] >= 0, keep)
+    if mode == "capacity":
+        assert not keep.all()
+    assert np.array_equal(r["qx"], c["d"])
+    assert np.array_equal(r["sx"].astype(np.float64), 2.0 ** c["m"])
+
+    kept = r["kept"]
+    a = r["sorted"].astype(np.int64)
+    t_of, j_of = a // K, a % K
+    acc1 = r["gpu_tensors"]["acc1"].view(-1, 2 * F)[:kept].cpu().numpy()
+    qh = r["gpu_tensors"]["qh"].view(-1, F)[:kept].cpu().numpy()
+    sh = r["gpu_tensors"]["sh"][:kept].cpu().numpy()
+    y_gpu = r["gpu_tensors"]["y"].view(-1, H)[:kept].cpu().numpy().astype(np.float64)
+    for i in range(kept):
+        t, e = int(t_of[i]), int(ids[t_of[i], j_of[i]])
+        p = c["plan"][e]
+        acc_g = p["acc_g"][t]
+        assert np.all(acc1[i, :F] == acc_g) and np.array_equal(acc1[i, F:], 127 * p["n"])
+        assert np.array_equal(qh[i], p["n"]), "row %d: a requantised code moved" % i
+        expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
+        assert float(sh[i]) == acc_g * 127 * 2.0 ** expo
+
+    y = reference_y(c["x"], c["wg"], c["wu"], c["wd"], ids, keep)       # [T][K][H]
+    tiled = gemm_path == 2
+    y_rows = y[t_of, j_of]
+    y_err = np.abs(y_gpu - y_rows)
+    y_bound = _y_error_bound(y_rows, tiled)
+    assert np.all(y_err <= y_bound), "y: %g of its bound" % (y_err / np.maximum(y_bound, 1e-300)).max()
+
+    ref = np.einsum("tk,tkh->th", w * keep, y)
+    out = synth.bf16_bits_to_f32(r["out"]).reshape(T, H).astype(np.float64)
+    absw = np.abs(w * keep)
+    bound = np.zeros((T, H))
+    for j in range(K):
+        bound += absw[:, j, None] * (_y_error_bound(y[:, j], tiled) + 2.0 ** -22 * np.abs(y[:, j]))
+    bound += 0.5 * bf16_step(out)
+    err = np.abs(out - ref)
+    _say("[exact grid] y: max error %.3g of its bound; out: max error %.3g of its bound, "
+         "%.3g x RMS" % ((y_err / np.maximum(y_bound, 1e-300)).max(),
+                          (err / np.maximum(bound, 1e-300)).max(),
+                          err.max() / np.sqrt(np.mean(ref ** 2))))
+    assert np.all(err <= bound)

@@ -37,7 +37,6 @@ def torch_cuda():
 
 
 @functools.lru_cache(maxsize=2)
-@functools.lru_cache(maxsize=2)
 def _layer_and_cal(wl: synth.Workload):
     """The seeded layer and its oracle calibration, kept for the next test on
     the same workload (both only read)."""

@@ -17,10 +17,11 @@ The inputs are built so that no step of the quantised path loses anything:
     the row maximum is 127 * (g * 127 * 2^e) and the codes are the n_f;
   - every product and sum stays within 24 (fp32) and 53 (fp64) significant
     bits.
-Channels 6 and 7 are zero in every token and carry the 127 of the gate and up
-rows, so those rows have their maximum where it does not touch the sums. A
-fifth expert is never routed; it holds each channel's weight range, which
-fixes s.
+The last two channels are zero in every token and carry the 127 of the gate
+and up rows, so those rows have their maximum where it does not touch the
+sums. The last expert is never routed; it holds each channel's weight range,
+which fixes s. The helpers take any size; tests/test_gpu_exact_grid.py builds
+the same construction at the GPU kernels' sizes.
 
 The reference uses nothing of the oracle: top-k by (logit descending, index
 ascending) with softmax weights renormalised over the chosen experts
@@ -50,11 +51,9 @@ from test_oracle_pins import _bf16_nearest_bruteforce
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
-H, F, E, K, T = 8, 4, 5, 2, 6
 FORMATS = {"int8": (oracle.FMT_INT8, 127), "fp8": (oracle.FMT_FP8, 448)}
-ROUTED = 4          # experts 0..3; expert 4 only carries the weight ranges
+SMALL = dict(H=8, F=4, E=5, K=2, T=6)
 ALPHA = 0.5
-ANCHOR, GATE_PAD, UP_PAD = 0, 6, 7
 
 
 def _pow2(e):
@@ -84,16 +83,18 @@ def _grid(qmax):
     448)."""
     if qmax == 127:
         return np.arange(-127, 128)
-    pos = [v for v in range(1, 449) if v < 16 or (v >> (v.bit_length() - 4)) << (v.bit_length() - 4) == v]
+    pos = [v for v in range(1, 449)
+           if v < 16 or (v >> (v.bit_length() - 4)) << (v.bit_length() - 4) == v]
     return np.array(sorted([-v for v in pos] + [0] + pos))
 
 
-def _reference_route(logits):
+def reference_route(logits, k):
     """Top-k with ties to the lower index; softmax renormalised over the k."""
-    ids = np.empty((T, K), np.int32)
-    w = np.empty((T, K), np.float64)
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
     for t in range(T):
-        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:K]
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
         ids[t] = order
         ex = np.array([math.exp(float(logits[t, e]) - float(logits[t, order[0]]))
                        for e in order])
@@ -101,26 +102,29 @@ def _reference_route(logits):
     return ids, w
 
 
-def _reference_keep(ids, cf):
+def reference_keep(ids, cf, E):
     """The first C assignments of each expert in (token, slot) order."""
-    keep = np.ones((T, K), bool)
+    T, k = ids.shape
+    keep = np.ones((T, k), bool)
     if cf <= 0:
         return keep
-    C = math.ceil(cf * T * K / E)
+    C = math.ceil(cf * T * k / E)
     seen = np.zeros(E, int)
     for t in range(T):
-        for j in range(K):
+        for j in range(k):
             e = ids[t, j]
             keep[t, j] = seen[e] < C
             seen[e] += 1
     return keep
 
 
-def _reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up=False):
-    """Dense MoE FFN in fp64 on the unquantised tensors."""
-    out = np.zeros((T, H))
+def reference_y(x, wg, wu, wd, ids, keep, swap_gate_up=False):
+    """Each kept assignment's expert output W_down[e] (silu(W_gate[e] x) *
+    (W_up[e] x)) in fp64 on the unquantised tensors: [T][k][H], 0 if dropped."""
+    T, k = ids.shape
+    y = np.zeros((T, k, wd.shape[1]))
     for t in range(T):
-        for j in range(K):
+        for j in range(k):
             if not keep[t, j]:
                 continue
             e = ids[t, j]
@@ -128,16 +132,29 @@ def _reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up
             u = wu[e].astype(np.float64) @ x[t]
             if swap_gate_up:
                 g, u = u, g
-            h = g / (1.0 + np.exp(-g)) * u
-            wj = w[t, K - 1 - j] if swap_slots else w[t, j]
-            out[t] += float(wj) * (wd[e].astype(np.float64) @ h)
+            y[t, j] = wd[e].astype(np.float64) @ (g / (1.0 + np.exp(-g)) * u)
+    return y
+
+
+def reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up=False):
+    """Dense MoE FFN in fp64: sum over the kept slots of w * y, slot order."""
+    y = reference_y(x, wg, wu, wd, ids, keep, swap_gate_up)
+    k = ids.shape[1]
+    out = np.zeros((x.shape[0], wd.shape[1]))
+    for j in range(k):
+        wj = w[:, k - 1 - j] if swap_slots else w[:, j]
+        out += wj.astype(np.float64)[:, None] * y[:, j]
     return out
 
 
-def _build(seed, qmax=127):
-    """One lossless case: tensors, the planted codes and exponents, logits."""
-    rng = np.random.default_rng([4242, seed, qmax])
+def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6):
+    """One lossless case: tensors, the planted codes and exponents, logits.
+    Experts 0..E-2 are routed; expert E-1 only carries the weight ranges.
+    Channel 0 is the anchor (qmax in every token); channels H-2 and H-1 are
+    zero in every token and hold the qmax of the gate and the up rows."""
+    rng = np.random.default_rng([4242, seed, qmax, H, T])
     grid = _grid(qmax)
+    routed, anchor, gate_pad, up_pad = E - 1, 0, H - 2, H - 1
     b = rng.integers(-1, 3, size=H)                 # s_j = 2^b_j
     a = rng.integers(5, 7, size=H) + (qmax > 127)   # weight range aw_j = 4^a_j
     aw = np.array([4.0 ** int(v) for v in a])
@@ -145,31 +162,31 @@ def _build(seed, qmax=127):
     calib = np.stack([ax * rng.choice([-1, 1], size=H), ax / 2 * rng.choice([-1, 1], size=H)])
     s = np.array([_pow2(int(v)) for v in b])
 
-    # tokens: codes d on the grid with d[ANCHOR] = qmax, zero padding channels
+    # tokens: codes d on the grid with d[anchor] = qmax, zero padding channels
     m = rng.integers(-1, 2, size=T)
     d = rng.choice(grid, size=(T, H))
-    d[:, ANCHOR] = qmax
-    d[:, GATE_PAD] = 0
-    d[:, UP_PAD] = 0
+    d[:, anchor] = qmax
+    d[:, gate_pad] = 0
+    d[:, up_pad] = 0
     x = (d * np.array([_pow2(int(v)) for v in m])[:, None]) * s[None, :]
     x32 = x.astype(np.float32)
     assert np.array_equal(x32.astype(np.float64), x)
     x_bits = f32_to_bf16_bits(x32)
     assert np.array_equal(x_bits.astype(np.uint32) << 16, x32.view(np.uint32)), "x not bf16"
 
-    # routing, fixed before the gate rows so that every pair used can be checked
+    # routing: two routed experts tied at the top of every token (weights
+    # exactly 1/2); the carrier expert sometimes ties too and must lose
     logits = np.zeros((T, E), np.float32)
     for t in range(T):
-        A, B = sorted(rng.choice(ROUTED, size=2, replace=False))
+        A, B = sorted(rng.choice(routed, size=2, replace=False))
         L = np.float32(rng.integers(-8, 9) / 4)
         logits[t] = L - np.float32(1 + rng.integers(0, 4, size=E))
         logits[t, A] = logits[t, B] = L
-        if rng.random() < 0.5:      # a higher index tied at the top: it must lose
-            logits[t, 4] = L
-    pre_ids = np.stack([rng.permutation(ROUTED)[:K] for _ in range(T)]).astype(np.int32)
+        if rng.random() < 0.5:
+            logits[t, routed] = L
+    pre_ids = np.stack([rng.permutation(routed)[:K] for _ in range(T)]).astype(np.int32)
     pre_w = (rng.integers(1, 9, size=(T, K)) / 8).astype(np.float32)
-
-    r_ids, _ = _reference_route(logits)
+    r_ids, _ = reference_route(logits, K)
     pairs = {(t, int(e)) for t in range(T) for e in r_ids[t]} | \
             {(t, int(e)) for t in range(T) for e in pre_ids[t]}
 
@@ -177,24 +194,23 @@ def _build(seed, qmax=127):
     wu = np.zeros((E, F, H), np.float32)
     wd = np.zeros((E, H, F), np.float32)
     plan = {}
-    for e in range(ROUTED):
-        pg, pu, pr = (int(v) for v in rng.integers(-1, 2, size=3))
-        for _ in range(1000):
-            cg = np.zeros(H, np.int64)
-            cg[ANCHOR] = rng.integers(2, 4)
-            live = rng.choice(np.arange(1, GATE_PAD), size=2, replace=False)
-            cg[live] = rng.choice([-1, 1], size=2)
-            cg[GATE_PAD] = qmax
-            acc_g = {t: int(d[t] @ cg) for t in range(T) if (t, e) in pairs}
-            if all(v * _pow2(int(m[t]) + pg) >= 40 for t, v in acc_g.items()):
-                break
-        else:
-            raise AssertionError("no gate row with every gate value >= 40")
+    for e in range(routed):
+        pu, pr = (int(v) for v in rng.integers(-1, 2, size=2))
+        # gate anchor code 3 and two live +-1: acc_g >= 3*qmax - 2*qmax = qmax,
+        # and with 2^(m + pg) >= 1/2 every gate value is at least qmax/2 >= 40
+        pg = int(rng.integers(0, 2))
+        cg = np.zeros(H, np.int64)
+        cg[anchor] = 3
+        live = rng.choice(np.arange(1, gate_pad), size=2, replace=False)
+        cg[live] = rng.choice([-1, 1], size=2)
+        cg[gate_pad] = qmax
+        acc_g = {t: int(d[t] @ cg) for t in range(T) if (t, e) in pairs}
+        assert all(v * _pow2(int(m[t]) + pg) >= 40 for t, v in acc_g.items())
         n = rng.choice(grid, size=F)
         n[rng.integers(F)] = qmax * rng.choice([-1, 1])
         cu = np.zeros((F, H), np.int64)
-        cu[:, ANCHOR] = n
-        cu[:, UP_PAD] = qmax
+        cu[:, anchor] = n
+        cu[:, up_pad] = qmax
         cd = rng.choice(grid, size=(H, F))
         cd[np.arange(H), rng.integers(0, F, size=H)] = qmax * rng.choice([-1, 1], size=H)
         # smoothed rows are 2^p * codes; the stored weights divide by s
@@ -203,15 +219,16 @@ def _build(seed, qmax=127):
         wd[e] = (_pow2(pr) * cd).astype(np.float32)
         plan[e] = dict(pg=pg, pu=pu, pr=pr, cg=cg, n=n, cu=cu, cd=cd, acc_g=acc_g)
     # the never-routed expert attains each channel's weight range
-    wg[ROUTED, 0] = (aw * rng.choice([-1, 1], size=H)).astype(np.float32)
-    wu[ROUTED] = rng.uniform(-1, 1, size=(F, H)).astype(np.float32)
-    wd[ROUTED] = rng.uniform(-1, 1, size=(H, F)).astype(np.float32)
+    wg[routed, 0] = (aw * rng.choice([-1, 1], size=H)).astype(np.float32)
+    wu[routed] = rng.uniform(-1, 1, size=(F, H)).astype(np.float32)
+    wd[routed] = rng.uniform(-1, 1, size=(H, F)).astype(np.float32)
     for j in range(H):
         assert np.abs(np.concatenate([wg[:, :, j], wu[:, :, j]])).max() == aw[j]
         assert np.abs(calib[:, j]).max() == ax[j]
     calib_bits = f32_to_bf16_bits(calib.astype(np.float32))
-    return dict(x=x, x_bits=x_bits, d=d, m=m, s=s, calib_bits=calib_bits, wg=wg, wu=wu, wd=wd,
-                plan=plan, logits=logits, pre_ids=pre_ids, pre_w=pre_w)
+    return dict(H=H, F=F, E=E, K=K, T=T, qmax=qmax, x=x, x_bits=x_bits, d=d, m=m, s=s,
+                calib_bits=calib_bits, wg=wg, wu=wu, wd=wd, plan=plan, logits=logits,
+                pre_ids=pre_ids, pre_w=pre_w)
 
 
 MODES = ["logits", "capacity", "pre_routed"]
@@ -222,7 +239,8 @@ MODES = ["logits", "capacity", "pre_routed"]
 @pytest.mark.parametrize("fmt_name", sorted(FORMATS))
 def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
     fmt, qmax = FORMATS[fmt_name]
-    c = _build(seed, qmax)
+    c = build(seed, qmax, **SMALL)
+    F, E, K = c["F"], c["E"], c["K"]
     cal = oracle.calibrate(c["calib_bits"], c["wg"], c["wu"], c["wd"], ALPHA, fmt=fmt)
     # calibration: exact s, the planted codes and power-of-2 scales
     assert np.array_equal(cal["s"].astype(np.float64), c["s"])
@@ -240,12 +258,12 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
         ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
         o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"], fmt=fmt)
     else:
-        ids, w = _reference_route(c["logits"])
+        ids, w = reference_route(c["logits"], K)
         o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf, fmt=fmt)
         assert np.array_equal(o["ids"], ids)
         assert np.array_equal(o["w"].astype(np.float64), w)     # ties: exactly 1/2
-        assert np.all(w == 0.5) and np.all(ids < ROUTED)
-    keep = _reference_keep(ids, cf)
+        assert np.all(w == 0.5) and np.all(ids < E - 1)
+    keep = reference_keep(ids, cf, E)
     assert np.array_equal(o["row_of"] >= 0, keep)
     if mode == "capacity":
         assert not keep.all()
@@ -262,17 +280,15 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
         expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
         assert float(o["sh"][i]) == p["acc_g"][t] * qmax * _pow2(expo)
 
-    ref = _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids, w, keep)
+    args = (c["x"], c["wg"], c["wu"], c["wd"], ids, w)
+    ref = reference_layer(*args, keep)
     assert np.array_equal(o["out_exact"], ref), np.abs(o["out_exact"] - ref).max()
     want = np.array([[_bf16_nearest_bruteforce(float(v)) for v in row] for row in ref], np.uint16)
     assert np.array_equal(o["out"], want)
 
     # the pin has power: plausible slips in the layer change the result
-    assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids, w,
-                                                    keep, swap_gate_up=True))
+    assert not np.array_equal(ref, reference_layer(*args, keep, swap_gate_up=True))
     if mode == "pre_routed":
-        assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids,
-                                                        w, keep, swap_slots=True))
+        assert not np.array_equal(ref, reference_layer(*args, keep, swap_slots=True))
     if mode == "capacity":
-        assert not np.array_equal(ref, _reference_layer(c["x"], c["wg"], c["wu"], c["wd"], ids,
-                                                        w, np.ones_like(keep)))
+        assert not np.array_equal(ref, reference_layer(*args, np.ones_like(keep)))
