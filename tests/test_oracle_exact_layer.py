@@ -147,13 +147,16 @@ def reference_layer(x, wg, wu, wd, ids, w, keep, swap_slots=False, swap_gate_up=
     return out
 
 
-def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6):
+def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     """One lossless case: tensors, the planted codes and exponents, logits.
     Experts 0..E-2 are routed; expert E-1 only carries the weight ranges.
     Channel 0 is the anchor (qmax in every token); channels H-2 and H-1 are
-    zero in every token and hold the qmax of the gate and the up rows."""
-    rng = np.random.default_rng([4242, seed, qmax, H, T])
+    zero in every token and hold the qmax of the gate and the up rows.
+    down_step: the requantised values n and the down codes are drawn from the
+    multiples of down_step on the grid."""
+    rng = np.random.default_rng([4242, seed, qmax, H, T, down_step])
     grid = _grid(qmax)
+    grid_down = grid[grid % down_step == 0]
     routed, anchor, gate_pad, up_pad = E - 1, 0, H - 2, H - 1
     b = rng.integers(-1, 3, size=H)                 # s_j = 2^b_j
     a = rng.integers(5, 7, size=H) + (qmax > 127)   # weight range aw_j = 4^a_j
@@ -206,12 +209,12 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6):
         cg[gate_pad] = qmax
         acc_g = {t: int(d[t] @ cg) for t in range(T) if (t, e) in pairs}
         assert all(v * _pow2(int(m[t]) + pg) >= 40 for t, v in acc_g.items())
-        n = rng.choice(grid, size=F)
+        n = rng.choice(grid_down, size=F)
         n[rng.integers(F)] = qmax * rng.choice([-1, 1])
         cu = np.zeros((F, H), np.int64)
         cu[:, anchor] = n
         cu[:, up_pad] = qmax
-        cd = rng.choice(grid, size=(H, F))
+        cd = rng.choice(grid_down, size=(H, F))
         cd[np.arange(H), rng.integers(0, F, size=H)] = qmax * rng.choice([-1, 1], size=H)
         # smoothed rows are 2^p * codes; the stored weights divide by s
         wg[e] = (_pow2(pg) * cg[None, :] / s[None, :]).astype(np.float32)
