@@ -1,8 +1,9 @@
 """The GPU path on inputs that every quantiser represents exactly: the
 construction of tests/test_oracle_exact_layer.py at the kernels' sizes
 (hidden 256, FFN 128, 8 routed experts and one that only carries the weight
-ranges, top-2), INT8, with the layer calibrated on the GPU from the
-unquantised weights ("MiniMax-M3 W8A8 inference on K100AI" §3.2).
+ranges, top-2; hidden 512, FFN 256, 64 routed experts, top-8), with the layer
+calibrated on the GPU from the unquantised weights ("MiniMax-M3 W8A8
+inference on K100AI" §3.2).
 
 On these inputs nothing in the quantised path may round, so the checks are
 exact where the path is integer and tight where it is not:
@@ -42,7 +43,8 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-DIMS = dict(H=256, F=128, E=9, K=2)
+SHAPES = {"E9_k2": dict(H=256, F=128, E=9, K=2),
+          "E65_k8": dict(H=512, F=256, E=65, K=8)}
 Y_GROUP = 16
 Y_CODE_MAX = 32767
 
@@ -65,19 +67,19 @@ FORMATS = {"int8": (oracle.FMT_INT8, 127, 1), "fp8": (oracle.FMT_FP8, 448, 4)}
 
 
 @functools.lru_cache(maxsize=1)
-def _case(T, fmt_name):
+def _case(T, fmt_name, shape):
     _, qmax, step = FORMATS[fmt_name]
-    return build(7, qmax, T=T, down_step=step, **DIMS)
+    return build(7, qmax, T=T, down_step=step, **SHAPES[shape])
 
 
 @functools.lru_cache(maxsize=1)
-def _gpu_layer(T, fmt_name):
+def _gpu_layer(T, fmt_name, shape):
     """The case's layer, calibrated on the GPU, after checking that the
     calibration reproduces the planted smoothing, codes and scales."""
     import torch
     import w8a8_int8_expert_amd as m
     fmt = FORMATS[fmt_name][0]
-    c = _case(T, fmt_name)
+    c = _case(T, fmt_name, shape)
     H, F, E, K = c["H"], c["F"], c["E"], c["K"]
     dev = torch.device("cuda")
     g = m.MoEW8A8(H, F, E, K, fp8=fmt == oracle.FMT_FP8)
@@ -109,15 +111,16 @@ def _y_error_bound(y, tiled):
 
 @pytest.mark.parametrize("gemm_path", [1, 2])
 @pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed"])
-@pytest.mark.parametrize("T", [40, 3000])
+@pytest.mark.parametrize("shape,T", [("E9_k2", 40), ("E9_k2", 3000), ("E65_k8", 200),
+                                     ("E65_k8", 3000)])
 @pytest.mark.parametrize("fmt_name", ["int8", "fp8"])
-def test_exact_grid_layer(torch_cuda, fmt_name, T, mode, gemm_path):
+def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     fmt, qmax, _ = FORMATS[fmt_name]
-    c = _case(T, fmt_name)
+    c = _case(T, fmt_name, shape)
     H, F, E, K = c["H"], c["F"], c["E"], c["K"]
     _say("[exact grid] %s T=%d H=%d F=%d E=%d k=%d mode=%s path=%d"
          % (fmt_name, T, H, F, E, K, mode, gemm_path))
-    g = _gpu_layer(T, fmt_name)
+    g = _gpu_layer(T, fmt_name, shape)
     cf = 0.75 if mode == "capacity" else 0.0
     if mode == "pre_routed":
         ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
@@ -127,7 +130,7 @@ def test_exact_grid_layer(torch_cuda, fmt_name, T, mode, gemm_path):
         inputs = synth.Inputs(x=c["x_bits"], logits=c["logits"])
     r = run_gpu(g, inputs, K, cf, gemm_path)
     if mode != "pre_routed":
-        assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 0.5)
+        assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 1.0 / K)
     keep = reference_keep(ids, cf, E)
     assert np.array_equal(r["row_of"] >= 0, keep)
     if mode == "capacity":
@@ -144,15 +147,19 @@ def test_exact_grid_layer(torch_cuda, fmt_name, T, mode, gemm_path):
     qh = r["gpu_tensors"]["qh"].view(-1, F)[:kept].cpu().numpy()
     sh = r["gpu_tensors"]["sh"][:kept].cpu().numpy()
     y_gpu = r["gpu_tensors"]["y"].view(-1, H)[:kept].cpu().numpy().astype(np.float64)
-    for i in range(kept):
-        t, e = int(t_of[i]), int(ids[t_of[i], j_of[i]])
-        p = c["plan"][e]
-        acc_g = p["acc_g"][t]
-        assert np.all(acc1[i, :F] == acc_g) and np.array_equal(acc1[i, F:], qmax * p["n"])
-        assert np.array_equal(_code_values(qh[i], fmt), p["n"]), \
-            "row %d: a requantised code moved" % i
-        expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
-        assert float(sh[i]) == acc_g * qmax * 2.0 ** expo
+    # the planted values of every kept row, gathered by its token and expert
+    e_of = ids[t_of, j_of]
+    plan = c["plan"]
+    cg = np.stack([plan[e]["cg"] for e in range(E - 1)])
+    n = np.stack([plan[e]["n"] for e in range(E - 1)])
+    pgu = np.array([plan[e]["pg"] + plan[e]["pu"] for e in range(E - 1)])
+    acc_g = np.einsum("rh,rh->r", c["d"][t_of], cg[e_of])
+    assert np.all(acc1[:, :F] == acc_g[:, None]), "GEMM1 gate sums differ"
+    assert np.array_equal(acc1[:, F:], qmax * n[e_of]), "GEMM1 up sums differ"
+    moved = np.nonzero(np.any(_code_values(qh, fmt) != n[e_of], axis=1))[0]
+    assert moved.size == 0, "rows %s: a requantised code moved" % moved[:5]
+    expo = 2 * c["m"][t_of] + pgu[e_of]
+    assert np.array_equal(sh.astype(np.float64), acc_g * qmax * 2.0 ** expo)
 
     y = reference_y(c["x"], c["wg"], c["wu"], c["wd"], ids, keep)       # [T][K][H]
     tiled = gemm_path == 2

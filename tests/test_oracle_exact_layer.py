@@ -52,7 +52,8 @@ from test_oracle_pins import _bf16_nearest_bruteforce
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 FORMATS = {"int8": (oracle.FMT_INT8, 127), "fp8": (oracle.FMT_FP8, 448)}
-SMALL = dict(H=8, F=4, E=5, K=2, T=6)
+# k is a power of 2, so that the weights of k tied experts (1/k) are exact
+SHAPES = {"E5_k2": dict(H=8, F=4, E=5, K=2, T=6), "E7_k4": dict(H=8, F=4, E=7, K=4, T=8)}
 ALPHA = 0.5
 
 
@@ -61,19 +62,22 @@ def _pow2(e):
 
 
 def _e4m3_byte_value(c):
-    """Value of an OCP e4m3 byte from its bit fields."""
-    c = int(c) & 0xFF
+    """Value of an OCP e4m3 byte from its bit fields (NaN for 0x7f, 0xff)."""
     sign = -1.0 if c & 0x80 else 1.0
     e, m = (c >> 3) & 0xF, c & 7
-    assert not (e == 15 and m == 7), "NaN code"
+    if e == 15 and m == 7:
+        return math.nan
     return sign * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+_E4M3 = np.array([_e4m3_byte_value(c) for c in range(256)])
 
 
 def _code_values(codes, fmt):
     codes = np.asarray(codes)
     if fmt == oracle.FMT_INT8:
         return codes.astype(np.float64)
-    return np.vectorize(_e4m3_byte_value, otypes=[np.float64])(codes.view(np.uint8))
+    return _E4M3[codes.view(np.uint8)]
 
 
 def _grid(qmax):
@@ -120,19 +124,18 @@ def reference_keep(ids, cf, E):
 
 def reference_y(x, wg, wu, wd, ids, keep, swap_gate_up=False):
     """Each kept assignment's expert output W_down[e] (silu(W_gate[e] x) *
-    (W_up[e] x)) in fp64 on the unquantised tensors: [T][k][H], 0 if dropped."""
+    (W_up[e] x)) in fp64 on the unquantised tensors: [T][k][H], 0 if dropped.
+    On the inputs built here every product and partial sum is a dyadic value
+    within 53 bits, so the order of the matrix products' sums is immaterial."""
     T, k = ids.shape
     y = np.zeros((T, k, wd.shape[1]))
-    for t in range(T):
-        for j in range(k):
-            if not keep[t, j]:
-                continue
-            e = ids[t, j]
-            g = wg[e].astype(np.float64) @ x[t]
-            u = wu[e].astype(np.float64) @ x[t]
-            if swap_gate_up:
-                g, u = u, g
-            y[t, j] = wd[e].astype(np.float64) @ (g / (1.0 + np.exp(-g)) * u)
+    for e in np.unique(ids[keep]):
+        t, j = np.nonzero((ids == e) & keep)
+        g = x[t] @ wg[e].astype(np.float64).T
+        u = x[t] @ wu[e].astype(np.float64).T
+        if swap_gate_up:
+            g, u = u, g
+        y[t, j] = (g / (1.0 + np.exp(-g)) * u) @ wd[e].astype(np.float64).T
     return y
 
 
@@ -177,14 +180,14 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     x_bits = f32_to_bf16_bits(x32)
     assert np.array_equal(x_bits.astype(np.uint32) << 16, x32.view(np.uint32)), "x not bf16"
 
-    # routing: two routed experts tied at the top of every token (weights
-    # exactly 1/2); the carrier expert sometimes ties too and must lose
+    # routing: K routed experts tied at the top of every token (weights
+    # exactly 1/K); the carrier expert sometimes ties too and must lose
     logits = np.zeros((T, E), np.float32)
     for t in range(T):
-        A, B = sorted(rng.choice(routed, size=2, replace=False))
+        top = rng.choice(routed, size=K, replace=False)
         L = np.float32(rng.integers(-8, 9) / 4)
         logits[t] = L - np.float32(1 + rng.integers(0, 4, size=E))
-        logits[t, A] = logits[t, B] = L
+        logits[t, top] = L
         if rng.random() < 0.5:
             logits[t, routed] = L
     pre_ids = np.stack([rng.permutation(routed)[:K] for _ in range(T)]).astype(np.int32)
@@ -239,10 +242,11 @@ MODES = ["logits", "capacity", "pre_routed"]
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("fmt_name", sorted(FORMATS))
-def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
+def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
     fmt, qmax = FORMATS[fmt_name]
-    c = build(seed, qmax, **SMALL)
+    c = build(seed, qmax, **SHAPES[shape])
     F, E, K = c["F"], c["E"], c["K"]
     cal = oracle.calibrate(c["calib_bits"], c["wg"], c["wu"], c["wd"], ALPHA, fmt=fmt)
     # calibration: exact s, the planted codes and power-of-2 scales
@@ -256,7 +260,7 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
         assert np.all(cal["sw_gu"][e, F:] == _pow2(p["pu"]))
         assert np.all(cal["sw_d"][e] == _pow2(p["pr"]))
 
-    cf = 0.75 if mode == "capacity" else 0.0     # C = ceil(0.75 * 12 / 5) = 2
+    cf = 0.75 if mode == "capacity" else 0.0     # C = 2 (E5_k2) and 4 (E7_k4)
     if mode == "pre_routed":
         ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
         o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"], fmt=fmt)
@@ -265,7 +269,7 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, seed, mode):
         o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf, fmt=fmt)
         assert np.array_equal(o["ids"], ids)
         assert np.array_equal(o["w"].astype(np.float64), w)     # ties: exactly 1/2
-        assert np.all(w == 0.5) and np.all(ids < E - 1)
+        assert np.all(w == 1.0 / K) and np.all(ids < E - 1)
     keep = reference_keep(ids, cf, E)
     assert np.array_equal(o["row_of"] >= 0, keep)
     if mode == "capacity":
