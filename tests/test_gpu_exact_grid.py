@@ -110,7 +110,7 @@ def _y_error_bound(y, tiled):
 
 
 @pytest.mark.parametrize("gemm_path", [1, 2])
-@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed"])
+@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated"])
 @pytest.mark.parametrize("shape,T", [("E9_k2", 40), ("E9_k2", 3000), ("E65_k8", 200),
                                      ("E65_k8", 3000)])
 @pytest.mark.parametrize("fmt_name", ["int8", "fp8"])
@@ -121,15 +121,17 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     _say("[exact grid] %s T=%d H=%d F=%d E=%d k=%d mode=%s path=%d"
          % (fmt_name, T, H, F, E, K, mode, gemm_path))
     g = _gpu_layer(T, fmt_name, shape)
-    cf = 0.75 if mode == "capacity" else 0.0
-    if mode == "pre_routed":
-        ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
-        inputs = synth.Inputs(x=c["x_bits"], ids=c["pre_ids"], w=c["pre_w"])
+    cf = 0.75 if mode in ("capacity", "repeated") else 0.0
+    if mode in ("pre_routed", "repeated"):
+        # repeated: every slot of about a third of the tokens names one expert
+        ids = c["pre_ids"] if mode == "pre_routed" else c["rep_ids"]
+        w = c["pre_w"].astype(np.float64)
+        inputs = synth.Inputs(x=c["x_bits"], ids=ids, w=c["pre_w"])
     else:
         ids, w = reference_route(c["logits"], K)
         inputs = synth.Inputs(x=c["x_bits"], logits=c["logits"])
     r = run_gpu(g, inputs, K, cf, gemm_path)
-    if mode != "pre_routed":
+    if mode in ("logits", "capacity"):
         assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 1.0 / K)
     keep = reference_keep(ids, cf, E)
     assert np.array_equal(r["row_of"] >= 0, keep)

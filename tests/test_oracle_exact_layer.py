@@ -192,6 +192,10 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
             logits[t, routed] = L
     pre_ids = np.stack([rng.permutation(routed)[:K] for _ in range(T)]).astype(np.int32)
     pre_w = (rng.integers(1, 9, size=(T, K)) / 8).astype(np.float32)
+    # the same with every slot of about a third of the tokens on one expert
+    rep_ids = pre_ids.copy()
+    rep = rng.choice(T, size=max(1, T // 3), replace=False)
+    rep_ids[rep] = rep_ids[rep, :1]
     r_ids, _ = reference_route(logits, K)
     pairs = {(t, int(e)) for t in range(T) for e in r_ids[t]} | \
             {(t, int(e)) for t in range(T) for e in pre_ids[t]}
@@ -234,10 +238,12 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     calib_bits = f32_to_bf16_bits(calib.astype(np.float32))
     return dict(H=H, F=F, E=E, K=K, T=T, qmax=qmax, x=x, x_bits=x_bits, d=d, m=m, s=s,
                 calib_bits=calib_bits, wg=wg, wu=wu, wd=wd, plan=plan, logits=logits,
-                pre_ids=pre_ids, pre_w=pre_w)
+                pre_ids=pre_ids, pre_w=pre_w, rep_ids=rep_ids)
 
 
-MODES = ["logits", "capacity", "pre_routed"]
+# pre_routed: given ids and unequal weights; repeated: given ids naming one
+# expert in every slot of some tokens (one row per slot), with capacity
+MODES = ["logits", "capacity", "pre_routed", "repeated"]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -260,10 +266,12 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
         assert np.all(cal["sw_gu"][e, F:] == _pow2(p["pu"]))
         assert np.all(cal["sw_d"][e] == _pow2(p["pr"]))
 
-    cf = 0.75 if mode == "capacity" else 0.0     # C = 2 (E5_k2) and 4 (E7_k4)
-    if mode == "pre_routed":
-        ids, w = c["pre_ids"], c["pre_w"].astype(np.float64)
-        o = oracle.forward(c["x_bits"], cal, K, ids=c["pre_ids"], w=c["pre_w"], fmt=fmt)
+    cf = 0.75 if mode in ("capacity", "repeated") else 0.0   # C = 2 (E5_k2), 4 (E7_k4)
+    if mode in ("pre_routed", "repeated"):
+        ids = c["pre_ids"] if mode == "pre_routed" else c["rep_ids"]
+        w = c["pre_w"].astype(np.float64)
+        o = oracle.forward(c["x_bits"], cal, K, ids=ids, w=c["pre_w"], capacity_factor=cf,
+                           fmt=fmt)
     else:
         ids, w = reference_route(c["logits"], K)
         o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf, fmt=fmt)
@@ -297,5 +305,13 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
     assert not np.array_equal(ref, reference_layer(*args, keep, swap_gate_up=True))
     if mode == "pre_routed":
         assert not np.array_equal(ref, reference_layer(*args, keep, swap_slots=True))
+    if mode == "repeated":
+        assert np.any(ids[:, 0] == ids[:, 1])
+        # where a repeated slot survives the capacity, keeping one row per
+        # token and expert instead of one per slot gives another result
+        dup = np.zeros_like(keep)
+        dup[:, 1:] = ids[:, 1:] == ids[:, :1]
+        if (keep & dup).any():
+            assert not np.array_equal(ref, reference_layer(*args, keep & ~dup))
     if mode == "capacity":
         assert not np.array_equal(ref, reference_layer(*args, np.ones_like(keep)))
