@@ -69,8 +69,8 @@ uint16_t oracle_f64_to_bf16(double v) {
 /* Symmetric per-row INT8 quantiser with the fp32 decision rule.
  *
  * [K100AI §1.2, §3.2]: weights are quantised per output channel from their
- * range, activations per token, both to 8 bits; the benchmark spec fixes
- * symmetric absmax. Readings: codes lie in [-127, 127] (symmetric, -128
+ * range, activations per token, both to 8 bits. Readings: symmetric absmax
+ * scaling; codes lie in [-127, 127] (symmetric, -128
  * unused); rounding is half to even; the code is rint(v * (127/amax)) with both
  * the reciprocal and the product rounded to fp32; the stored scale is
  * amax/127; an all-zero row gets scale 0 and codes 0. */
@@ -257,8 +257,8 @@ int oracle_calibrate(int32_t H, int32_t F, int32_t E, float alpha,
 /* Softmax top-k routing with deterministic ties.
  *
  * [Day0 §四 (MoE operator fusion)]: the fused top-k must reproduce the
- * reference exactly, tie-break rule included; the benchmark spec fixes
- * the rule as "lower expert index wins". [Opus-K3 §1.1]: every MoE layer
+ * reference exactly, tie-break rule included; the rule taken here is that the
+ * lower expert index wins. [Opus-K3 §1.1]: every MoE layer
  * routes each token to its top-k experts.
  * Definition: experts are ordered by (logit descending, index ascending) with
  * IEEE comparisons (so -0.0 and +0.0 tie); the first k are taken in that

@@ -1,7 +1,7 @@
 """Shared helpers of the tests: layout (un)packing, running the HIP path with
 every debug output, and the parity comparisons.
 
-Parity bar (what the benchmark spec of the layer fixes):
+Parity bar of the layer:
   - routing ids, grouping (counts, offsets, sorted, row_of), activation codes
     and scales, and the GEMM1 int32 accumulators: bit-exact;
   - routing weights: |diff| <= 1e-6;

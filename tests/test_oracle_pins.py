@@ -561,7 +561,7 @@ def _identity_perm(T, k, E, rng):
 
 
 def test_int8_gemms_exact_integer_matmul():
-    """acc1 and acc2 equal exact integer matmuls (spec check 1)."""
+    """acc1 and acc2 equal exact integer matmuls."""
     rng = np.random.default_rng(11)
     E, F, H, T, k = 3, 64, 128, 10, 2
     cal = dict(q_gu=rng.integers(-127, 128, (E, 2 * F, H)).astype(np.int8),
