@@ -404,6 +404,31 @@ def test_nonfinite_logits(torch_cuda, name):
     c.finish(name)
 
 
+@pytest.mark.parametrize("gemm_path", [1, 2])
+def test_deterministic_large(torch_cuda, gemm_path):
+    """Three runs of a batch of 3000 tokens (64 experts, top-8, capacity 1.25:
+    batched routing, many tiles whose order is taken from an atomic queue on
+    the tiled path, row maxima by atomics) give identical bits in the output
+    and in every debug stage."""
+    torch = torch_cuda
+    wl = synth.workload("tiny", T=3000, E=64, k=8, H=512, F=256, capacity_factor=1.25)
+    _say("[parity] case=determinism T=3000 E=64 k=8 path=%d" % gemm_path)
+    layer, cal = _layer_and_cal(wl)
+    inputs = synth.make_inputs(wl, layer)
+    gl = _gpu_layer(wl, cal)
+    runs = [run_gpu(gl, inputs, wl.k, wl.capacity_factor, gemm_path) for _ in range(3)]
+    first = runs[0]
+    for r in runs[1:]:
+        assert np.array_equal(r["out"], first["out"])
+        for name in ("ids", "row_of", "sorted", "qx", "sx"):
+            assert np.array_equal(r[name], first[name]), name
+        for name in ("acc1", "qh", "sh", "y"):
+            a = first["gpu_tensors"][name]
+            b = r["gpu_tensors"][name]
+            n = a.numel() * first["kept"] // max(wl.T * wl.k, 1)
+            assert bool((a[:n].view(torch.uint8) == b[:n].view(torch.uint8)).all()), name
+
+
 def test_deterministic_and_t0(torch_cuda):
     """Two runs give identical bits; T = 0 is a no-op."""
     import torch
