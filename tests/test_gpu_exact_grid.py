@@ -35,11 +35,11 @@ import functools
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from moe_testlib import bf16_step, bf16_tensor, run_gpu, unpack_tiled
 from test_oracle_exact_layer import (ALPHA, _code_values, build, reference_keep,
                                      reference_route, reference_y)
-import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -168,18 +168,19 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     y_rows = y[t_of, j_of]
     y_err = np.abs(y_gpu - y_rows)
     y_bound = _y_error_bound(y_rows, tiled)
-    assert np.all(y_err <= y_bound), "y: %g of its bound" % (y_err / np.maximum(y_bound, 1e-300)).max()
+    y_ratio = (y_err / np.maximum(y_bound, 1e-300)).max()
+    assert np.all(y_err <= y_bound), "y: %g of its bound" % y_ratio
 
     ref = np.einsum("tk,tkh->th", w * keep, y)
     out = synth.bf16_bits_to_f32(r["out"]).reshape(T, H).astype(np.float64)
     absw = np.abs(w * keep)
     bound = np.zeros((T, H))
     for j in range(K):
-        bound += absw[:, j, None] * (_y_error_bound(y[:, j], tiled) + 2.0 ** -22 * np.abs(y[:, j]))
+        y_j = y[:, j]
+        bound += absw[:, j, None] * (_y_error_bound(y_j, tiled) + 2.0 ** -22 * np.abs(y_j))
     bound += 0.5 * bf16_step(out)
     err = np.abs(out - ref)
     _say("[exact grid] y: max error %.3g of its bound; out: max error %.3g of its bound, "
-         "%.3g x RMS" % ((y_err / np.maximum(y_bound, 1e-300)).max(),
-                          (err / np.maximum(bound, 1e-300)).max(),
+         "%.3g x RMS" % (y_ratio, (err / np.maximum(bound, 1e-300)).max(),
                           err.max() / np.sqrt(np.mean(ref ** 2))))
     assert np.all(err <= bound)
