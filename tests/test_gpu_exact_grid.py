@@ -16,6 +16,9 @@ exact where the path is integer and tight where it is not:
   - the output differs from the dense fp64 MoE FFN by at most those errors
     weighted by |w|, the fp32 combine (2^-22 of sum |w y|) and half a bf16
     step at the output.
+A fifth mode adds a static activation clip that the construction keeps
+exact (static_clip in the CPU test): the reference then takes the clipped
+tokens.
 The reference is the dense FFN of the CPU test, with routing (ties to the
 lower index, "超大规模模型推理的Day0适配实践" §四) and capacity (§二.2) by
 their definitions; it takes nothing from the oracle or the GPU.
@@ -39,7 +42,7 @@ import oracle
 import synth
 from moe_testlib import bf16_step, bf16_tensor, run_gpu, unpack_tiled
 from test_oracle_exact_layer import (ALPHA, _code_values, build, reference_keep,
-                                     reference_route, reference_y)
+                                     reference_route, reference_y, static_clip)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +113,7 @@ def _y_error_bound(y, tiled):
 
 
 @pytest.mark.parametrize("gemm_path", [1, 2])
-@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated"])
+@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated", "clip"])
 @pytest.mark.parametrize("shape,T", [("E9_k2", 40), ("E9_k2", 3000), ("E65_k8", 200),
                                      ("E65_k8", 3000)])
 @pytest.mark.parametrize("fmt_name", ["int8", "fp8"])
@@ -122,6 +125,9 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
          % (fmt_name, T, H, F, E, K, mode, gemm_path))
     g = _gpu_layer(T, fmt_name, shape)
     cf = 0.75 if mode in ("capacity", "repeated") else 0.0
+    level, d, m, x = 0.0, c["d"], c["m"], c["x"]
+    if mode == "clip":     # a static activation clip the construction keeps exact
+        level, d, m, x = static_clip(c)
     if mode in ("pre_routed", "repeated"):
         # repeated: every slot of about a third of the tokens names one expert
         ids = c["pre_ids"] if mode == "pre_routed" else c["rep_ids"]
@@ -130,15 +136,20 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     else:
         ids, w = reference_route(c["logits"], K)
         inputs = synth.Inputs(x=c["x_bits"], logits=c["logits"])
-    r = run_gpu(g, inputs, K, cf, gemm_path)
-    if mode in ("logits", "capacity"):
+    g.act_clip.fill_(level)
+    g.set_clip(static=mode == "clip")
+    try:
+        r = run_gpu(g, inputs, K, cf, gemm_path)
+    finally:
+        g.set_clip(static=False)
+    if mode in ("logits", "capacity", "clip"):
         assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 1.0 / K)
     keep = reference_keep(ids, cf, E)
     assert np.array_equal(r["row_of"] >= 0, keep)
     if mode == "capacity":
         assert not keep.all()
-    assert np.array_equal(_code_values(r["qx"], fmt), c["d"])
-    assert np.array_equal(r["sx"].astype(np.float64), 2.0 ** c["m"])
+    assert np.array_equal(_code_values(r["qx"], fmt), d)
+    assert np.array_equal(r["sx"].astype(np.float64), 2.0 ** m)
 
     kept = r["kept"]
     a = r["sorted"].astype(np.int64)
@@ -155,15 +166,15 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     cg = np.stack([plan[e]["cg"] for e in range(E - 1)])
     n = np.stack([plan[e]["n"] for e in range(E - 1)])
     pgu = np.array([plan[e]["pg"] + plan[e]["pu"] for e in range(E - 1)])
-    acc_g = np.einsum("rh,rh->r", c["d"][t_of], cg[e_of])
+    acc_g = np.einsum("rh,rh->r", d[t_of], cg[e_of])
     assert np.all(acc1[:, :F] == acc_g[:, None]), "GEMM1 gate sums differ"
     assert np.array_equal(acc1[:, F:], qmax * n[e_of]), "GEMM1 up sums differ"
     moved = np.nonzero(np.any(_code_values(qh, fmt) != n[e_of], axis=1))[0]
     assert moved.size == 0, "rows %s: a requantised code moved" % moved[:5]
-    expo = 2 * c["m"][t_of] + pgu[e_of]
+    expo = 2 * m[t_of] + pgu[e_of]
     assert np.array_equal(sh.astype(np.float64), acc_g * qmax * 2.0 ** expo)
 
-    y = reference_y(c["x"], c["wg"], c["wu"], c["wd"], ids, keep)       # [T][K][H]
+    y = reference_y(x, c["wg"], c["wu"], c["wd"], ids, keep)       # [T][K][H]
     tiled = gemm_path == 2
     y_rows = y[t_of, j_of]
     y_err = np.abs(y_gpu - y_rows)

@@ -241,9 +241,29 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
                 pre_ids=pre_ids, pre_w=pre_w, rep_ids=rep_ids)
 
 
+def static_clip(c):
+    """A static activation clip that the construction keeps exact: the level
+    qmax * 2^q, q the smallest token exponent, so every token with a larger
+    exponent is clipped ("一晚上完成MoE模型推理优化…" §3.2: activations beyond
+    the calibrated level are cut off). Smoothed values beyond the level become
+    +-level and the others d * 2^(m - q), integers (e4m3 ones for FP8), so the
+    codes stay exact; the anchor code stays qmax. Returns the level, the codes
+    and exponents the tokens quantise to, and the clipped tokens
+    clamp(x * inv_s, +-level) * s that the dense reference takes."""
+    qmax = c["qmax"]
+    q = int(c["m"].min())
+    level = qmax * _pow2(q)
+    d = np.clip(c["d"] * 2.0 ** (c["m"] - q)[:, None], -qmax, qmax)
+    m = np.full_like(c["m"], q)
+    x = np.clip(c["x"] / c["s"][None, :], -level, level) * c["s"][None, :]
+    assert np.array_equal(x, d * _pow2(q) * c["s"][None, :])
+    return level, d, m, x
+
+
 # pre_routed: given ids and unequal weights; repeated: given ids naming one
-# expert in every slot of some tokens (one row per slot), with capacity
-MODES = ["logits", "capacity", "pre_routed", "repeated"]
+# expert in every slot of some tokens (one row per slot), with capacity;
+# clip: logits routing with a static activation clip
+MODES = ["logits", "capacity", "pre_routed", "repeated", "clip"]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -267,6 +287,10 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
         assert np.all(cal["sw_d"][e] == _pow2(p["pr"]))
 
     cf = 0.75 if mode in ("capacity", "repeated") else 0.0   # C = 2 (E5_k2), 4 (E7_k4)
+    level, d, m, x = 0.0, c["d"], c["m"], c["x"]
+    if mode == "clip":
+        level, d, m, x = static_clip(c)
+        assert np.any(c["m"] > m), "no token is clipped"
     if mode in ("pre_routed", "repeated"):
         ids = c["pre_ids"] if mode == "pre_routed" else c["rep_ids"]
         w = c["pre_w"].astype(np.float64)
@@ -274,7 +298,8 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
                            fmt=fmt)
     else:
         ids, w = reference_route(c["logits"], K)
-        o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf, fmt=fmt)
+        o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf,
+                           clip=level, fmt=fmt)
         assert np.array_equal(o["ids"], ids)
         assert np.array_equal(o["w"].astype(np.float64), w)     # ties: exactly 1/2
         assert np.all(w == 1.0 / K) and np.all(ids < E - 1)
@@ -284,18 +309,18 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
         assert not keep.all()
 
     # token codes and scales are the planted ones
-    assert np.array_equal(_code_values(o["qx"], fmt), c["d"])
-    assert np.array_equal(o["sx"].astype(np.float64), [_pow2(int(v)) for v in c["m"]])
+    assert np.array_equal(_code_values(o["qx"], fmt), d)
+    assert np.array_equal(o["sx"].astype(np.float64), [_pow2(int(v)) for v in m])
     # every kept row requantises to its expert's n_f, with the exact scale
     for i in range(o["kept"]):
         a = int(o["sorted"][i])
         t, e = a // K, int(o["ids"].reshape(-1)[a])
         p = c["plan"][e]
         assert np.array_equal(_code_values(o["qh"][i], fmt), p["n"])
-        expo = 2 * int(c["m"][t]) + p["pg"] + p["pu"]
-        assert float(o["sh"][i]) == p["acc_g"][t] * qmax * _pow2(expo)
+        expo = 2 * int(m[t]) + p["pg"] + p["pu"]
+        assert float(o["sh"][i]) == float(d[t] @ p["cg"]) * qmax * _pow2(expo)
 
-    args = (c["x"], c["wg"], c["wu"], c["wd"], ids, w)
+    args = (x, c["wg"], c["wu"], c["wd"], ids, w)
     ref = reference_layer(*args, keep)
     assert np.array_equal(o["out_exact"], ref), np.abs(o["out_exact"] - ref).max()
     want = np.array([[_bf16_nearest_bruteforce(float(v)) for v in row] for row in ref], np.uint16)
@@ -315,3 +340,5 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
             assert not np.array_equal(ref, reference_layer(*args, keep & ~dup))
     if mode == "capacity":
         assert not np.array_equal(ref, reference_layer(*args, np.ones_like(keep)))
+    if mode == "clip":
+        assert not np.array_equal(ref, reference_layer(c["x"], *args[1:], keep))
