@@ -18,7 +18,10 @@ exact where the path is integer and tight where it is not:
     step at the output.
 A fifth mode adds a static activation clip that the construction keeps
 exact (static_clip in the CPU test): the reference then takes the clipped
-tokens.
+tokens. A sixth routes by the router projection on the GPU ("超大规模模型推理
+的Day0适配实践" §四): the router matrix reads each expert's logit from a
+channel of its own, so the projected logits are exact and must equal the
+planted ones, with the chosen experts tied.
 The reference is the dense FFN of the CPU test, with routing (ties to the
 lower index, "超大规模模型推理的Day0适配实践" §四) and capacity (§二.2) by
 their definitions; it takes nothing from the oracle or the GPU.
@@ -113,7 +116,8 @@ def _y_error_bound(y, tiled):
 
 
 @pytest.mark.parametrize("gemm_path", [1, 2])
-@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated", "clip"])
+@pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated", "clip",
+                                  "router"])
 @pytest.mark.parametrize("shape,T", [("E9_k2", 40), ("E9_k2", 3000), ("E65_k8", 200),
                                      ("E65_k8", 3000)])
 @pytest.mark.parametrize("fmt_name", ["int8", "fp8"])
@@ -133,16 +137,24 @@ def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
         ids = c["pre_ids"] if mode == "pre_routed" else c["rep_ids"]
         w = c["pre_w"].astype(np.float64)
         inputs = synth.Inputs(x=c["x_bits"], ids=ids, w=c["pre_w"])
+    elif mode == "router":  # logits projected on the GPU from x and the router matrix
+        ids, w = reference_route(c["router_logits"], K)
+        inputs = synth.Inputs(x=c["x_bits"])
     else:
         ids, w = reference_route(c["logits"], K)
         inputs = synth.Inputs(x=c["x_bits"], logits=c["logits"])
     g.act_clip.fill_(level)
     g.set_clip(static=mode == "clip")
+    if mode == "router":
+        g.set_router(bf16_tensor(c["w_router_bits"], g.device))
     try:
-        r = run_gpu(g, inputs, K, cf, gemm_path)
+        r = run_gpu(g, inputs, K, cf, gemm_path, project=mode == "router")
     finally:
         g.set_clip(static=False)
-    if mode in ("logits", "capacity", "clip"):
+        g.set_router(None)
+    if mode == "router":
+        assert np.array_equal(r["router_logits"].astype(np.float64), c["router_logits"])
+    if mode in ("logits", "capacity", "clip", "router"):
         assert np.array_equal(r["ids"], ids) and np.all(r["w"] == 1.0 / K)
     keep = reference_keep(ids, cf, E)
     assert np.array_equal(r["row_of"] >= 0, keep)

@@ -53,7 +53,7 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 FORMATS = {"int8": (oracle.FMT_INT8, 127), "fp8": (oracle.FMT_FP8, 448)}
 # k is a power of 2, so that the weights of k tied experts (1/k) are exact
-SHAPES = {"E5_k2": dict(H=8, F=4, E=5, K=2, T=6), "E7_k4": dict(H=8, F=4, E=7, K=4, T=8)}
+SHAPES = {"E5_k2": dict(H=8, F=4, E=5, K=2, T=6), "E7_k4": dict(H=16, F=4, E=7, K=4, T=8)}
 ALPHA = 0.5
 
 
@@ -156,12 +156,21 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     Channel 0 is the anchor (qmax in every token); channels H-2 and H-1 are
     zero in every token and hold the qmax of the gate and the up rows.
     down_step: the requantised values n and the down codes are drawn from the
-    multiples of down_step on the grid."""
+    multiples of down_step on the grid.
+    Router projection: channel 1 + e is routed expert e's routing channel
+    (s = 1 there); the router matrix reads expert e's logit from it
+    (w_router[e] = one-hot at 1 + e; the carrier reads expert 0's channel, so
+    it ties expert 0 whenever that one is chosen, and must lose). Each token
+    holds one value v on the channels of its K chosen experts and smaller
+    ones on the others, so the projected logits d * 2^m are exact and tie at
+    the top (weights exactly 1/K)."""
     rng = np.random.default_rng([4242, seed, qmax, H, T, down_step])
     grid = _grid(qmax)
     grid_down = grid[grid % down_step == 0]
     routed, anchor, gate_pad, up_pad = E - 1, 0, H - 2, H - 1
+    assert routed + 3 <= H, "no room for a routing channel per expert"
     b = rng.integers(-1, 3, size=H)                 # s_j = 2^b_j
+    b[1:1 + routed] = 0
     a = rng.integers(5, 7, size=H) + (qmax > 127)   # weight range aw_j = 4^a_j
     aw = np.array([4.0 ** int(v) for v in a])
     ax = np.array([4.0 ** int(a[j] + b[j]) for j in range(H)])
@@ -174,6 +183,12 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     d[:, anchor] = qmax
     d[:, gate_pad] = 0
     d[:, up_pad] = 0
+    router_top = np.stack([np.sort(rng.choice(routed, size=K, replace=False)) for _ in range(T)])
+    for t in range(T):
+        i = int(rng.integers(5, grid.size))
+        lower = grid[i - rng.integers(1, 6, size=routed)]
+        d[t, 1:1 + routed] = lower
+        d[t, 1 + router_top[t]] = grid[i]
     x = (d * np.array([_pow2(int(v)) for v in m])[:, None]) * s[None, :]
     x32 = x.astype(np.float32)
     assert np.array_equal(x32.astype(np.float64), x)
@@ -196,9 +211,17 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     rep_ids = pre_ids.copy()
     rep = rng.choice(T, size=max(1, T // 3), replace=False)
     rep_ids[rep] = rep_ids[rep, :1]
+    w_router = np.zeros((E, H), np.float32)
+    w_router[np.arange(routed), 1 + np.arange(routed)] = 1.0
+    w_router[routed, 1] = 1.0
+    router_logits = x @ w_router.astype(np.float64).T
+    assert np.array_equal(router_logits[:, :routed], d[:, 1:1 + routed] * 2.0 ** m[:, None])
     r_ids, _ = reference_route(logits, K)
+    p_ids, _ = reference_route(router_logits, K)
+    assert np.array_equal(p_ids, router_top)
     pairs = {(t, int(e)) for t in range(T) for e in r_ids[t]} | \
-            {(t, int(e)) for t in range(T) for e in pre_ids[t]}
+            {(t, int(e)) for t in range(T) for e in pre_ids[t]} | \
+            {(t, int(e)) for t in range(T) for e in p_ids[t]}
 
     wg = np.zeros((E, F, H), np.float32)
     wu = np.zeros((E, F, H), np.float32)
@@ -238,7 +261,8 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     calib_bits = f32_to_bf16_bits(calib.astype(np.float32))
     return dict(H=H, F=F, E=E, K=K, T=T, qmax=qmax, x=x, x_bits=x_bits, d=d, m=m, s=s,
                 calib_bits=calib_bits, wg=wg, wu=wu, wd=wd, plan=plan, logits=logits,
-                pre_ids=pre_ids, pre_w=pre_w, rep_ids=rep_ids)
+                pre_ids=pre_ids, pre_w=pre_w, rep_ids=rep_ids,
+                w_router_bits=f32_to_bf16_bits(w_router), router_logits=router_logits)
 
 
 def static_clip(c):
@@ -262,8 +286,9 @@ def static_clip(c):
 
 # pre_routed: given ids and unequal weights; repeated: given ids naming one
 # expert in every slot of some tokens (one row per slot), with capacity;
-# clip: logits routing with a static activation clip
-MODES = ["logits", "capacity", "pre_routed", "repeated", "clip"]
+# clip: logits routing with a static activation clip; router: logits from the
+# router projection of the tokens
+MODES = ["logits", "capacity", "pre_routed", "repeated", "clip", "router"]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -296,6 +321,12 @@ def test_lossless_layer_equals_dense_ffn(fmt_name, shape, seed, mode):
         w = c["pre_w"].astype(np.float64)
         o = oracle.forward(c["x_bits"], cal, K, ids=ids, w=c["pre_w"], capacity_factor=cf,
                            fmt=fmt)
+    elif mode == "router":
+        lg = oracle.router_logits(c["x_bits"], c["w_router_bits"])
+        assert np.array_equal(lg, c["router_logits"])
+        ids, w = reference_route(c["router_logits"], K)
+        o = oracle.forward(c["x_bits"], cal, K, logits=lg.astype(np.float32), fmt=fmt)
+        assert np.array_equal(o["ids"], ids) and np.all(w == 1.0 / K) and np.all(ids < E - 1)
     else:
         ids, w = reference_route(c["logits"], K)
         o = oracle.forward(c["x_bits"], cal, K, logits=c["logits"], capacity_factor=cf,
