@@ -50,7 +50,9 @@ from test_oracle_exact_layer import (ALPHA, _code_values, build, reference_keep,
 pytestmark = pytest.mark.gpu
 
 SHAPES = {"E9_k2": dict(H=256, F=128, E=9, K=2),
-          "E65_k8": dict(H=512, F=256, E=65, K=8)}
+          "E65_k8": dict(H=512, F=256, E=65, K=8),
+          # the decode layer: hidden 4096, FFN 1536, 64 routed experts, top-8
+          "decode": dict(H=4096, F=1536, E=65, K=8)}
 Y_GROUP = 16
 Y_CODE_MAX = 32767
 
@@ -75,6 +77,10 @@ FORMATS = {"int8": (oracle.FMT_INT8, 127, 1), "fp8": (oracle.FMT_FP8, 448, 4)}
 @functools.lru_cache(maxsize=1)
 def _case(T, fmt_name, shape):
     _, qmax, step = FORMATS[fmt_name]
+    if fmt_name == "fp8" and SHAPES[shape]["F"] > 256:
+        # FFN 1536: GEMM2 partial sums reach 2^28, so every product is made a
+        # multiple of 256 (values multiples of 16) to keep them within fp32
+        step = 16
     return build(7, qmax, T=T, down_step=step, **SHAPES[shape])
 
 
@@ -119,7 +125,7 @@ def _y_error_bound(y, tiled):
 @pytest.mark.parametrize("mode", ["logits", "capacity", "pre_routed", "repeated", "clip",
                                   "router"])
 @pytest.mark.parametrize("shape,T", [("E9_k2", 40), ("E9_k2", 3000), ("E65_k8", 200),
-                                     ("E65_k8", 3000)])
+                                     ("E65_k8", 3000), ("decode", 32)])
 @pytest.mark.parametrize("fmt_name", ["int8", "fp8"])
 def test_exact_grid_layer(torch_cuda, fmt_name, shape, T, mode, gemm_path):
     fmt, qmax, _ = FORMATS[fmt_name]

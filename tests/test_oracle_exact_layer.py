@@ -255,9 +255,9 @@ def build(seed, qmax=127, H=8, F=4, E=5, K=2, T=6, down_step=1):
     wg[routed, 0] = (aw * rng.choice([-1, 1], size=H)).astype(np.float32)
     wu[routed] = rng.uniform(-1, 1, size=(F, H)).astype(np.float32)
     wd[routed] = rng.uniform(-1, 1, size=(H, F)).astype(np.float32)
-    for j in range(H):
-        assert np.abs(np.concatenate([wg[:, :, j], wu[:, :, j]])).max() == aw[j]
-        assert np.abs(calib[:, j]).max() == ax[j]
+    assert np.array_equal(np.maximum(np.abs(wg).max(axis=(0, 1)), np.abs(wu).max(axis=(0, 1))),
+                          aw)
+    assert np.array_equal(np.abs(calib).max(axis=0), ax)
     calib_bits = f32_to_bf16_bits(calib.astype(np.float32))
     return dict(H=H, F=F, E=E, K=K, T=T, qmax=qmax, x=x, x_bits=x_bits, d=d, m=m, s=s,
                 calib_bits=calib_bits, wg=wg, wu=wu, wd=wd, plan=plan, logits=logits,
